@@ -1,0 +1,21 @@
+"""CPU oracle for the blockwise-scaled FP8 linear layer.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite, the package smoke
+check and the benchmark's CPU-baseline leg may import this package.  It shares
+no code with the HIP path.
+"""
+from .oracle import (  # noqa: F401
+    MODE_AMAX,
+    MODE_POW2,
+    build,
+    e4m3_decode_table,
+    e4m3_encode,
+    block_scale,
+    quant_act_1x128,
+    quant_weight_128x128,
+    gemm_f64,
+    gemm_sampled_f64,
+    grouped_gemm_f64,
+    grouped_gemm_sampled_f64,
+    num_threads,
+)
