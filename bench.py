@@ -1,0 +1,310 @@
+"""Benchmark of the blockwise-scaled FP8 linear layer on one MI355X.
+
+One step = the FP8 forward of the four Llama-3.1-8B-shaped linear layers at
+4096 tokens (QKV 4096->6144, O 4096->4096, gate+up 4096->28672, down
+14336->4096): per layer, dynamic 1x128 activation quantization followed by the
+block-scaled FP8 GEMM (fp32 accumulation, bf16 output).  The weights are
+quantized (128x128 blocks) before the timed region, as they are once per
+policy update; the recalibration pass over all 128 linear weights of the
+32-layer model is timed separately.  Inputs are seeded synthetic tensors
+(no checkpoints, no datasets), resident in HBM when timing starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 MFMA, TFLOP/s
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def act_quant_bytes(M, K):
+    """Algorithmic bytes of one 1x128 activation quantization: 2 B read and
+    1 B written per element, 4 B per block scale."""
+    return M * K * 3 + (M * K // 128) * 4
+
+
+def weight_quant_bytes(N, K):
+    return N * K * 3 + (N // 128) * (K // 128) * 4
+
+
+def time_loop(fn, reps, torch):
+    """Average duration (s) of fn() over reps launches, HIP events on the
+    current stream (the stream the library enqueues on)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="tokens per layer in the oracle's CPU-baseline sample")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the step (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on one GPU's share; see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import blockwise_scaled_fp8_quant_amd as fp8q
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("library", fp8q.library_path())
+
+    # ---- inputs of the step (Llama-3.1-8B-shaped layers, 4096 tokens) ----
+    M = synth.LLAMA_TOKENS
+    layers = []
+    for i, (name, N, K) in enumerate(synth.LLAMA_LAYERS):
+        x, w = synth.llama_layer_inputs(i, device=dev)
+        bq, bs = fp8q.fp8_quant_weight_128x128(w)
+        aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        layers.append(dict(name=name, N=N, K=K, x=x, w=w, bq=bq, bs=bs, aq=aq, as_=as_, y=y))
+    torch.cuda.synchronize()
+    step_flops = sum(2.0 * M * l["N"] * l["K"] for l in layers)
+
+    def step():
+        for l in layers:
+            fp8q.fp8_quant_act_1x128(l["x"], out=(l["aq"], l["as_"]))
+            fp8q.fp8_blockscaled_gemm(l["aq"], l["as_"], l["bq"], l["bs"], out=l["y"])
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing", args.steps, "steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = start.elapsed_time(end) / 1e3 / args.steps
+    value = step_flops / step_s / 1e12
+    log(f"step {step_s * 1e3:.3f} ms  ({wall:.3f} s wall for {args.steps} steps)  {value:.1f} TFLOP/s")
+
+    result = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate -> bf16",
+        "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x20, N(0,0.02) weights)",
+        "config": {
+            "workload": "Llama-3.1-8B-shaped FP8 linear layers (QKV, O, gate+up, down), 4096 tokens: "
+                        "1x128 activation quantization + block-scaled FP8 GEMM per layer",
+            "tokens": M,
+            "layers": [[l["name"], l["N"], l["K"]] for l in layers],
+            "weight_blocks": "128x128", "activation_blocks": "1x128", "scale_mode": "amax/448",
+            "parallelism": "single GPU",
+        },
+    }
+
+    # ---- per-kernel timing (events around repeated launches) ----
+    reps = max(10, args.steps)
+    gemm_s, gemm_flops, per_layer = 0.0, 0.0, {}
+    for l in layers:
+        t = time_loop(lambda l=l: fp8q.fp8_blockscaled_gemm(l["aq"], l["as_"], l["bq"], l["bs"], out=l["y"]),
+                      reps, torch)
+        f = 2.0 * M * l["N"] * l["K"]
+        gemm_s += t
+        gemm_flops += f
+        per_layer[l["name"]] = {"gemm_us": round(t * 1e6, 2), "gemm_tflops": round(f / t / 1e12, 1)}
+    gemm_tflops = gemm_flops / gemm_s / 1e12
+    log(f"gemm {gemm_tflops:.1f} TFLOP/s over the 4 layers")
+
+    # activation quantization: rotate through >= 1 GB of distinct inputs so the
+    # 256 MB last-level cache cannot hold them
+    q_s, q_bytes = 0.0, 0.0
+    for l in layers:
+        K = l["K"]
+        nrot = max(1, int(np.ceil(1.2e9 / (M * K * 3))))
+        xs = [l["x"]] + [torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+                         for _ in range(nrot - 1)]
+        ctr = [0]
+
+        def qa(l=l, xs=xs, ctr=ctr):
+            fp8q.fp8_quant_act_1x128(xs[ctr[0] % len(xs)], out=(l["aq"], l["as_"]))
+            ctr[0] += 1
+        t = time_loop(qa, reps * len(xs), torch)
+        b = act_quant_bytes(M, K)
+        q_s += t
+        q_bytes += b
+        per_layer[l["name"]].update(act_quant_us=round(t * 1e6, 2), act_quant_gbs=round(b / t / 1e9, 1))
+        del xs
+    act_gbs = q_bytes / q_s / 1e9
+    log(f"act quant {act_gbs:.1f} GB/s")
+
+    result["kernels"] = {
+        "gemm_tflops": round(gemm_tflops, 1),
+        "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+        "act_quant_gbs": round(act_gbs, 1),
+        "act_quant_frac_hbm": round(act_gbs / HBM_PEAK_GBS, 4),
+        "per_layer": per_layer,
+    }
+    result["roofline"] = {
+        "kernel": "gemm_kernel (dense block-scaled FP8 GEMM), 4 Llama layer shapes",
+        "bound": "mfma",
+        "achieved": round(gemm_tflops, 1),
+        "peak": FP8_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+        "traffic": None,
+    }
+
+    if not args.skip_extras:
+        result["recalibration"] = recalibration(fp8q, synth, torch, dev)
+        result["moe"] = moe(fp8q, synth, torch, dev, reps)
+        result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
+        for l in layers:
+            del l["w"]
+        result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def recalibration(fp8q, synth, torch, dev):
+    """Requantize all 128 linear weights of the 32-layer Llama-3.1-8B shape."""
+    log("recalibration pass: generating 32 x 4 weights")
+    ws, outs, total = [], [], 0
+    for layer in range(synth.LLAMA_NUM_LAYERS):
+        for kind in range(4):
+            w = synth.llama_weight(layer, kind, device=dev)
+            N, K = w.shape
+            ws.append(w)
+            outs.append((torch.empty((N, K), dtype=torch.uint8, device=dev),
+                         torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)))
+            total += weight_quant_bytes(N, K)
+    torch.cuda.synchronize()
+    res = {"matrices": len(ws), "params": int(sum(w.numel() for w in ws)), "bytes_per_pass": total}
+    for mode in ("amax", "pow2"):
+        def one_pass(mode=mode):
+            for w, o in zip(ws, outs):
+                fp8q.fp8_quant_weight_128x128(w, mode, out=o)
+        one_pass()
+        t = time_loop(one_pass, 3, torch)
+        gbs = total / t / 1e9
+        res[mode] = {"ms_per_pass": round(t * 1e3, 3), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"recalibration {mode}: {t * 1e3:.3f} ms/pass, {gbs:.1f} GB/s")
+    del ws, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def moe(fp8q, synth, torch, dev, reps):
+    """Grouped GEMM on the Qwen3-30B-A3B and Moonlight-16B expert shapes."""
+    out = {}
+    for shape in (synth.QWEN3, synth.MOONLIGHT):
+        for layer in ("gate_up", "down"):
+            x, w, off = synth.moe_inputs(shape, layer, device=dev)
+            G, N, K = w.shape
+            Mt = x.shape[0]
+            bq = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+            bs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+            for g in range(G):
+                fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
+            del w
+            offd = torch.from_numpy(off).to(dev)
+            aq, as_ = fp8q.fp8_quant_act_1x128(x)
+            y = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+            t = time_loop(lambda: fp8q.fp8_grouped_gemm(aq, as_, bq, bs, offd, out=y), reps, torch)
+            flops = 2.0 * Mt * N * K
+            tf = flops / t / 1e12
+            hbm_bytes = Mt * K + G * N * K + 2 * Mt * N + Mt * (K // 128) * 4 + G * (N // 128) * (K // 128) * 4
+            roof = min(FP8_PEAK_TFLOPS, flops / (hbm_bytes / (HBM_PEAK_GBS * 1e9)) / 1e12)
+            out[f"{shape.name}/{layer}"] = {
+                "rows": Mt, "groups": G, "N": N, "K": K, "us": round(t * 1e6, 2),
+                "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                "roof_tflops": round(roof, 1), "frac_roof": round(tf / roof, 4)}
+            log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}")
+            del x, bq, bs, aq, as_, y
+            torch.cuda.empty_cache()
+    return out
+
+
+def bf16_compare(layers, torch, M, reps, fp8_gemm_tflops):
+    """torch.matmul in bf16 (hipBLASLt) on the same shapes, for the FP8/BF16 ratio."""
+    tot_s, tot_f, per = 0.0, 0.0, {}
+    for l in layers:
+        x, w = l["x"], l["w"]
+        t = time_loop(lambda: torch.matmul(x, w.t()), reps, torch)
+        f = 2.0 * M * l["N"] * l["K"]
+        tot_s += t
+        tot_f += f
+        per[l["name"]] = round(f / t / 1e12, 1)
+    tf = tot_f / tot_s / 1e12
+    log(f"bf16 torch.matmul {tf:.1f} TFLOP/s")
+    return {"tflops": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "per_layer_tflops": per, "fp8_over_bf16": round(fp8_gemm_tflops / tf, 3)}
+
+
+def cpu_baseline(layers, synth, M, rows):
+    """The CPU oracle, as it stands, on a bounded sample of the same step: the
+    first `rows` tokens of each of the four layers (activation quantization of
+    those rows + their GEMM rows in fp64)."""
+    import oracle
+    log(f"cpu baseline: oracle on {rows} of {M} tokens per layer")
+    inputs = []
+    for l in layers:
+        xs = synth.bf16_bits(l["x"][:rows])
+        bq = l["bq"].cpu().numpy()
+        bs = l["bs"].cpu().numpy()
+        inputs.append((xs, bq, bs, l["N"], l["K"]))
+    flops = 0.0
+    t0 = time.perf_counter()
+    for xs, bq, bs, N, K in inputs:
+        aq, as_ = oracle.quant_act_1x128(xs)
+        oracle.gemm_f64(aq, as_, bq, bs)
+        flops += 2.0 * rows * N * K
+    dt = time.perf_counter() - t0
+    v = flops / dt / 1e12
+    log(f"cpu baseline {v * 1e3:.2f} GFLOP/s in {dt:.1f} s")
+    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {rows} of {M} tokens of each of the 4 Llama layers: "
+                      "1x128 quantization + fp64 block-scaled GEMM rows"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+"""Blockwise-scaled FP8 linear layer for AMD MI355X (gfx950).
+
+Python face of the C ABI in include/fp8q.h.  These functions only check and
+marshal arguments (torch tensors in device memory, the current HIP stream);
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams only.
+
+The layer is the one of the end-to-end FP8 RL recipe (page "NVIDIA NeMo RL
+erreicht 48% Geschwindigkeitssteigerung mit End-to-End FP8-Praezisionstraining",
+section "Der technische Durchbruch"): E4M3 codes, one fp32 scale per 1x128
+activation block and per 128x128 weight block, and a block-scaled GEMM with
+fp32 accumulation and bf16 output; weights are requantized after every policy
+update (section "Leistungsgewinne in der Praxis"), optionally with
+power-of-two scales (section "Warum dies fuer die KI-Oekonomie wichtig ist").
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+SCALE_AMAX = 0
+SCALE_POW2 = 1
+_MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_POW2: SCALE_POW2}
+
+__all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
+           "fp8_blockscaled_gemm", "fp8_grouped_gemm", "abi_version", "library_path"]
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def abi_version():
+    return _lib.load().fp8q_abi_version()
+
+
+def _mode(mode):
+    try:
+        return _MODES[mode]
+    except KeyError:
+        raise ValueError(f"unknown scale mode {mode!r} (use 'amax' or 'pow2')") from None
+
+
+def _stream(t):
+    return ctypes.c_void_p(int(torch.cuda.current_stream(t.device).cuda_stream))
+
+
+def _dev(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in device memory (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(int(t.data_ptr()))
+
+
+def _as_bytes(t, name, ndim):
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    return t, _dev(t, name, torch.uint8, ndim)
+
+
+def fp8_quant_act_1x128(x, mode="amax", out=None):
+    """x: bf16 [M, K] (K % 128 == 0) -> (q uint8 [M, K] E4M3 codes, s fp32 [M, K/128])."""
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if out is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    _, pq = _as_bytes(q, "q", 2)
+    ps = _dev(s, "scales", torch.float32, 2)
+    if tuple(q.shape) != (M, K) or tuple(s.shape) != (M, K // 128):
+        raise ValueError("output shapes do not match x")
+    _lib.check("fp8_quant_act_1x128",
+               _lib.load().fp8_quant_act_1x128(px, M, K, pq, ps, _mode(mode), _stream(x)))
+    return q, s
+
+
+def fp8_quant_weight_128x128(w, mode="amax", out=None):
+    """w: bf16 [N, K] (N, K % 128 == 0) -> (q uint8 [N, K], s fp32 [N/128, K/128])."""
+    pw = _dev(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    if out is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    else:
+        q, s = out
+    _, pq = _as_bytes(q, "q", 2)
+    ps = _dev(s, "scales", torch.float32, 2)
+    if tuple(q.shape) != (N, K) or tuple(s.shape) != (N // 128, K // 128):
+        raise ValueError("output shapes do not match w")
+    _lib.check("fp8_quant_weight_128x128",
+               _lib.load().fp8_quant_weight_128x128(pw, N, K, pq, ps, _mode(mode), _stream(w)))
+    return q, s
+
+
+def fp8_blockscaled_gemm(a_q, a_s, b_q, b_s, out=None):
+    """Y[M, N] bf16 = dequant(a_q, a_s) @ dequant(b_q, b_s)^T (fp32 accumulation)."""
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 2)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 2)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K or tuple(a_s.shape) != (M, K // 128) or tuple(b_s.shape) != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
+    py = _dev(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_blockscaled_gemm",
+               _lib.load().fp8_blockscaled_gemm(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
+    return y
+
+
+def fp8_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, out=None):
+    """Grouped (mixture-of-experts) GEMM.
+
+    a_q [M_total, K], a_s [M_total, K/128], b_q [G, N, K], b_s [G, N/128, K/128],
+    group_offsets int32 [G+1] in device memory (rows of group g are
+    [offsets[g], offsets[g+1])).  Returns Y bf16 [M_total, N].
+    """
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 3)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 3)
+    poff = _dev(group_offsets, "group_offsets", torch.int32, 1)
+    M, K = a_q.shape
+    G, N, Kb = b_q.shape
+    if Kb != K or tuple(a_s.shape) != (M, K // 128) or tuple(b_s.shape) != (G, N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    if group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must have G+1 entries")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
+    py = _dev(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_grouped_gemm",
+               _lib.load().fp8_grouped_gemm(pa, pas, pb, pbs, poff, G, M, N, K, py, _stream(a_q)))
+    return y

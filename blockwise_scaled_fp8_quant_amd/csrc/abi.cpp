@@ -1,0 +1,146 @@
+// C ABI entry points (declared in include/fp8q.h): argument checks on the
+// host, then the kernel launch on the caller's stream.  Nothing here touches
+// the device before every check has passed.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/fp8q.h"
+#include "fp8q_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp8q_status fail(fp8q_status st, const char *fn, const char *what) {
+  g_last_error = std::string(fn) + ": " + what;
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device check that the current device is a gfx950 (cached).
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+fp8q_status check_device(const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(FP8Q_EDEVICE, fn, e != hipSuccess ? hipGetErrorString(e) : "no usable HIP device");
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    g_dev_ok[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                     std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+  });
+  if (!g_dev_ok[dev]) return fail(FP8Q_EDEVICE, fn, "current device is not gfx950 (MI355X)");
+  return FP8Q_OK;
+}
+
+fp8q_status launched(hipError_t e, const char *fn) {
+  if (e != hipSuccess) return fail(FP8Q_EHIP, fn, hipGetErrorString(e));
+  return FP8Q_OK;
+}
+
+#define FP8Q_REQUIRE(cond, st, msg) \
+  do {                              \
+    if (!(cond)) return fail(st, __func__, msg); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q,
+                                float *scales, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(M >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  if (M == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(x && q && scales, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(x) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,
+               "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_quant_act_1x128(x, M, K, q, scales, mode, (hipStream_t)stream), __func__);
+}
+
+fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q,
+                                     float *scales, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
+  if (N == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(w && q && scales, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(w) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,
+               "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_quant_weight_128x128(w, N, K, q, scales, mode, (hipStream_t)stream),
+                  __func__);
+}
+
+fp8q_status fp8_blockscaled_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                 const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                 void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(M >= 0 && N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
+  FP8Q_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, FP8Q_EINVAL, "M or N too large");
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_blockscaled_gemm(a_q, a_s, b_q, b_s, y, M, N, K, (hipStream_t)stream),
+                  __func__);
+}
+
+fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                             const float *b_s, const int32_t *group_offsets, int32_t G,
+                             int64_t M_total, int64_t N, int64_t K, uint16_t *y, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(G >= 1, FP8Q_EINVAL, "G must be >= 1");
+  FP8Q_REQUIRE(M_total >= 0 && N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
+  FP8Q_REQUIRE(M_total < ((int64_t)1 << 31) && N <= ((int64_t)1 << 31), FP8Q_EINVAL,
+               "M_total or N too large");
+  if (M_total == 0 || N == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y && group_offsets, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y) &&
+                   aligned16(group_offsets),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y,
+                                            (hipStream_t)stream),
+                  __func__);
+}
+
+const char *fp8q_status_string(int status) {
+  switch (status) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_EINVAL: return "invalid argument";
+    case FP8Q_ESHAPE: return "unsupported shape";
+    case FP8Q_EALIGN: return "misaligned pointer";
+    case FP8Q_EDEVICE: return "unsupported or missing device";
+    case FP8Q_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *fp8q_last_error(void) { return g_last_error.c_str(); }
+
+int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// Kernel launchers behind the C ABI (host side).  Arguments are validated by
+// the ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
+                                  uint8_t *q, float *s, int mode,
+                                  hipStream_t stream);
+
+hipError_t launch_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
+                                       uint8_t *q, float *s, int mode,
+                                       hipStream_t stream);
+
+hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
+                                   const uint8_t *b_q, const float *b_s,
+                                   uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                   hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
+                               const uint8_t *b_q, const float *b_s,
+                               const int32_t *group_offsets, int32_t G,
+                               int64_t M_total, int64_t N, int64_t K,
+                               uint16_t *y, hipStream_t stream);
+
+}  // namespace fp8q

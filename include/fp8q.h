@@ -1,0 +1,153 @@
+/*
+ * fp8q.h -- C ABI of the blockwise-scaled FP8 linear layer for AMD MI355X
+ * (CDNA4, gfx950).
+ *
+ * The layer is the one of the end-to-end FP8 reinforcement-learning recipe
+ * described on the page "NVIDIA NeMo RL erreicht 48% Geschwindigkeitssteigerung
+ * mit End-to-End FP8-Praezisionstraining":
+ *   - section "Der technische Durchbruch": linear layers compute in FP8 E4M3,
+ *     with one scale per 1x128 block of activations and one per 128x128 block
+ *     of weights;
+ *   - section "Leistungsgewinne in der Praxis": the weight scales are
+ *     recalibrated (and the weights requantized) after every policy update;
+ *   - section "Warum dies fuer die KI-Oekonomie wichtig ist": the scales may be
+ *     restricted to powers of two.
+ * The +-448 range of E4M3 is from the page "FP8 Trainingsinfrastructuur:
+ * Numerieke Precisie van de Volgende Generatie", section "Het landschap van
+ * numerieke precisie".
+ *
+ * Conventions shared by every entry point
+ *  - Memory: every tensor pointer is DEVICE memory, allocated and owned by the
+ *    caller.  The library allocates nothing and keeps no per-call state; it is
+ *    reentrant and may be called from several host threads.
+ *  - Layout: all tensors are dense and row-major, no strides.  bf16 values are
+ *    passed as their raw 16-bit patterns, E4M3 values as raw bytes (OCP
+ *    "E4M3FN": bias 7, largest finite 448, NaN only 0x7F/0xFF), scales as fp32.
+ *  - Scales are dequantisation multipliers: x ~= decode(q) * s.
+ *  - Alignment: every pointer must be 16-byte aligned (torch allocations are).
+ *  - Shapes: K is a positive multiple of 128; N is a multiple of 128; M (and
+ *    every group size) is any value >= 0 -- ragged tails are masked.  M == 0 or
+ *    N == 0 is a valid empty call that enqueues nothing.
+ *  - Execution: each call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *    is the null stream) and returns without synchronising.  The outputs are
+ *    valid once the stream reaches that point.
+ *  - Errors: arguments are checked on the host before anything is enqueued; on
+ *    any error nothing is enqueued and the outputs are untouched.  A HIP launch
+ *    failure returns FP8Q_EHIP.  fp8q_last_error() gives a message for the last
+ *    failing call of the calling thread.
+ *  - Inputs must be finite (no NaN or Inf); the results for other inputs are
+ *    unspecified but every access stays inside the given tensors.
+ *  - Determinism: the same inputs give the same output bits on every call.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum fp8q_status {
+    FP8Q_OK = 0,
+    FP8Q_EINVAL = 1,  /* null pointer, negative size, unknown mode, G < 1 */
+    FP8Q_ESHAPE = 2,  /* K not a positive multiple of 128, or N not a multiple of 128 */
+    FP8Q_EALIGN = 3,  /* a pointer not 16-byte aligned */
+    FP8Q_EDEVICE = 4, /* no HIP device, or the current device is not gfx950 */
+    FP8Q_EHIP = 5     /* the HIP runtime reported an error while enqueueing */
+} fp8q_status;
+
+/* Scale rule of one block whose largest magnitude is amax.  An all-zero block
+ * (amax == 0) always gets s = 1. */
+typedef enum fp8q_scale_mode {
+    FP8Q_SCALE_AMAX = 0, /* s = amax / 448, rounded to the nearest fp32 */
+    FP8Q_SCALE_POW2 = 1  /* s = 2^e, e the smallest integer with 448 * 2^e >= amax */
+} fp8q_scale_mode;
+
+/*
+ * Dynamic activation quantization, 1x128 blocks (page 1, "Der technische
+ * Durchbruch").
+ *   x       [M][K] bf16 bits (in)
+ *   q       [M][K] E4M3 bytes (out)
+ *   scales  [M][K/128] fp32 (out): block (m, kb) covers x[m][128*kb .. 128*kb+127]
+ *   mode    fp8q_scale_mode
+ * Every element: q = E4M3(RN_fp32(x / s)), rounded to nearest with ties to an
+ * even mantissa and saturated to +-448; a zero keeps its sign.
+ * The result is bit-identical to that rule for every finite input.
+ */
+fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
+                                uint8_t *q, float *scales, int mode,
+                                void *stream);
+
+/*
+ * Weight recalibration and requantization, 128x128 blocks (page 1, "Der
+ * technische Durchbruch" and "Leistungsgewinne in der Praxis"; power-of-two
+ * mode: "Warum dies fuer die KI-Oekonomie wichtig ist").
+ *   w       [N][K] bf16 bits (in), N and K multiples of 128
+ *   q       [N][K] E4M3 bytes (out)
+ *   scales  [N/128][K/128] fp32 (out): tile (nb, kb) covers rows 128*nb.. and
+ *           columns 128*kb.. (127 more each)
+ *   mode    fp8q_scale_mode
+ * Element rule as in fp8_quant_act_1x128, with the tile's scale.
+ */
+fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
+                                     uint8_t *q, float *scales, int mode,
+                                     void *stream);
+
+/*
+ * Block-scaled FP8 GEMM of a linear layer, Y = X * W^T (page 1, "Der
+ * technische Durchbruch"; the GEMM outputs feed bf16 operators):
+ *   Y[m][n] = sum_kb a_s[m][kb] * b_s[n/128][kb] *
+ *                    sum_{k in block kb} dec(a_q[m][k]) * dec(b_q[n][k])
+ * with fp32 accumulation; Y is rounded once to bf16 (nearest, ties to even).
+ *   a_q [M][K] E4M3, a_s [M][K/128] fp32   (from fp8_quant_act_1x128)
+ *   b_q [N][K] E4M3, b_s [N/128][K/128]     (from fp8_quant_weight_128x128)
+ *   y   [M][N] bf16 bits (out)
+ * The summation order inside the GPU is fixed but unspecified; results agree
+ * with the exact value to within fp32 accumulation and the final bf16 rounding.
+ */
+fp8q_status fp8_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
+                                 const uint8_t *b_q, const float *b_s,
+                                 uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                 void *stream);
+
+/*
+ * Grouped block-scaled FP8 GEMM for mixture-of-experts layers (the recipe's
+ * MoE models on page 1, "Leistungsgewinne in der Praxis" and "Warum dies fuer
+ * die KI-Oekonomie wichtig ist"): group g owns rows
+ * [group_offsets[g], group_offsets[g+1]) of a_q, a_s and y and multiplies them
+ * by its own weight matrix.
+ *   a_q [M_total][K], a_s [M_total][K/128]
+ *   b_q [G][N][K],    b_s [G][N/128][K/128]
+ *   group_offsets [G+1] int32, DEVICE memory: non-decreasing, offsets[0] = 0,
+ *                 offsets[G] = M_total.  Empty groups are allowed.  The offsets
+ *                 are read on the device (no host synchronisation); values
+ *                 outside [0, M_total] are clamped and a decrease is treated as
+ *                 an empty group, so a malformed array cannot cause an access
+ *                 outside the tensors (rows no group covers are left unwritten).
+ *   y   [M_total][N] bf16 bits (out)
+ * Per group the arithmetic is that of fp8_blockscaled_gemm.
+ */
+fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s,
+                             const uint8_t *b_q, const float *b_s,
+                             const int32_t *group_offsets, int32_t G,
+                             int64_t M_total, int64_t N, int64_t K,
+                             uint16_t *y, void *stream);
+
+/* Static English text of a status code (never NULL). */
+const char *fp8q_status_string(int status);
+
+/* Message of the last failing call on the calling thread ("" if none).  The
+ * pointer stays valid until the next call of this library on the thread. */
+const char *fp8q_last_error(void);
+
+/* FP8Q_ABI_VERSION of the built library. */
+int fp8q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports every entry point that include/fp8q.h
+declares, and rejects bad arguments on the host before touching any device
+(these calls never reach a kernel, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from blockwise_scaled_fp8_quant_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from blockwise_scaled_fp8_quant_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8\w*)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
+              "fp8_grouped_gemm", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fp8q_abi_version() == 1
+    for st in range(6):
+        assert lib.fp8q_status_string(st)
+    assert lib.fp8q_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)      # a 16-byte-aligned address that is never dereferenced
+ODD = P(0x10008)
+
+
+def _err(lib):
+    return lib.fp8q_last_error().decode()
+
+
+@pytest.mark.parametrize("fn", ["fp8_quant_act_1x128", "fp8_quant_weight_128x128"])
+def test_quantizer_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    assert f(GOOD, 128, 100, GOOD, GOOD, 0, None) == 2          # K % 128
+    assert f(GOOD, 128, 0, GOOD, GOOD, 0, None) == 2            # K == 0
+    assert f(GOOD, -1, 128, GOOD, GOOD, 0, None) == 1           # negative size
+    assert f(GOOD, 128, 128, GOOD, GOOD, 7, None) == 1          # unknown mode
+    assert "mode" in _err(lib)
+    assert f(None, 128, 128, GOOD, GOOD, 0, None) == 1          # null pointer
+    assert f(GOOD, 128, 128, None, GOOD, 1, None) == 1
+    assert f(ODD, 128, 128, GOOD, GOOD, 0, None) == 3           # misaligned
+    assert f(GOOD, 0, 128, None, None, 0, None) == 0            # empty: no-op
+    if fn == "fp8_quant_weight_128x128":
+        assert f(GOOD, 100, 128, GOOD, GOOD, 0, None) == 2      # N % 128
+
+
+def test_gemm_argument_errors(lib):
+    f = lib.fp8_blockscaled_gemm
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, None) == 2
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 100, 128, None) == 2
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, -1, 128, 128, None) == 1
+    assert f(GOOD, None, GOOD, GOOD, GOOD, 64, 128, 128, None) == 1
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, 64, 128, 128, None) == 3
+    assert f(None, None, None, None, None, 0, 128, 128, None) == 0
+
+
+def test_grouped_argument_errors(lib):
+    f = lib.fp8_grouped_gemm
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 128, 128, GOOD, None) == 1   # G < 1
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 100, GOOD, None) == 2
+    assert f(GOOD, GOOD, GOOD, GOOD, None, 2, 64, 128, 128, GOOD, None) == 1   # null offsets
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, None) == 3
+    assert f(None, None, None, None, None, 3, 0, 128, 128, None, None) == 0
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.fp8_quant_act_1x128(GOOD, 1, 128, GOOD, GOOD, 0, None) == 4
+    assert "device" in _err(lib) or "HIP" in _err(lib) or _err(lib)
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    import blockwise_scaled_fp8_quant_amd as fp8q
+    with pytest.raises(ValueError):
+        fp8q.fp8_quant_act_1x128(torch.zeros((4, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fp8q.fp8_quant_act_1x128(torch.zeros((4, 128), dtype=torch.bfloat16), mode="nope")
