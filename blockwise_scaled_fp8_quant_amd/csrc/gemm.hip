@@ -11,20 +11,26 @@
 //  - One v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, neutral E8M0 scales)
 //    covers exactly one 128-wide scale block of K, so P_kb comes out of a
 //    single MFMA with a zero accumulator and is folded into the fp32
-//    accumulator with one FMA per output: acc += P_kb * (a_s * b_s).
+//    accumulator with one FMA per output: acc += P_kb * (a_s * b_s).  The
+//    FMAs run on the VALU while the matrix core works on the next MFMAs.
 //  - The weight tile is the MFMA "A" operand (rows of D) and the token tile the
 //    "B" operand (columns of D).  Then each lane's four outputs are four
 //    consecutive n of one token row m: they share one scale product and are
-//    stored as one 8-byte bf16 quad.  b_s is uniform per wave (scalar load).
-//  - Tiles of 256 (n) x 128 (m) x 128 (k); 4 waves in a 2x2 grid, each owning
-//    128 n x 64 m = 8 x 4 MFMA sub-tiles (128 fp32 accumulators per lane).
-//  - Operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4,
-//    16 B per lane, one 1 KB piece per wave instruction), double-buffered so
-//    the next K block streams in while the current one is multiplied.  Rows
-//    are 128 B; 16-byte chunks are XOR-swizzled by row so that the fragment
-//    reads (two ds_read_b128 per lane) hit distinct banks.
+//    stored as one 8-byte bf16 quad.
+//  - Each wave owns 128 (n) x 64 (m) outputs = 8 x 4 MFMA sub-tiles (128 fp32
+//    accumulators per lane).  Two tile shapes:
+//      256 x 256 tiles, 8 waves (2 per SIMD), 2-stage pipeline  (large M)
+//      256 x 128 tiles, 4 waves (1 per SIMD), 3-stage pipeline  (small M,
+//                                                                 grouped)
+//  - Everything a K block needs -- the weight and token tiles and both scale
+//    vectors -- reaches LDS by direct global->LDS DMA (global_load_lds), so a
+//    stage is a fixed number of vector-memory instructions per wave and the
+//    wait for stage k is one s_waitcnt vmcnt(<later stages' count>).
+//  - Rows are 128 B in LDS; 16-byte chunks are XOR-swizzled by row so that the
+//    fragment reads (two ds_read_b128 per lane) hit distinct banks.
 //  - Workgroup ids are remapped so that each XCD (own L2) gets a contiguous
-//    range of tiles that share operand panels.
+//    range of tiles, enumerated in groups of 4 weight panels so that the tiles
+//    running at the same time share operand panels.
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 
@@ -36,14 +42,38 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kBN = 256;  // weight rows per tile
-constexpr int kBM = 128;  // token rows per tile
 constexpr int kBK = 128;  // one scale block of K
-constexpr int kThreads = 256;
 constexpr int kSubN = 8;  // 16-row MFMA sub-tiles per wave along n (128 rows)
 constexpr int kSubM = 4;  // 16-col MFMA sub-tiles per wave along m (64 rows)
-constexpr int kTileBytesB = kBN * kBK;
-constexpr int kTileBytesA = kBM * kBK;
 constexpr int kNumXcd = 8;
+constexpr int kGroupN = 4;  // weight panels per rasterization group
+
+template <int kBM_, int kWaves_, int kStages_>
+struct TileCfg {
+  static constexpr int kBM = kBM_;
+  static constexpr int kWaves = kWaves_;
+  static constexpr int kStages = kStages_;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesM = kWaves / 2;  // waves along m; 2 along n
+  static_assert(kBM == 64 * kWavesM, "each wave owns 64 token rows");
+  static constexpr int kBytesB = kBN * kBK;        // weight tile
+  static constexpr int kBytesA = kBM * kBK;        // token tile
+  static constexpr int kBytesSA = kBM * 4;         // activation scales
+  static constexpr int kBytesSB = kWaves * 8;      // weight scales (per-wave copy)
+  static constexpr int kOffA = kBytesB;
+  static constexpr int kOffSA = kOffA + kBytesA;
+  static constexpr int kOffSB = kOffSA + kBytesSA;
+  static constexpr int kStageBytes = (kOffSB + kBytesSB + 1023) / 1024 * 1024;
+  static constexpr int kLdsBytes = kStageBytes * kStages;
+  static constexpr int kPiecesB = kBytesB / 1024 / kWaves;  // 1 KB DMA pieces per wave
+  static constexpr int kPiecesA = kBytesA / 1024 / kWaves;
+  static_assert(kBM / kWaves == 32, "32 activation scales per wave");
+  static constexpr int kLoadsPerStage = kPiecesB + kPiecesA + 2;  // + sa, sb
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+using CfgLarge = TileCfg<256, 8, 2>;
+using CfgSmall = TileCfg<128, 4, 3>;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -51,21 +81,61 @@ constexpr int kNumXcd = 8;
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
-// Stage one K block (128 bytes per row) of kRows rows into LDS.  src points at
-// row 0 of the tile at the block's first column; rows >= rows_valid read row
-// rows_valid-1 instead (their products only reach masked outputs).
-template <int kRows>
-__device__ __forceinline__ void stage(const uint8_t *src, int64_t ld, int rows_valid,
-                                      uint8_t *lds, int wave, int lane) {
-  constexpr int kPerWave = kRows / 8 / (kThreads / 64);
+// Position in the activation-scale vector of row r = wm*64 + mi*16 + j:
+// wm*64 + j*4 + mi, so that lane j of a wave reads its four rows (mi = 0..3)
+// with one 16-byte LDS read.
+__device__ __forceinline__ int sa_row_of_pos(int p) {
+  const int wm = p >> 6, j = (p & 63) >> 2, mi = p & 3;
+  return wm * 64 + mi * 16 + j;
+}
+
+struct TileJob {
+  const uint8_t *a_q;  // row 0 of the token tile
+  const float *a_s;    // scale row of token row 0
+  const uint8_t *b_q;  // row 0 of the weight tile
+  const float *b_s;    // weight-scale row of the tile's first 128 rows
+  int m_valid;         // token rows in the tile (1..kBM)
+  int n_valid;         // weight rows in the tile (128 or 256)
+  int64_t K;
+  int KB;
+};
+
+// Issue the DMA of K block k into one stage buffer: kPiecesB + kPiecesA
+// 16-byte loads, one 4-byte activation-scale load (32 lanes) and one weight-
+// scale load (2 lanes) per wave -- exactly kLoadsPerStage vector-memory
+// instructions.  Rows past the valid range read the last valid row (their
+// products only reach masked outputs).
+template <class C>
+__device__ __forceinline__ void issue_stage(const TileJob &t, int k, uint8_t *buf, int wave, int lane) {
+  const int64_t kbyte = (int64_t)k * kBK;
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int piece = wave * kPerWave + i;
+  for (int i = 0; i < C::kPiecesB; ++i) {
+    const int piece = wave * C::kPiecesB + i;
     const int r = piece * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    const int rg = r < rows_valid ? r : rows_valid - 1;
-    const uint8_t *g = src + (int64_t)rg * ld + (c << 4);
-    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(lds + piece * 1024), 16, 0, 0);
+    const int rg = r < t.n_valid ? r : t.n_valid - 1;
+    const uint8_t *g = t.b_q + (int64_t)rg * t.K + kbyte + (c << 4);
+    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + piece * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kPiecesA; ++i) {
+    const int piece = wave * C::kPiecesA + i;
+    const int r = piece * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const int rg = r < t.m_valid ? r : t.m_valid - 1;
+    const uint8_t *g = t.a_q + (int64_t)rg * t.K + kbyte + (c << 4);
+    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, 0, 0);
+  }
+  if (lane < 32) {
+    int r = sa_row_of_pos(wave * 32 + lane);
+    r = r < t.m_valid ? r : t.m_valid - 1;
+    const float *g = t.a_s + (int64_t)r * t.KB + k;
+    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffSA + wave * 128), 4, 0, 0);
+  }
+  if (lane < 2) {
+    const int nb = (lane * 128 < t.n_valid) ? lane : 0;
+    const float *g = t.b_s + (int64_t)nb * t.KB + k;
+    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffSB + wave * 8), 4, 0, 0);
   }
 }
 
@@ -90,13 +160,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));  // RNE
 }
 
-// One K block: fragments from LDS, 32 MFMAs, 128 FMAs per lane.  Software
-// pipelined by hand: the four MFMAs of sub-tile row ni+1 are issued before the
-// FMAs that fold row ni into the accumulators, so the matrix core always has
-// independent work while the VALU applies the scales.
-__device__ __forceinline__ void mma_block(const uint8_t *tb, const uint8_t *ta, int wn, int wm,
-                                          int lane, const float (&scl)[kSubM],
+// One K block of one wave: fragments from LDS, 32 MFMAs, 128 FMAs per lane.
+// Software pipelined: the four MFMAs of sub-tile row ni+1 are issued before
+// the FMAs that fold row ni into the accumulators.
+template <class C>
+__device__ __forceinline__ void mma_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
                                           v4f (&acc)[kSubN][kSubM]) {
+  const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
+  const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wave * 8 + wn * 4);
+  const float scl[kSubM] = {sa4.x * sb, sa4.y * sb, sa4.z * sb, sa4.w * sb};
+  const uint8_t *tb = buf;
+  const uint8_t *ta = buf + C::kOffA;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   v8i xf[kSubM];
 #pragma unroll
@@ -125,30 +199,32 @@ __device__ __forceinline__ void mma_block(const uint8_t *tb, const uint8_t *ta, 
   }
 }
 
-// One output tile: rows [m0, m0 + m_valid) of A/Y (m_valid in 1..128) and
-// columns [n0, n0 + n_valid) of Y (n_valid 128 or 256) against weights b_q.
-__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ a_q, const float *__restrict__ a_s,
-                                          const uint8_t *__restrict__ b_q, const float *__restrict__ b_s,
-                                          uint16_t *__restrict__ y, int64_t m0, int m_valid, int64_t n0,
-                                          int n_valid, int64_t N, int64_t K, uint8_t *buf0, uint8_t *buf1) {
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence.  The only LDS writes are the DMA
+// stages, whose completion each wave establishes with wait_vmcnt before it
+// arrives; every LDS read of a buffer is consumed (lgkmcnt-waited) before the
+// wave arrives at the barrier that allows the buffer to be refilled.  A fenced
+// __syncthreads() would also wait for the DMA of the blocks still in flight.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
+// n_valid), written to y (row stride N) at y[0][0].
+template <class C>
+__device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict__ y, int64_t N,
+                                          uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
-  const int KB = (int)(K / kBK);
-  const uint8_t *ga = a_q + m0 * K;
-  const uint8_t *gb = b_q + n0 * K;
-
-  int64_t srow[kSubM];
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) {
-    int r = wm * 64 + mi * 16 + (lane & 15);
-    r = r < m_valid ? r : m_valid - 1;
-    srow[mi] = (m0 + r) * KB;
-  }
-  // weight-scale row of this wave's 128 columns (a wave past n_valid reads the
-  // tile's first row instead; its outputs are masked)
-  const int nbw = (int)(n0 >> 7) + ((wn * 128 < n_valid) ? wn : 0);
-  const float *sbrow = b_s + (int64_t)nbw * KB;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int KB = t.KB;
 
   v4f acc[kSubN][kSubM];
 #pragma unroll
@@ -156,52 +232,36 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ a_q, const
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  float sa[kSubM], sb;
-  stage<kBN>(gb, K, n_valid, buf0, wave, lane);
-  stage<kBM>(ga, K, m_valid, buf0 + kTileBytesB, wave, lane);
 #pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) sa[mi] = a_s[srow[mi]];
-  sb = sbrow[0];
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < KB) issue_stage<C>(t, s, lds + s * C::kStageBytes, wave, lane);
 
-  // K loop unrolled by two so that each half reads one buffer and fills the
-  // other; the barrier at the top of a half guarantees every wave finished
-  // reading the buffer that the half's DMA overwrites.
-  for (int kb = 0; kb < KB; kb += 2) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k = kb + half;
-      if (k < KB) {
-        uint8_t *cur = half ? buf1 : buf0;
-        uint8_t *nxt = half ? buf0 : buf1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        // scales of this block were loaded one step ahead, so the wait above
-        // was the only one; the next block's scales ride with its DMA
-        float scl[kSubM];
-#pragma unroll
-        for (int mi = 0; mi < kSubM; ++mi) scl[mi] = sa[mi] * sb;
-        if (k + 1 < KB) {
-          stage<kBN>(gb + (int64_t)(k + 1) * kBK, K, n_valid, nxt, wave, lane);
-          stage<kBM>(ga + (int64_t)(k + 1) * kBK, K, m_valid, nxt + kTileBytesB, wave, lane);
-#pragma unroll
-          for (int mi = 0; mi < kSubM; ++mi) sa[mi] = a_s[srow[mi] + k + 1];
-          sb = sbrow[k + 1];
-        }
-        mma_block(cur, cur + kTileBytesB, wn, wm, lane, scl, acc);
-      }
-    }
+  int cur = 0;                   // stage buffer of block k
+  int nxt = C::kStages - 1;      // stage buffer of block k + kStages - 1
+  for (int k = 0; k < KB; ++k) {
+    // Block k has landed once at most the loads of the later blocks already
+    // issued (k+1 .. k+kStages-2) are still in flight.
+    if (k + C::kStages - 2 < KB)
+      wait_vmcnt<C::kLoadsPerStage * (C::kStages - 2)>();
+    else
+      wait_vmcnt<0>();
+    barrier_nofence();  // everyone's block k is in LDS; everyone is done with block k-1
+    if (k + C::kStages - 1 < KB) issue_stage<C>(t, k + C::kStages - 1, lds + nxt * C::kStageBytes, wave, lane);
+    mma_block<C>(lds + cur * C::kStageBytes, wave, wn, wm, lane, acc);
+    cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
+    nxt = (nxt + 1 == C::kStages) ? 0 : nxt + 1;
   }
 
   // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) {
     const int r = wm * 64 + mi * 16 + (lane & 15);
-    if (r < m_valid) {
-      uint16_t *yrow = y + (m0 + r) * N + n0;
+    if (r < t.m_valid) {
+      uint16_t *yrow = y + (int64_t)r * N;
 #pragma unroll
       for (int ni = 0; ni < kSubN; ++ni) {
         const int nn = wn * 128 + ni * 16 + 4 * (lane >> 4);
-        if (nn < n_valid) {
+        if (nn < t.n_valid) {
           uint2 o;
           o.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
           o.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
@@ -220,6 +280,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nwg) {
   return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// Logical id -> (m slot, n tile): groups of kGroupN weight panels; inside a
+// group the m slot varies slowest... fastest over the group's n tiles.
+__device__ __forceinline__ void raster(int64_t L, int64_t slots_m, int64_t tiles_n, int64_t &tm,
+                                       int64_t &tn) {
+  const int64_t per_group = (int64_t)kGroupN * slots_m;
+  const int64_t g = L / per_group;
+  const int64_t r = L - g * per_group;
+  const int64_t n0 = g * kGroupN;
+  const int64_t gw = (tiles_n - n0) < kGroupN ? (tiles_n - n0) : kGroupN;
+  tm = r / gw;
+  tn = n0 + (r - tm * gw);
+}
+
 struct GemmParams {
   const uint8_t *a_q;
   const float *a_s;
@@ -229,6 +302,7 @@ struct GemmParams {
   uint16_t *y;
   int64_t M;  // dense: M; grouped: M_total
   int64_t N, K;
+  int64_t slots_m;
   int32_t G;
   int32_t tiles_n;
 };
@@ -238,20 +312,18 @@ __device__ __forceinline__ int64_t clamp_off(const int32_t *off, int32_t g, int6
   return v < 0 ? 0 : (v > M ? M : v);
 }
 
-// Dense: logical tile L -> (m tile L / tiles_n, n tile L % tiles_n).
-// Grouped: group g owns the m-tile slots [S_g, S_{g+1}) with
-// S_g = floor(off[g] / 128) + g, which always holds ceil(rows_g / 128) tiles;
-// a slot beyond its group's rows exits at once.  The group of a slot is found
-// by binary search over S (wave-uniform, scalar loads), so no prefix sums or
-// workspace are needed and the offsets never leave the device.
-template <bool kGrouped>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytesB + kTileBytesA];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytesB + kTileBytesA];
+// Dense: m slot = m tile.  Grouped: group g owns the m slots [S_g, S_{g+1})
+// with S_g = floor(off[g] / kBM) + g, which always holds ceil(rows_g / kBM)
+// tiles; a slot beyond its group's rows exits at once.  The group of a slot is
+// found by binary search over S (wave-uniform, scalar loads), so no prefix sums
+// or workspace are needed and the offsets never leave the device.
+template <class C, bool kGrouped>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t tm = L / p.tiles_n;
-  const int64_t tn = L - tm * p.tiles_n;
+  int64_t tm, tn;
+  raster(L, p.slots_m, p.tiles_n, tm, tn);
   const int64_t n0 = tn * kBN;
   const int n_valid = (int)((p.N - n0) < kBN ? (p.N - n0) : kBN);
 
@@ -259,26 +331,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
   const uint8_t *bq = p.b_q;
   const float *bs = p.b_s;
   if (!kGrouped) {
-    m0 = tm * kBM;
+    m0 = tm * C::kBM;
     m_end = p.M;
   } else {
     int32_t lo = 0, hi = p.G;  // largest g in [0, G) with S_g <= tm
     while (hi - lo > 1) {
       const int32_t mid = (lo + hi) >> 1;
-      const int64_t s = clamp_off(p.offsets, mid, p.M) / kBM + mid;
+      const int64_t s = clamp_off(p.offsets, mid, p.M) / C::kBM + mid;
       if (s <= tm) lo = mid; else hi = mid;
     }
     const int32_t g = lo;
     const int64_t g0 = clamp_off(p.offsets, g, p.M);
     const int64_t g1 = clamp_off(p.offsets, g + 1, p.M);
-    m0 = g0 + (tm - (g0 / kBM + g)) * kBM;
+    m0 = g0 + (tm - (g0 / C::kBM + g)) * C::kBM;
     m_end = g1;
     bq += (int64_t)g * p.N * p.K;
     bs += (int64_t)g * (p.N / 128) * (p.K / kBK);
   }
   if (m0 >= m_end || m0 < 0) return;
-  const int m_valid = (int)((m_end - m0) < kBM ? (m_end - m0) : kBM);
-  gemm_tile(p.a_q, p.a_s, bq, bs, p.y, m0, m_valid, n0, n_valid, p.N, p.K, buf0, buf1);
+
+  TileJob t;
+  t.KB = (int)(p.K / kBK);
+  t.K = p.K;
+  t.a_q = p.a_q + m0 * p.K;
+  t.a_s = p.a_s + m0 * t.KB;
+  t.b_q = bq + n0 * p.K;
+  t.b_s = bs + (n0 >> 7) * t.KB;
+  t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
+  t.n_valid = n_valid;
+  gemm_tile<C>(t, p.y + m0 * p.N + n0, p.N, lds);
+}
+
+template <class C, bool kGrouped>
+static hipError_t launch(GemmParams p, hipStream_t stream) {
+  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = p.slots_m * p.tiles_n;
+  hipLaunchKernelGGL((gemm_kernel<C, kGrouped>), dim3((unsigned)grid), dim3(C::kThreads),
+                     C::kLdsBytes, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
@@ -286,11 +382,16 @@ hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
                                    uint16_t *y, int64_t M, int64_t N, int64_t K,
                                    hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, M, N, K, 1, (int32_t)((N + kBN - 1) / kBN)};
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t grid = tiles_m * p.tiles_n;
-  hipLaunchKernelGGL(gemm_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
+  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, M, N, K, 0, 1, tiles_n};
+  // Large tiles when they still give at least one tile per CU.
+  const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
+  if (large_tiles >= 256) {
+    p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
+    return launch<CfgLarge, false>(p, stream);
+  }
+  p.slots_m = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  return launch<CfgSmall, false>(p, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
@@ -299,12 +400,10 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                int64_t M_total, int64_t N, int64_t K,
                                uint16_t *y, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K, G,
-               (int32_t)((N + kBN - 1) / kBN)};
-  const int64_t slots_m = M_total / kBM + G;
-  const int64_t grid = slots_m * p.tiles_n;
-  hipLaunchKernelGGL(gemm_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K,
+               M_total / CfgSmall::kBM + G, G, tiles_n};
+  return launch<CfgSmall, true>(p, stream);
 }
 
 }  // namespace fp8q

@@ -90,16 +90,16 @@ def test_special_blocks(mode):
     rows[2, ::5] |= 0x8000
     rows[3, :] = 0x7F7F                                        # bf16 max
     rows[3, 1::2] = 0xFF7F
-    rows[4, :] = synth.bf16_bits(torch.linspace(-448, 448, 256))
-    rows[5, :] = synth.bf16_bits(torch.full((256,), 1e-35))    # amax < 2^-100
+    rows[4, :] = synth.bf16_bits(torch.linspace(-448, 448, 256).to(torch.bfloat16))
+    rows[5, :] = synth.bf16_bits(torch.full((256,), 1e-35).to(torch.bfloat16))    # amax < 2^-100
     rows[5, 7] = 0x8001
-    rows[6, :] = synth.bf16_bits(torch.randn(256) * 1e30)
+    rows[6, :] = synth.bf16_bits((torch.randn(256) * 1e30).to(torch.bfloat16))
     rows[7, :128] = 0x0001                                     # min subnormal block
-    rows[8, :] = synth.bf16_bits(torch.randn(256))
-    rows[8, 3] = synth.bf16_bits(torch.tensor([3.0e4]))[0]     # one large outlier
-    rows[9, :] = synth.bf16_bits(torch.randn(256) * 2.0 ** -110)
-    rows[10, :] = synth.bf16_bits(torch.randn(256) * 2.0 ** -101)
-    rows[11, :] = synth.bf16_bits(torch.randn(256) * 2.0 ** 100)
+    rows[8, :] = synth.bf16_bits(torch.randn(256).to(torch.bfloat16))
+    rows[8, 3] = synth.bf16_bits(torch.tensor([3.0e4]).to(torch.bfloat16))[0]     # one large outlier
+    rows[9, :] = synth.bf16_bits((torch.randn(256) * 2.0 ** -110).to(torch.bfloat16))
+    rows[10, :] = synth.bf16_bits((torch.randn(256) * 2.0 ** -101).to(torch.bfloat16))
+    rows[11, :] = synth.bf16_bits((torch.randn(256) * 2.0 ** 100).to(torch.bfloat16))
     _act_parity(rows, mode, "special blocks")
     # one 128x128 weight tile per special pattern: tile j repeats row j's first
     # 128 values, rotated by one more position on every row
