@@ -40,6 +40,50 @@ def weight_quant_bytes(N, K):
     return N * K * 3 + (N // 128) * (K // 128) * 4
 
 
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_llama4096_traffic.txt")
+GEMM_SOURCES = ("blockwise_scaled_fp8_quant_amd/csrc/gemm.hip",
+                "blockwise_scaled_fp8_quant_amd/csrc/fp8q_device.h",
+                "blockwise_scaled_fp8_quant_amd/build.py")
+
+
+def gemm_source_digest():
+    """sha256 over the GEMM kernel's sources and build flags."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gemm_traffic_per_launch():
+    """HBM bytes per GEMM launch (average over the four layer shapes) from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the
+    copy-kernel calibration stored with it; None when the summary is missing
+    or was taken on other kernel sources."""
+    try:
+        with open(GEMM_TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines()
+                      if "=" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("source_sha256") != gemm_source_digest():
+            return None
+        return float(kv["calibrated_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibration_copy(torch, dev, nbytes=1 << 30, reps=3):
+    """A plain copy of known size (read nbytes, write nbytes) for scaling the
+    HBM counters of a profiler run."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def time_loop(fn, reps, torch):
     """Average duration (s) of fn() over reps launches, HIP events on the
     current stream (the stream the library enqueues on)."""
@@ -63,6 +107,8 @@ def main():
                     help="tokens per layer in the oracle's CPU-baseline sample")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a 1 GiB copy kernel first (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -80,6 +126,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("library", fp8q.library_path())
+    if args.calib_copy:
+        calibration_copy(torch, dev)
 
     # ---- inputs of the step (Llama-3.1-8B-shaped layers, 4096 tokens) ----
     M = synth.LLAMA_TOKENS
@@ -103,20 +151,36 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Timed region.  HIP events on the current stream (the one the library
+    # enqueues on) bracket the whole region and, inside it, every launch, so
+    # the per-kernel averages come from the same launches as the step time.
     log("timing", args.steps, "steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    Ev = torch.cuda.Event
+    marks = [[(Ev(enable_timing=True), Ev(enable_timing=True), Ev(enable_timing=True))
+              for _ in layers] for _ in range(args.steps)]
+    start, end = Ev(enable_timing=True), Ev(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        step()
+    for s in range(args.steps):
+        for l, (e0, e1, e2) in zip(layers, marks[s]):
+            e0.record()
+            fp8q.fp8_quant_act_1x128(l["x"], out=(l["aq"], l["as_"]))
+            e1.record()
+            fp8q.fp8_blockscaled_gemm(l["aq"], l["as_"], l["bq"], l["bs"], out=l["y"])
+            e2.record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_s = start.elapsed_time(end) / 1e3 / args.steps
     value = step_flops / step_s / 1e12
     log(f"step {step_s * 1e3:.3f} ms  ({wall:.3f} s wall for {args.steps} steps)  {value:.1f} TFLOP/s")
+    in_step = {l["name"]: {"quant_s": 0.0, "gemm_s": 0.0} for l in layers}
+    for s in range(args.steps):
+        for l, (e0, e1, e2) in zip(layers, marks[s]):
+            in_step[l["name"]]["quant_s"] += e0.elapsed_time(e1) / 1e3 / args.steps
+            in_step[l["name"]]["gemm_s"] += e1.elapsed_time(e2) / 1e3 / args.steps
 
     result = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)",
@@ -141,18 +205,20 @@ def main():
         },
     }
 
-    # ---- per-kernel timing (events around repeated launches) ----
+    # ---- per-kernel figures from the timed region ----
     reps = max(10, args.steps)
     gemm_s, gemm_flops, per_layer = 0.0, 0.0, {}
     for l in layers:
-        t = time_loop(lambda l=l: fp8q.fp8_blockscaled_gemm(l["aq"], l["as_"], l["bq"], l["bs"], out=l["y"]),
-                      reps, torch)
+        t = in_step[l["name"]]["gemm_s"]
+        tq = in_step[l["name"]]["quant_s"]
         f = 2.0 * M * l["N"] * l["K"]
         gemm_s += t
         gemm_flops += f
-        per_layer[l["name"]] = {"gemm_us": round(t * 1e6, 2), "gemm_tflops": round(f / t / 1e12, 1)}
+        per_layer[l["name"]] = {"gemm_us": round(t * 1e6, 2), "gemm_tflops": round(f / t / 1e12, 1),
+                                "act_quant_in_step_us": round(tq * 1e6, 2)}
     gemm_tflops = gemm_flops / gemm_s / 1e12
-    log(f"gemm {gemm_tflops:.1f} TFLOP/s over the 4 layers")
+    gemm_avg_us = gemm_s / len(layers) * 1e6
+    log(f"gemm {gemm_tflops:.1f} TFLOP/s over the 4 layers (average launch {gemm_avg_us:.2f} us)")
 
     # activation quantization: rotate through >= 1 GB of distinct inputs so the
     # 256 MB last-level cache cannot hold them
@@ -190,7 +256,9 @@ def main():
         "peak": FP8_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-        "traffic": None,
+        "traffic": gemm_traffic_per_launch(),
+        "launch_us": round(gemm_avg_us, 2),
+        "flops_per_launch": gemm_flops / len(layers),
     }
 
     if not args.skip_extras:
