@@ -22,6 +22,10 @@ fp8q_status fail(fp8q_status st, const char *fn, const char *what) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The GEMM kernels address one tile's operands (at most 256 rows of K bytes)
+// with 32-bit buffer offsets.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
+
 // Per-device check that the current device is a gfx950 (cached).
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -95,6 +99,7 @@ fp8q_status fp8_blockscaled_gemm(const uint8_t *a_q, const float *a_s, const uin
   FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
   FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
   FP8Q_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, FP8Q_EINVAL, "M or N too large");
+  FP8Q_REQUIRE(K <= kMaxGemmK, FP8Q_ESHAPE, "K larger than 4194304");
   if (M == 0 || N == 0) return FP8Q_OK;
   FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y, FP8Q_EINVAL, "null pointer");
   FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y),
@@ -115,6 +120,7 @@ fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t
   FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
   FP8Q_REQUIRE(M_total < ((int64_t)1 << 31) && N <= ((int64_t)1 << 31), FP8Q_EINVAL,
                "M_total or N too large");
+  FP8Q_REQUIRE(K <= kMaxGemmK, FP8Q_ESHAPE, "K larger than 4194304");
   if (M_total == 0 || N == 0) return FP8Q_OK;
   FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y && group_offsets, FP8Q_EINVAL, "null pointer");
   FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y) &&

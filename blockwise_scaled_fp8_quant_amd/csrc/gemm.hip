@@ -100,44 +100,98 @@ struct TileJob {
   int KB;
 };
 
-// Issue the DMA of K block k into one stage buffer: kPiecesB + kPiecesA
-// 16-byte loads, one 4-byte activation-scale load (32 lanes) and one weight-
-// scale load (2 lanes) per wave -- exactly kLoadsPerStage vector-memory
-// instructions.  Rows past the valid range read the last valid row (their
-// products only reach masked outputs).
+// Raw buffer resources of one tile's operands.  num_records bounds each one to
+// the tile's valid rows, so a load past them returns zeros (those products only
+// reach masked outputs) and never touches memory outside the tensors.
+struct TileRsrc {
+  __amdgpu_buffer_rsrc_t b, a, sa, sb;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit buffer access
+
+__device__ __forceinline__ TileRsrc make_rsrc(const TileJob &t) {
+  TileRsrc r;
+  r.b = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_q, (short)0, (int)(t.n_valid * t.K), kRsrcWord3);
+  r.a = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_q, (short)0, (int)(t.m_valid * t.K), kRsrcWord3);
+  r.sa = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_s, (short)0, t.m_valid * t.KB * 4, kRsrcWord3);
+  r.sb = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_s, (short)0, ((t.n_valid + 127) >> 7) * t.KB * 4,
+                                           kRsrcWord3);
+  return r;
+}
+
+// Per-lane byte offsets of the DMA pattern (constant over K blocks).  Piece p
+// of a tile holds rows 8p .. 8p+7; lane l fills row 8p + l/8, LDS slot l%8,
+// which holds logical chunk c = (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (p%2).
+struct DmaLane {
+  uint32_t b[2];  // weight tile, even / odd pieces (without the piece's row offset)
+  uint32_t a[2];  // token tile
+  uint32_t sa;    // activation-scale row of this lane (lanes 0..31)
+  uint32_t sb;    // weight-scale row (lanes 0..1)
+};
+
 template <class C>
-__device__ __forceinline__ void issue_stage(const TileJob &t, int k, uint8_t *buf, int wave, int lane) {
-  const int64_t kbyte = (int64_t)k * kBK;
+__device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane) {
+  DmaLane d;
+  const uint32_t row = (uint32_t)(lane >> 3);
+  const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t K = (uint32_t)t.K;
 #pragma unroll
-  for (int i = 0; i < C::kPiecesB; ++i) {
-    const int piece = wave * C::kPiecesB + i;
-    const int r = piece * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const int rg = r < t.n_valid ? r : t.n_valid - 1;
-    const uint8_t *g = t.b_q + (int64_t)rg * t.K + kbyte + (c << 4);
-    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + piece * 1024), 16, 0, 0);
+  for (int par = 0; par < 2; ++par) {
+    d.b[par] = row * K + ((c0 ^ par) << 4);
+    d.a[par] = d.b[par];
   }
-#pragma unroll
-  for (int i = 0; i < C::kPiecesA; ++i) {
-    const int piece = wave * C::kPiecesA + i;
-    const int r = piece * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const int rg = r < t.m_valid ? r : t.m_valid - 1;
-    const uint8_t *g = t.a_q + (int64_t)rg * t.K + kbyte + (c << 4);
-    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, 0, 0);
-  }
-  if (lane < 32) {
-    int r = sa_row_of_pos(wave * 32 + lane);
-    r = r < t.m_valid ? r : t.m_valid - 1;
-    const float *g = t.a_s + (int64_t)r * t.KB + k;
-    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffSA + wave * 128), 4, 0, 0);
-  }
-  if (lane < 2) {
-    const int nb = (lane * 128 < t.n_valid) ? lane : 0;
-    const float *g = t.b_s + (int64_t)nb * t.KB + k;
-    __builtin_amdgcn_global_load_lds((glb_void_t *)g, (lds_void_t *)(buf + C::kOffSB + wave * 8), 4, 0, 0);
+  d.sa = (uint32_t)sa_row_of_pos(wave * 32 + (lane & 31)) * (uint32_t)t.KB * 4u;
+  d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
+  return d;
+}
+
+// The DMA of K block k into one stage buffer is kLoadsPerStage vector-memory
+// instructions per wave: kPiecesB + kPiecesA 16-byte pieces (1 KB each), one
+// 4-byte activation-scale load (32 lanes) and one weight-scale load (2 lanes).
+// issue_piece(q) issues instruction q; issue_stage issues all of them.
+template <class C>
+__device__ __forceinline__ void issue_piece(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
+                                            uint8_t *buf, int wave, int lane, int q) {
+  const uint32_t kbyte = (uint32_t)k * kBK;
+  const uint32_t K8 = (uint32_t)t.K * 8u;
+  if (q < C::kPiecesB) {
+    const int piece = wave * C::kPiecesB + q;
+    const uint32_t voff = d.b[piece & 1] + (uint32_t)piece * K8 + kbyte;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.b, (lds_void_t *)(buf + piece * 1024), 16, voff, 0, 0, 0);
+  } else if (q < C::kPiecesB + C::kPiecesA) {
+    const int piece = wave * C::kPiecesA + (q - C::kPiecesB);
+    const uint32_t voff = d.a[piece & 1] + (uint32_t)piece * K8 + kbyte;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.a, (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, voff, 0, 0,
+                                             0);
+  } else if (q == C::kPiecesB + C::kPiecesA) {
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + wave * 128), 4,
+                                               d.sa + (uint32_t)k * 4u, 0, 0, 0);
+  } else {
+    if (lane < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + wave * 8), 4,
+                                               d.sb + (uint32_t)k * 4u, 0, 0, 0);
   }
 }
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
+                                            uint8_t *buf, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < C::kLoadsPerStage; ++q) issue_piece<C>(t, rs, d, k, buf, wave, lane, q);
+}
+
+// The DMA of a stage that the next block issues, right after its first LDS
+// reads (so those are not queued behind it).
+struct StageDma {
+  const TileJob *t;
+  const TileRsrc *rs;
+  const DmaLane *d;
+  int k;
+  uint8_t *buf;
+  int wave, lane;
+  bool on;
+};
 
 // MFMA operand of a 16-row sub-tile: lane l supplies row (l % 16), bytes
 // [32*(l/16), 32*(l/16) + 32) of the 128-byte K block.  A and B operands use
@@ -160,43 +214,84 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));  // RNE
 }
 
-// One K block of one wave: fragments from LDS, 32 MFMAs, 128 FMAs per lane.
-// Software pipelined: the four MFMAs of sub-tile row ni+1 are issued before
-// the FMAs that fold row ni into the accumulators.
+// Fragments of one K block that a wave keeps in registers: the four token
+// sub-tiles (B operands), the first weight sub-tile (A operand) and the four
+// combined scales a_s[row] * b_s of this lane's token rows.
+struct BlockFrags {
+  v8i xf[kSubM];
+  v8i wf;
+  float scl[kSubM];
+};
+
 template <class C>
-__device__ __forceinline__ void mma_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
-                                          v4f (&acc)[kSubN][kSubM]) {
+__device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
+                                           BlockFrags &f) {
   const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wave * 8 + wn * 4);
-  const float scl[kSubM] = {sa4.x * sb, sa4.y * sb, sa4.z * sb, sa4.w * sb};
-  const uint8_t *tb = buf;
-  const uint8_t *ta = buf + C::kOffA;
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
+  f.wf = frag(buf, wn * 128, lane);
+  f.scl[0] = sa4.x * sb;
+  f.scl[1] = sa4.y * sb;
+  f.scl[2] = sa4.z * sb;
+  f.scl[3] = sa4.w * sb;
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+
+// The 32 MFMAs of one K block, j = 4*ni + mi (sub-tile row ni, column mi).
+// Before row ni the LDS reads of weight sub-tile ni+1 are issued; after MFMA j
+// the scale fold of MFMA j-2 follows, whose result is two MFMAs old.  The
+// partial products live in a ring of three.  The folds of j = 30, 31 are left
+// to the caller, which issues them after requesting the next block's
+// fragments so that the LDS latency at the block boundary overlaps FMAs.
+constexpr int kRing = 3;
+constexpr int kMfmaPerBlock = kSubN * kSubM;
+
+__device__ __forceinline__ void fold1(v4f &acc, const v4f &p, float s) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], s, acc[r]);
+}
+
+// Keeps a value's computation above this point: without it the compiler may
+// sink the MFMAs and folds of a block past the block-boundary branch, away
+// from the schedule laid out here.
+__device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
+
+template <class C>
+__device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
+                                          v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const StageDma &dma) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  v8i xf[kSubM];
+  v8i wf[2];
+  wf[0] = f.wf;
 #pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) xf[mi] = frag(ta, wm * 64 + mi * 16, lane);
-  v4f p[2][kSubM];
-  {
-    const v8i wf = frag(tb, wn * 128, lane);
-#pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi)
-      p[0][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mi], zero, 0, 0, 0, 127, 0, 127);
-  }
-#pragma unroll
-  for (int ni = 0; ni < kSubN; ++ni) {
-    if (ni + 1 < kSubN) {
-      const v8i wf = frag(tb, wn * 128 + (ni + 1) * 16, lane);
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi)
-        p[(ni + 1) & 1][mi] =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mi], zero, 0, 0, 0, 127, 0, 127);
+  for (int j = 0; j < kMfmaPerBlock; ++j) {
+    const int ni = j / kSubM, mi = j % kSubM;
+    if (mi == 0) {
+      // the reads of sub-tile ni+1 go out before any MFMA of row ni
+      __builtin_amdgcn_sched_barrier(0);
+      if (ni + 1 < kSubN) wf[(ni + 1) & 1] = frag(tb, wn * 128 + (ni + 1) * 16, lane);
+      if (ni == 0 && dma.on) issue_stage<C>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[ni][mi][r] = __builtin_fmaf(p[ni & 1][mi][r], scl[mi], acc[ni][mi][r]);
+    p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni & 1], f.xf[mi], zero, 0, 0, 0, 127, 0,
+                                                                     127);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (j >= 2) {
+      const int jj = j - 2;
+      fold1(acc[jj / kSubM][jj % kSubM], p[jj % kRing], f.scl[jj % kSubM]);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ni = 0; ni < kSubN; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) pin(acc[ni][mi]);
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) pin(p[r]);
 }
 
 template <int N>
@@ -216,6 +311,17 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until the DMA of block kk has landed in every wave's view: at most the
+// later blocks already issued (kk+1 .. kk+kStages-2) may still be in flight.
+template <class C>
+__device__ __forceinline__ void wait_block(int kk, int KB) {
+  if (kk + C::kStages - 2 < KB)
+    wait_vmcnt<C::kLoadsPerStage * (C::kStages - 2)>();
+  else
+    wait_vmcnt<0>();
+  barrier_nofence();
+}
+
 // One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
 // n_valid), written to y (row stride N) at y[0][0].
 template <class C>
@@ -232,24 +338,40 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
+  const TileRsrc rs = make_rsrc(t);
+  const DmaLane dl = dma_lane<C>(t, wave, lane);
+
+  // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < KB) issue_stage<C>(t, s, lds + s * C::kStageBytes, wave, lane);
+    if (s < KB) issue_stage<C>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
 
-  int cur = 0;                   // stage buffer of block k
-  int nxt = C::kStages - 1;      // stage buffer of block k + kStages - 1
+  wait_block<C>(0, KB);
+  BlockFrags f;
+  load_block<C>(lds, wave, wn, wm, lane, f);
+
+  v4f p[kRing];
+  int cur = 0;  // stage buffer of block k
+  StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
+               C::kStages - 1 < KB};
   for (int k = 0; k < KB; ++k) {
-    // Block k has landed once at most the loads of the later blocks already
-    // issued (k+1 .. k+kStages-2) are still in flight.
-    if (k + C::kStages - 2 < KB)
-      wait_vmcnt<C::kLoadsPerStage * (C::kStages - 2)>();
-    else
-      wait_vmcnt<0>();
-    barrier_nofence();  // everyone's block k is in LDS; everyone is done with block k-1
-    if (k + C::kStages - 1 < KB) issue_stage<C>(t, k + C::kStages - 1, lds + nxt * C::kStageBytes, wave, lane);
-    mma_block<C>(lds + cur * C::kStageBytes, wave, wn, wm, lane, acc);
-    cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-    nxt = (nxt + 1 == C::kStages) ? 0 : nxt + 1;
+    mma_steps<C>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
+    const float s30 = f.scl[(kMfmaPerBlock - 2) % kSubM];
+    const float s31 = f.scl[(kMfmaPerBlock - 1) % kSubM];
+    if (k + 1 < KB) {
+      // Block k's buffer is free once every wave is past this barrier; it
+      // receives block k + kStages.
+      wait_block<C>(k + 1, KB);
+      // block k + kStages goes into block k's buffer during the next block
+      dma.k = k + C::kStages;
+      dma.buf = lds + cur * C::kStageBytes;
+      dma.on = k + C::kStages < KB;
+      cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
+      load_block<C>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
+    }
+    constexpr int j30 = kMfmaPerBlock - 2, j31 = kMfmaPerBlock - 1;
+    fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
+    fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
   }
 
   // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.

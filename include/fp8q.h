@@ -27,7 +27,8 @@
  *  - Alignment: every pointer must be 16-byte aligned (torch allocations are).
  *  - Shapes: K is a positive multiple of 128; N is a multiple of 128; M (and
  *    every group size) is any value >= 0 -- ragged tails are masked.  M == 0 or
- *    N == 0 is a valid empty call that enqueues nothing.
+ *    N == 0 is a valid empty call that enqueues nothing.  The GEMMs accept
+ *    K <= 4194304 (FP8Q_ESHAPE otherwise).
  *  - Execution: each call enqueues its kernels on `stream` (a hipStream_t; NULL
  *    is the null stream) and returns without synchronising.  The outputs are
  *    valid once the stream reaches that point.
@@ -53,7 +54,7 @@ extern "C" {
 typedef enum fp8q_status {
     FP8Q_OK = 0,
     FP8Q_EINVAL = 1,  /* null pointer, negative size, unknown mode, G < 1 */
-    FP8Q_ESHAPE = 2,  /* K not a positive multiple of 128, or N not a multiple of 128 */
+    FP8Q_ESHAPE = 2,  /* K not a positive multiple of 128 (or, for a GEMM, above 4194304), or N not a multiple of 128 */
     FP8Q_EALIGN = 3,  /* a pointer not 16-byte aligned */
     FP8Q_EDEVICE = 4, /* no HIP device, or the current device is not gfx950 */
     FP8Q_EHIP = 5     /* the HIP runtime reported an error while enqueueing */

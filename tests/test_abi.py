@@ -78,6 +78,8 @@ def test_gemm_argument_errors(lib):
     assert f(GOOD, None, GOOD, GOOD, GOOD, 64, 128, 128, None) == 1
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, 64, 128, 128, None) == 3
     assert f(None, None, None, None, None, 0, 128, 128, None) == 0
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, None) == 2   # K too large
+    assert "K" in _err(lib)
 
 
 def test_grouped_argument_errors(lib):
@@ -87,6 +89,7 @@ def test_grouped_argument_errors(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, None, 2, 64, 128, 128, GOOD, None) == 1   # null offsets
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, None) == 3
     assert f(None, None, None, None, None, 3, 0, 128, 128, None, None) == 0
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, (1 << 22) + 128, GOOD, None) == 2
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):

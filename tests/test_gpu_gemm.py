@@ -139,3 +139,22 @@ def test_llama_layers_full_size_sampled(layer):
     ref = oracle.gemm_sampled_f64(haq, has, hbq, hbs, ms, ns)
     got = y.float().cpu().numpy().astype(np.float64)[ms, ns]
     gemm_tolerance_check(got, ref, f"llama {name} sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (300, 32640, 128), (300, 32640, 256), (257, 32768, 384), (513, 16512, 640), (4096, 4096, 1408),
+])
+def test_wide_shapes_ragged(M, N, K):
+    """Shapes with at least 256 output tiles of 256 x 256 (the configuration of
+    the large-M kernel): ragged token and weight tiles, 1, 2, 3, 5 and 11 K
+    blocks (every remainder of the three-block main loop)."""
+    require_gpu()
+    aq, as_, bq, bs = _quantized(M, N, K, seed=M + N + K, outliers=0.01)
+    say("gemm wide", M, N, K)
+    y = _run_gemm(aq, as_, bq, bs)
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], rng.integers(0, M, 6)]))
+    ms = np.concatenate([np.repeat(rows, N), rng.integers(0, M, 20000)])
+    ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 20000)])
+    ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms, ns)
+    gemm_tolerance_check(y[ms, ns], ref, f"{M}x{N}x{K}")
