@@ -84,6 +84,18 @@ def calibration_copy(torch, dev, nbytes=1 << 30, reps=3):
     del src, dst
 
 
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """GB/s (bytes read + written) of a plain 1 GiB elementwise copy: what a
+    streaming kernel can reach on this HBM, next to the 8 TB/s spec figure."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    t = time_loop(lambda: torch.neg(src, out=dst), reps, torch)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
+
+
 def time_loop(fn, reps, torch):
     """Average duration (s) of fn() over reps launches, HIP events on the
     current stream (the stream the library enqueues on)."""
@@ -242,11 +254,16 @@ def main():
     act_gbs = q_bytes / q_s / 1e9
     log(f"act quant {act_gbs:.1f} GB/s")
 
+    copy_gbs = copy_bandwidth(torch, dev)
+    log(f"copy kernel {copy_gbs:.1f} GB/s")
+
     result["kernels"] = {
         "gemm_tflops": round(gemm_tflops, 1),
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "act_quant_gbs": round(act_gbs, 1),
         "act_quant_frac_hbm": round(act_gbs / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbs": round(copy_gbs, 1),
+        "act_quant_frac_copy": round(act_gbs / copy_gbs, 4),
         "per_layer": per_layer,
     }
     result["roofline"] = {
@@ -262,7 +279,7 @@ def main():
     }
 
     if not args.skip_extras:
-        result["recalibration"] = recalibration(fp8q, synth, torch, dev)
+        result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
         for l in layers:
@@ -271,7 +288,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def recalibration(fp8q, synth, torch, dev):
+def recalibration(fp8q, synth, torch, dev, copy_gbs=None):
     """Requantize all 128 linear weights of the 32-layer Llama-3.1-8B shape."""
     log("recalibration pass: generating 32 x 4 weights")
     ws, outs, total = [], [], 0
@@ -294,6 +311,8 @@ def recalibration(fp8q, synth, torch, dev):
         gbs = total / t / 1e9
         res[mode] = {"ms_per_pass": round(t * 1e3, 3), "gbs": round(gbs, 1),
                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        if copy_gbs:
+            res[mode]["frac_copy"] = round(gbs / copy_gbs, 4)
         log(f"recalibration {mode}: {t * 1e3:.3f} ms/pass, {gbs:.1f} GB/s")
     del ws, outs
     torch.cuda.empty_cache()

@@ -48,32 +48,37 @@ constexpr int kSubM = 4;  // 16-col MFMA sub-tiles per wave along m (64 rows)
 constexpr int kNumXcd = 8;
 constexpr int kGroupN = 4;  // weight panels per rasterization group
 
-template <int kBM_, int kWaves_, int kStages_>
+template <int kBM_, int kWaves_, int kStages_, int kLoaders_>
 struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
   static constexpr int kStages = kStages_;
+  // The last kLoaders waves (one per SIMD when kLoaders = 4) issue the stage
+  // DMA; while one stalls on it, the other wave of its SIMD keeps issuing MFMAs.
+  static constexpr int kLoaders = kLoaders_;
+  static constexpr int kFirstLoader = kWaves - kLoaders;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kWavesM = kWaves / 2;  // waves along m; 2 along n
   static_assert(kBM == 64 * kWavesM, "each wave owns 64 token rows");
   static constexpr int kBytesB = kBN * kBK;        // weight tile
   static constexpr int kBytesA = kBM * kBK;        // token tile
   static constexpr int kBytesSA = kBM * 4;         // activation scales
-  static constexpr int kBytesSB = kWaves * 8;      // weight scales (per-wave copy)
+  static constexpr int kBytesSB = kLoaders * 8;    // weight scales (one copy per loader; all read copy 0)
   static constexpr int kOffA = kBytesB;
   static constexpr int kOffSA = kOffA + kBytesA;
   static constexpr int kOffSB = kOffSA + kBytesSA;
   static constexpr int kStageBytes = (kOffSB + kBytesSB + 1023) / 1024 * 1024;
   static constexpr int kLdsBytes = kStageBytes * kStages;
-  static constexpr int kPiecesB = kBytesB / 1024 / kWaves;  // 1 KB DMA pieces per wave
-  static constexpr int kPiecesA = kBytesA / 1024 / kWaves;
-  static_assert(kBM / kWaves == 32, "32 activation scales per wave");
-  static constexpr int kLoadsPerStage = kPiecesB + kPiecesA + 2;  // + sa, sb
+  static constexpr int kPiecesB = kBytesB / 1024 / kLoaders;  // 1 KB DMA pieces per loader wave
+  static constexpr int kPiecesA = kBytesA / 1024 / kLoaders;
+  static constexpr int kScalesPerLoader = kBM / kLoaders;     // activation scales per loader wave
+  static_assert(kScalesPerLoader <= 64 && kBM % kLoaders == 0, "activation scales: one per lane");
+  static constexpr int kLoadsPerStage = kPiecesB + kPiecesA + 2;  // + sa, sb (per loader wave)
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-using CfgLarge = TileCfg<256, 8, 2>;
-using CfgSmall = TileCfg<128, 4, 3>;
+using CfgLarge = TileCfg<256, 8, 2, 4>;
+using CfgSmall = TileCfg<128, 4, 3, 4>;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -140,7 +145,8 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
     d.b[par] = row * K + ((c0 ^ par) << 4);
     d.a[par] = d.b[par];
   }
-  d.sa = (uint32_t)sa_row_of_pos(wave * 32 + (lane & 31)) * (uint32_t)t.KB * 4u;
+  const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
+  d.sa = (uint32_t)sa_row_of_pos(l * C::kScalesPerLoader + lane % C::kScalesPerLoader) * (uint32_t)t.KB * 4u;
   d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
   return d;
 }
@@ -154,22 +160,23 @@ __device__ __forceinline__ void issue_piece(const TileJob &t, const TileRsrc &rs
                                             uint8_t *buf, int wave, int lane, int q) {
   const uint32_t kbyte = (uint32_t)k * kBK;
   const uint32_t K8 = (uint32_t)t.K * 8u;
+  const int l = wave - C::kFirstLoader;  // loader index
   if (q < C::kPiecesB) {
-    const int piece = wave * C::kPiecesB + q;
+    const int piece = l * C::kPiecesB + q;
     const uint32_t voff = d.b[piece & 1] + (uint32_t)piece * K8 + kbyte;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.b, (lds_void_t *)(buf + piece * 1024), 16, voff, 0, 0, 0);
   } else if (q < C::kPiecesB + C::kPiecesA) {
-    const int piece = wave * C::kPiecesA + (q - C::kPiecesB);
+    const int piece = l * C::kPiecesA + (q - C::kPiecesB);
     const uint32_t voff = d.a[piece & 1] + (uint32_t)piece * K8 + kbyte;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.a, (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, voff, 0, 0,
                                              0);
   } else if (q == C::kPiecesB + C::kPiecesA) {
-    if (lane < 32)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + wave * 128), 4,
-                                               d.sa + (uint32_t)k * 4u, 0, 0, 0);
+    if (lane < C::kScalesPerLoader)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * C::kScalesPerLoader * 4),
+                                               4, d.sa + (uint32_t)k * 4u, 0, 0, 0);
   } else {
     if (lane < 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + wave * 8), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + l * 8), 4,
                                                d.sb + (uint32_t)k * 4u, 0, 0, 0);
   }
 }
@@ -217,9 +224,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Fragments of one K block that a wave keeps in registers: the four token
 // sub-tiles (B operands), the first weight sub-tile (A operand) and the four
 // combined scales a_s[row] * b_s of this lane's token rows.
+constexpr int kWAhead = 1;  // weight sub-tiles read ahead of their MFMAs
+
 struct BlockFrags {
   v8i xf[kSubM];
-  v8i wf;
+  v8i wf[kWAhead];  // the block's first weight sub-tiles
   float scl[kSubM];
 };
 
@@ -227,10 +236,11 @@ template <class C>
 __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
                                            BlockFrags &f) {
   const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
-  const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wave * 8 + wn * 4);
+  const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
-  f.wf = frag(buf, wn * 128, lane);
+#pragma unroll
+  for (int a = 0; a < kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
   f.scl[0] = sa4.x * sb;
   f.scl[1] = sa4.y * sb;
   f.scl[2] = sa4.z * sb;
@@ -264,19 +274,22 @@ template <class C>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const StageDma &dma) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  v8i wf[2];
-  wf[0] = f.wf;
+  constexpr int R = kWAhead + 1;
+  v8i wf[R];
+#pragma unroll
+  for (int a = 0; a < kWAhead; ++a) wf[a] = f.wf[a];
 #pragma unroll
   for (int j = 0; j < kMfmaPerBlock; ++j) {
     const int ni = j / kSubM, mi = j % kSubM;
     if (mi == 0) {
-      // the reads of sub-tile ni+1 go out before any MFMA of row ni
+      // the reads of sub-tile ni+kWAhead go out before any MFMA of row ni
       __builtin_amdgcn_sched_barrier(0);
-      if (ni + 1 < kSubN) wf[(ni + 1) & 1] = frag(tb, wn * 128 + (ni + 1) * 16, lane);
-      if (ni == 0 && dma.on) issue_stage<C>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
+      if (ni + kWAhead < kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * 128 + (ni + kWAhead) * 16, lane);
+      if (ni == 0 && dma.on && dma.wave >= C::kFirstLoader)
+        issue_stage<C>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni & 1], f.xf[mi], zero, 0, 0, 0, 127, 0,
+    p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni % R], f.xf[mi], zero, 0, 0, 0, 127, 0,
                                                                      127);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if (j >= 2) {
@@ -344,7 +357,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
   // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < KB) issue_stage<C>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
+    if (s < KB && wave >= C::kFirstLoader) issue_stage<C>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
 
   wait_block<C>(0, KB);
   BlockFrags f;
@@ -523,8 +536,14 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                uint16_t *y, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K,
-               M_total / CfgSmall::kBM + G, G, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K, 0, G, tiles_n};
+  // 256-row tiles once the average group fills one; their ragged last tile
+  // per group then wastes at most half of the work it would at 128 rows.
+  if (M_total >= (int64_t)G * CfgLarge::kBM) {
+    p.slots_m = M_total / CfgLarge::kBM + G;
+    return launch<CfgLarge, true>(p, stream);
+  }
+  p.slots_m = M_total / CfgSmall::kBM + G;
   return launch<CfgSmall, true>(p, stream);
 }
 

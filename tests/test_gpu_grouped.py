@@ -44,6 +44,8 @@ def _run(aq, as_, bq, bs, off):
     ([0, 0, 0, 17], 384, 384),
     ([500], 128, 128),
     ([129, 127, 128, 1, 256, 0, 64], 640, 512),
+    ([600, 0, 257, 1024, 1, 300, 256], 384, 640),    # average >= 256 rows: 256-row tiles
+    ([2048, 513], 2816, 1408),
 ])
 def test_ragged_and_empty_groups(sizes, N, K):
     require_gpu()
