@@ -279,6 +279,7 @@ def main():
     }
 
     if not args.skip_extras:
+        result["pow2"] = pow2_gemm(fp8q, layers, torch, M, reps)
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
@@ -286,6 +287,38 @@ def main():
             del l["w"]
         result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def pow2_gemm(fp8q, layers, torch, M, reps):
+    """The same four layers with power-of-two scales (the recipe's pow2 option):
+    activations and weights quantized in pow2 mode, product by the GEMM whose
+    matrix cores apply the scales (E8M0).  Steps: quantize + GEMM per layer."""
+    ops = []
+    for l in layers:
+        bq, bs = fp8q.fp8_quant_weight_128x128(l["w"], "pow2")
+        aq, as_ = fp8q.fp8_quant_act_1x128(l["x"], "pow2")
+        ops.append((l, aq, as_, bq, bs))
+    torch.cuda.synchronize()
+    per, g_s, g_f = {}, 0.0, 0.0
+    for l, aq, as_, bq, bs in ops:
+        fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"])
+        t = time_loop(lambda: fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"]), reps, torch)
+        f = 2.0 * M * l["N"] * l["K"]
+        g_s += t
+        g_f += f
+        per[l["name"]] = {"gemm_us": round(t * 1e6, 2), "gemm_tflops": round(f / t / 1e12, 1)}
+
+    def step():
+        for l, aq, as_, bq, bs in ops:
+            fp8q.fp8_quant_act_1x128(l["x"], "pow2", out=(aq, as_))
+            fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"])
+    step()
+    t_step = time_loop(step, reps, torch)
+    tf = g_f / g_s / 1e12
+    log(f"pow2 gemm {tf:.1f} TFLOP/s; pow2 step {g_f / t_step / 1e12:.1f} TFLOP/s")
+    del ops
+    return {"gemm_tflops": round(tf, 1), "gemm_frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "step_tflops": round(g_f / t_step / 1e12, 1), "per_layer": per}
 
 
 def recalibration(fp8q, synth, torch, dev, copy_gbs=None):

@@ -24,7 +24,8 @@ SCALE_POW2 = 1
 _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_POW2: SCALE_POW2}
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
-           "fp8_blockscaled_gemm", "fp8_grouped_gemm", "abi_version", "library_path"]
+           "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
+           "fp8_grouped_gemm_pow2", "abi_version", "library_path"]
 
 
 def library_path():
@@ -102,8 +103,7 @@ def fp8_quant_weight_128x128(w, mode="amax", out=None):
     return q, s
 
 
-def fp8_blockscaled_gemm(a_q, a_s, b_q, b_s, out=None):
-    """Y[M, N] bf16 = dequant(a_q, a_s) @ dequant(b_q, b_s)^T (fp32 accumulation)."""
+def _gemm(fn, a_q, a_s, b_q, b_s, out):
     a_q, pa = _as_bytes(a_q, "a_q", 2)
     b_q, pb = _as_bytes(b_q, "b_q", 2)
     pas = _dev(a_s, "a_s", torch.float32, 2)
@@ -116,18 +116,22 @@ def fp8_blockscaled_gemm(a_q, a_s, b_q, b_s, out=None):
     py = _dev(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("output shape does not match")
-    _lib.check("fp8_blockscaled_gemm",
-               _lib.load().fp8_blockscaled_gemm(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
+    _lib.check(fn, getattr(_lib.load(), fn)(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
     return y
 
 
-def fp8_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, out=None):
-    """Grouped (mixture-of-experts) GEMM.
+def fp8_blockscaled_gemm(a_q, a_s, b_q, b_s, out=None):
+    """Y[M, N] bf16 = dequant(a_q, a_s) @ dequant(b_q, b_s)^T (fp32 accumulation)."""
+    return _gemm("fp8_blockscaled_gemm", a_q, a_s, b_q, b_s, out)
 
-    a_q [M_total, K], a_s [M_total, K/128], b_q [G, N, K], b_s [G, N/128, K/128],
-    group_offsets int32 [G+1] in device memory (rows of group g are
-    [offsets[g], offsets[g+1])).  Returns Y bf16 [M_total, N].
-    """
+
+def fp8_blockscaled_gemm_pow2(a_q, a_s, b_q, b_s, out=None):
+    """As fp8_blockscaled_gemm, for scales that are all powers of two (the
+    matrix cores apply them); an output that depends on any other scale is NaN."""
+    return _gemm("fp8_blockscaled_gemm_pow2", a_q, a_s, b_q, b_s, out)
+
+
+def _grouped(fn, a_q, a_s, b_q, b_s, group_offsets, out):
     a_q, pa = _as_bytes(a_q, "a_q", 2)
     b_q, pb = _as_bytes(b_q, "b_q", 3)
     pas = _dev(a_s, "a_s", torch.float32, 2)
@@ -143,6 +147,20 @@ def fp8_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, out=None):
     py = _dev(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("output shape does not match")
-    _lib.check("fp8_grouped_gemm",
-               _lib.load().fp8_grouped_gemm(pa, pas, pb, pbs, poff, G, M, N, K, py, _stream(a_q)))
+    _lib.check(fn, getattr(_lib.load(), fn)(pa, pas, pb, pbs, poff, G, M, N, K, py, _stream(a_q)))
     return y
+
+
+def fp8_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, out=None):
+    """Grouped (mixture-of-experts) GEMM.
+
+    a_q [M_total, K], a_s [M_total, K/128], b_q [G, N, K], b_s [G, N/128, K/128],
+    group_offsets int32 [G+1] in device memory (rows of group g are
+    [offsets[g], offsets[g+1])).  Returns Y bf16 [M_total, N].
+    """
+    return _grouped("fp8_grouped_gemm", a_q, a_s, b_q, b_s, group_offsets, out)
+
+
+def fp8_grouped_gemm_pow2(a_q, a_s, b_q, b_s, group_offsets, out=None):
+    """As fp8_grouped_gemm, for scales that are all powers of two."""
+    return _grouped("fp8_grouped_gemm_pow2", a_q, a_s, b_q, b_s, group_offsets, out)

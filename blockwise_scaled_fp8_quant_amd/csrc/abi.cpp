@@ -91,46 +91,77 @@ fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, ui
                   __func__);
 }
 
+}  // extern "C"
+
+namespace {
+
+fp8q_status gemm_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                       const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2,
+                       void *stream) {
+  g_last_error.clear();
+  if (!(M >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (N % 128 != 0) return fail(FP8Q_ESHAPE, fn, "N must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31)) return fail(FP8Q_EINVAL, fn, "M or N too large");
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (!(a_q && a_s && b_q && b_s && y)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_blockscaled_gemm(a_q, a_s, b_q, b_s, y, M, N, K, pow2, (hipStream_t)stream), fn);
+}
+
+fp8q_status grouped_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                          const float *b_s, const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N,
+                          int64_t K, uint16_t *y, bool pow2, void *stream) {
+  g_last_error.clear();
+  if (G < 1) return fail(FP8Q_EINVAL, fn, "G must be >= 1");
+  if (!(M_total >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (N % 128 != 0) return fail(FP8Q_ESHAPE, fn, "N must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M_total < ((int64_t)1 << 31) && N <= ((int64_t)1 << 31)))
+    return fail(FP8Q_EINVAL, fn, "M_total or N too large");
+  if (M_total == 0 || N == 0) return FP8Q_OK;
+  if (!(a_q && a_s && b_q && b_s && y && group_offsets)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y) &&
+        aligned16(group_offsets)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, pow2,
+                                            (hipStream_t)stream),
+                  fn);
+}
+
+}  // namespace
+
+extern "C" {
+
 fp8q_status fp8_blockscaled_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
                                  const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
                                  void *stream) {
-  g_last_error.clear();
-  FP8Q_REQUIRE(M >= 0 && N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
-  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
-  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
-  FP8Q_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, FP8Q_EINVAL, "M or N too large");
-  FP8Q_REQUIRE(K <= kMaxGemmK, FP8Q_ESHAPE, "K larger than 4194304");
-  if (M == 0 || N == 0) return FP8Q_OK;
-  FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y, FP8Q_EINVAL, "null pointer");
-  FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y),
-               FP8Q_EALIGN, "pointers must be 16-byte aligned");
-  fp8q_status st = check_device(__func__);
-  if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_blockscaled_gemm(a_q, a_s, b_q, b_s, y, M, N, K, (hipStream_t)stream),
-                  __func__);
+  return gemm_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, false, stream);
+}
+
+fp8q_status fp8_blockscaled_gemm_pow2(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                      const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                      void *stream) {
+  return gemm_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, true, stream);
 }
 
 fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
                              const float *b_s, const int32_t *group_offsets, int32_t G,
                              int64_t M_total, int64_t N, int64_t K, uint16_t *y, void *stream) {
-  g_last_error.clear();
-  FP8Q_REQUIRE(G >= 1, FP8Q_EINVAL, "G must be >= 1");
-  FP8Q_REQUIRE(M_total >= 0 && N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
-  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
-  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
-  FP8Q_REQUIRE(M_total < ((int64_t)1 << 31) && N <= ((int64_t)1 << 31), FP8Q_EINVAL,
-               "M_total or N too large");
-  FP8Q_REQUIRE(K <= kMaxGemmK, FP8Q_ESHAPE, "K larger than 4194304");
-  if (M_total == 0 || N == 0) return FP8Q_OK;
-  FP8Q_REQUIRE(a_q && a_s && b_q && b_s && y && group_offsets, FP8Q_EINVAL, "null pointer");
-  FP8Q_REQUIRE(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y) &&
-                   aligned16(group_offsets),
-               FP8Q_EALIGN, "pointers must be 16-byte aligned");
-  fp8q_status st = check_device(__func__);
-  if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y,
-                                            (hipStream_t)stream),
-                  __func__);
+  return grouped_entry(__func__, a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, false, stream);
+}
+
+fp8q_status fp8_grouped_gemm_pow2(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                  const float *b_s, const int32_t *group_offsets, int32_t G,
+                                  int64_t M_total, int64_t N, int64_t K, uint16_t *y, void *stream) {
+  return grouped_entry(__func__, a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, true, stream);
 }
 
 const char *fp8q_status_string(int status) {

@@ -15,15 +15,17 @@ hipError_t launch_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
                                        uint8_t *q, float *s, int mode,
                                        hipStream_t stream);
 
+// pow2: every scale is a power of two and the matrix core applies it (E8M0
+// scale operands); otherwise the per-K-block scale fold runs on the VALU.
 hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
                                    const uint8_t *b_q, const float *b_s,
                                    uint16_t *y, int64_t M, int64_t N, int64_t K,
-                                   hipStream_t stream);
+                                   bool pow2, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const uint8_t *b_q, const float *b_s,
                                const int32_t *group_offsets, int32_t G,
                                int64_t M_total, int64_t N, int64_t K,
-                               uint16_t *y, hipStream_t stream);
+                               uint16_t *y, bool pow2, hipStream_t stream);
 
 }  // namespace fp8q

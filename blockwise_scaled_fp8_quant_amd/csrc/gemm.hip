@@ -230,9 +230,24 @@ struct BlockFrags {
   v8i xf[kSubM];
   v8i wf[kWAhead];  // the block's first weight sub-tiles
   float scl[kSubM];
+  // power-of-two scales: E8M0 exponent bytes (token rows mi = 0..3 in byte mi;
+  // the weight block's), and which of them (bit mi; bit 4: the weight
+  // block's) was, in some K block so far, not a power of two in [2^-126, 2^127]
+  uint32_t ea, eb;
+  uint32_t bad;
 };
 
-template <class C>
+// E8M0 byte of a power-of-two fp32 scale 2^(e-127), 1 <= e <= 254: its
+// exponent field.  Sets `bit` in bad for anything else (a mantissa, a sign,
+// zero, subnormal, infinity or NaN).
+__device__ __forceinline__ uint32_t e8m0_of(float s, uint32_t &bad, uint32_t bit) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t e = u >> 23;  // sign bit included: must be 0
+  if ((u & 0x7FFFFFu) != 0u || e == 0u || e >= 255u) bad |= bit;
+  return e & 0xFFu;
+}
+
+template <class C, bool kPow2>
 __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
                                            BlockFrags &f) {
   const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
@@ -241,10 +256,16 @@ __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn,
   for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
 #pragma unroll
   for (int a = 0; a < kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
-  f.scl[0] = sa4.x * sb;
-  f.scl[1] = sa4.y * sb;
-  f.scl[2] = sa4.z * sb;
-  f.scl[3] = sa4.w * sb;
+  if constexpr (kPow2) {
+    f.ea = e8m0_of(sa4.x, f.bad, 1u) | (e8m0_of(sa4.y, f.bad, 2u) << 8) | (e8m0_of(sa4.z, f.bad, 4u) << 16) |
+           (e8m0_of(sa4.w, f.bad, 8u) << 24);
+    f.eb = e8m0_of(sb, f.bad, 16u);
+  } else {
+    f.scl[0] = sa4.x * sb;
+    f.scl[1] = sa4.y * sb;
+    f.scl[2] = sa4.z * sb;
+    f.scl[3] = sa4.w * sb;
+  }
 }
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
@@ -260,6 +281,23 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kRing = 3;
 constexpr int kMfmaPerBlock = kSubN * kSubM;
 
+// acc + A*B with the E8M0 scale eb on every row of A (one weight block) and,
+// on column j of B, byte `sel` of the lane's ea (its token row's exponent).
+template <int kSel>
+__device__ __forceinline__ v4f mfma_pow2_sel(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)eb, kSel, (int)ea);
+}
+
+__device__ __forceinline__ v4f mfma_pow2(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea,
+                                         int sel) {
+  switch (sel) {
+    case 0: return mfma_pow2_sel<0>(a, b, c, eb, ea);
+    case 1: return mfma_pow2_sel<1>(a, b, c, eb, ea);
+    case 2: return mfma_pow2_sel<2>(a, b, c, eb, ea);
+    default: return mfma_pow2_sel<3>(a, b, c, eb, ea);
+  }
+}
+
 __device__ __forceinline__ void fold1(v4f &acc, const v4f &p, float s) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], s, acc[r]);
@@ -270,7 +308,12 @@ __device__ __forceinline__ void fold1(v4f &acc, const v4f &p, float s) {
 // from the schedule laid out here.
 __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 
-template <class C>
+//
+// With power-of-two scales (kPow2) the matrix core applies them itself: the
+// E8M0 scale operands of each MFMA carry the weight block's and the token
+// row's exponents, and the MFMA accumulates straight into acc -- no partial
+// products and no folds.
+template <class C, bool kPow2>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const StageDma &dma) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -288,6 +331,10 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       if (ni == 0 && dma.on && dma.wave >= C::kFirstLoader)
         issue_stage<C>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kPow2) {
+      acc[ni][mi] = mfma_pow2(wf[ni % R], f.xf[mi], acc[ni][mi], f.eb, f.ea, mi);
+      continue;
     }
     p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni % R], f.xf[mi], zero, 0, 0, 0, 127, 0,
                                                                      127);
@@ -337,7 +384,7 @@ __device__ __forceinline__ void wait_block(int kk, int KB) {
 
 // One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
 // n_valid), written to y (row stride N) at y[0][0].
-template <class C>
+template <class C, bool kPow2>
 __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict__ y, int64_t N,
                                           uint8_t *lds) {
   const int lane = threadIdx.x & 63;
@@ -361,14 +408,15 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
 
   wait_block<C>(0, KB);
   BlockFrags f;
-  load_block<C>(lds, wave, wn, wm, lane, f);
+  f.bad = 0;
+  load_block<C, kPow2>(lds, wave, wn, wm, lane, f);
 
   v4f p[kRing];
   int cur = 0;  // stage buffer of block k
   StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
                C::kStages - 1 < KB};
   for (int k = 0; k < KB; ++k) {
-    mma_steps<C>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
+    mma_steps<C, kPow2>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
     const float s30 = f.scl[(kMfmaPerBlock - 2) % kSubM];
     const float s31 = f.scl[(kMfmaPerBlock - 1) % kSubM];
     if (k + 1 < KB) {
@@ -380,11 +428,23 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
       dma.buf = lds + cur * C::kStageBytes;
       dma.on = k + C::kStages < KB;
       cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-      load_block<C>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
+      load_block<C, kPow2>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
     }
-    constexpr int j30 = kMfmaPerBlock - 2, j31 = kMfmaPerBlock - 1;
-    fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
-    fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
+    if constexpr (!kPow2) {
+      constexpr int j30 = kMfmaPerBlock - 2, j31 = kMfmaPerBlock - 1;
+      fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
+      fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
+    }
+  }
+  // A scale outside the power-of-two contract turns the outputs that depend
+  // on it into NaN rather than into a silently wrong product.
+  if (kPow2 && f.bad) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi)
+      if (f.bad & ((1u << mi) | 16u))
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
   }
 
   // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.
@@ -452,7 +512,7 @@ __device__ __forceinline__ int64_t clamp_off(const int32_t *off, int32_t g, int6
 // tiles; a slot beyond its group's rows exits at once.  The group of a slot is
 // found by binary search over S (wave-uniform, scalar loads), so no prefix sums
 // or workspace are needed and the offsets never leave the device.
-template <class C, bool kGrouped>
+template <class C, bool kGrouped, bool kPow2>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -494,28 +554,27 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   t.b_s = bs + (n0 >> 7) * t.KB;
   t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
   t.n_valid = n_valid;
-  gemm_tile<C>(t, p.y + m0 * p.N + n0, p.N, lds);
+  gemm_tile<C, kPow2>(t, p.y + m0 * p.N + n0, p.N, lds);
 }
 
-template <class C, bool kGrouped>
+template <class C, bool kGrouped, bool kPow2>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t grid = p.slots_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<C, kGrouped>), dim3((unsigned)grid), dim3(C::kThreads),
+  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2>), dim3((unsigned)grid), dim3(C::kThreads),
                      C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
-                                   const uint8_t *b_q, const float *b_s,
-                                   uint16_t *y, int64_t M, int64_t N, int64_t K,
-                                   hipStream_t stream) {
+template <bool kPow2>
+static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
+                        uint16_t *y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, M, N, K, 0, 1, tiles_n};
@@ -523,17 +582,16 @@ hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
   const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
   if (large_tiles >= 256) {
     p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
-    return launch<CfgLarge, false>(p, stream);
+    return launch<CfgLarge, false, kPow2>(p, stream);
   }
   p.slots_m = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  return launch<CfgSmall, false>(p, stream);
+  return launch<CfgSmall, false, kPow2>(p, stream);
 }
 
-hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
-                               const uint8_t *b_q, const float *b_s,
-                               const int32_t *group_offsets, int32_t G,
-                               int64_t M_total, int64_t N, int64_t K,
-                               uint16_t *y, hipStream_t stream) {
+template <bool kPow2>
+static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
+                          const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N, int64_t K,
+                          uint16_t *y, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K, 0, G, tiles_n};
@@ -541,10 +599,27 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
     p.slots_m = M_total / CfgLarge::kBM + G;
-    return launch<CfgLarge, true>(p, stream);
+    return launch<CfgLarge, true, kPow2>(p, stream);
   }
   p.slots_m = M_total / CfgSmall::kBM + G;
-  return launch<CfgSmall, true>(p, stream);
+  return launch<CfgSmall, true, kPow2>(p, stream);
+}
+
+hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
+                                   const uint8_t *b_q, const float *b_s,
+                                   uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                   bool pow2, hipStream_t stream) {
+  return pow2 ? dense<true>(a_q, a_s, b_q, b_s, y, M, N, K, stream)
+              : dense<false>(a_q, a_s, b_q, b_s, y, M, N, K, stream);
+}
+
+hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
+                               const uint8_t *b_q, const float *b_s,
+                               const int32_t *group_offsets, int32_t G,
+                               int64_t M_total, int64_t N, int64_t K,
+                               uint16_t *y, bool pow2, hipStream_t stream) {
+  return pow2 ? grouped<true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, stream)
+              : grouped<false>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, stream);
 }
 
 }  // namespace fp8q

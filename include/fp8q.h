@@ -137,6 +137,31 @@ fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s,
                              int64_t M_total, int64_t N, int64_t K,
                              uint16_t *y, void *stream);
 
+/*
+ * The same two products for operands whose scales are all powers of two --
+ * what fp8_quant_act_1x128 and fp8_quant_weight_128x128 produce in
+ * FP8Q_SCALE_POW2 mode (page 1, "Warum dies fuer die KI-Oekonomie wichtig
+ * ist": power-of-two scale factors as an option "for additional
+ * optimization").  On gfx950 the matrix cores then apply the scales
+ * themselves (E8M0 block-scale operands), so no per-block rescaling runs on
+ * the vector ALUs.  Arguments, layouts, errors and the result (up to the fp32
+ * summation order) are those of fp8_blockscaled_gemm / fp8_grouped_gemm.
+ * Precondition: every scale an output depends on is 2^e with -126 <= e <= 127;
+ * an output that depends on any other scale value is written as NaN instead
+ * of a silently different product.  (POW2-mode quantization gives e < -126
+ * only for blocks whose largest magnitude is below 448 * 2^-127.)
+ */
+fp8q_status fp8_blockscaled_gemm_pow2(const uint8_t *a_q, const float *a_s,
+                                      const uint8_t *b_q, const float *b_s,
+                                      uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                      void *stream);
+
+fp8q_status fp8_grouped_gemm_pow2(const uint8_t *a_q, const float *a_s,
+                                  const uint8_t *b_q, const float *b_s,
+                                  const int32_t *group_offsets, int32_t G,
+                                  int64_t M_total, int64_t N, int64_t K,
+                                  uint16_t *y, void *stream);
+
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -26,10 +26,11 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(fp8\w*)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
-              "fp8_grouped_gemm", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
+              "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
+              "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
 
@@ -70,8 +71,9 @@ def test_quantizer_argument_errors(lib, fn):
         assert f(GOOD, 100, 128, GOOD, GOOD, 0, None) == 2      # N % 128
 
 
-def test_gemm_argument_errors(lib):
-    f = lib.fp8_blockscaled_gemm
+@pytest.mark.parametrize("fn", ["fp8_blockscaled_gemm", "fp8_blockscaled_gemm_pow2"])
+def test_gemm_argument_errors(lib, fn):
+    f = getattr(lib, fn)
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, None) == 2
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 100, 128, None) == 2
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, -1, 128, 128, None) == 1
@@ -82,8 +84,9 @@ def test_gemm_argument_errors(lib):
     assert "K" in _err(lib)
 
 
-def test_grouped_argument_errors(lib):
-    f = lib.fp8_grouped_gemm
+@pytest.mark.parametrize("fn", ["fp8_grouped_gemm", "fp8_grouped_gemm_pow2"])
+def test_grouped_argument_errors(lib, fn):
+    f = getattr(lib, fn)
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 128, 128, GOOD, None) == 1   # G < 1
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 100, GOOD, None) == 2
     assert f(GOOD, GOOD, GOOD, GOOD, None, 2, 64, 128, 128, GOOD, None) == 1   # null offsets
