@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
+    ap.add_argument("--sections", default="pow2,recal,moe,bf16,cpu",
+                    help="extra measurements after the step (comma list of pow2, recal, moe, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -125,7 +127,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernels run on one GPU's share; see the design notes on sharding)",
+              "(it times the kernels on one GPU; a multi-GPU run is not part of it)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -278,11 +280,16 @@ def main():
         "flops_per_launch": gemm_flops / len(layers),
     }
 
-    if not args.skip_extras:
+    sections = set() if args.skip_extras else set(args.sections.split(","))
+    if "pow2" in sections:
         result["pow2"] = pow2_gemm(fp8q, layers, torch, M, reps)
+    if "recal" in sections:
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
+    if "moe" in sections:
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
+    if "bf16" in sections:
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
+    if "cpu" in sections:
         for l in layers:
             del l["w"]
         result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
