@@ -404,8 +404,37 @@ def bf16_compare(layers, torch, M, reps, fp8_gemm_tflops):
         per[l["name"]] = round(f / t / 1e12, 1)
     tf = tot_f / tot_s / 1e12
     log(f"bf16 torch.matmul {tf:.1f} TFLOP/s")
-    return {"tflops": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-            "per_layer_tflops": per, "fp8_over_bf16": round(fp8_gemm_tflops / tf, 3)}
+    out = {"tflops": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+           "per_layer_tflops": per, "fp8_over_bf16": round(fp8_gemm_tflops / tf, 3)}
+    out["vendor_fp8_tensorwise"] = vendor_fp8_tensorwise(layers, torch, M, reps, fp8_gemm_tflops)
+    return out
+
+
+def vendor_fp8_tensorwise(layers, torch, M, reps, fp8_gemm_tflops):
+    """torch._scaled_mm (hipBLASLt) in E4M3 with ONE scale per tensor on the
+    same shapes: the vendor's FP8 GEMM without block scales (the library has
+    no 1x128/128x128 block-scaled mode on this platform), for context."""
+    try:
+        one = torch.ones((), device="cuda")
+        tot_s, tot_f, per = 0.0, 0.0, {}
+        for l in layers:
+            xq = l["x"].to(torch.float8_e4m3fn)
+            wq = l["w"].to(torch.float8_e4m3fn)
+            run = lambda: torch._scaled_mm(xq, wq.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            for _ in range(3):
+                run()
+            t = time_loop(run, reps, torch)
+            f = 2.0 * M * l["N"] * l["K"]
+            tot_s += t
+            tot_f += f
+            per[l["name"]] = round(f / t / 1e12, 1)
+            del xq, wq
+    except (RuntimeError, AttributeError) as e:
+        return {"error": str(e).splitlines()[0][:200]}
+    tf = tot_f / tot_s / 1e12
+    log(f"vendor fp8 tensorwise {tf:.1f} TFLOP/s")
+    return {"tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "per_layer_tflops": per,
+            "blockscaled_over_tensorwise": round(fp8_gemm_tflops / tf, 3)}
 
 
 def cpu_baseline(layers, synth, M, rows):

@@ -53,8 +53,7 @@ struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
   static constexpr int kStages = kStages_;
-  // The last kLoaders waves (one per SIMD when kLoaders = 4) issue the stage
-  // DMA; while one stalls on it, the other wave of its SIMD keeps issuing MFMAs.
+  // The last kLoaders waves issue the stage DMA.
   static constexpr int kLoaders = kLoaders_;
   static constexpr int kFirstLoader = kWaves - kLoaders;
   static constexpr int kThreads = 64 * kWaves;
@@ -63,7 +62,7 @@ struct TileCfg {
   static constexpr int kBytesB = kBN * kBK;        // weight tile
   static constexpr int kBytesA = kBM * kBK;        // token tile
   static constexpr int kBytesSA = kBM * 4;         // activation scales
-  static constexpr int kBytesSB = kLoaders * 8;    // weight scales (one copy per loader; all read copy 0)
+  static constexpr int kBytesSB = 8;               // weight scales of the tile's two 128-row blocks
   static constexpr int kOffA = kBytesB;
   static constexpr int kOffSA = kOffA + kBytesA;
   static constexpr int kOffSB = kOffSA + kBytesSA;
@@ -71,13 +70,13 @@ struct TileCfg {
   static constexpr int kLdsBytes = kStageBytes * kStages;
   static constexpr int kPiecesB = kBytesB / 1024 / kLoaders;  // 1 KB DMA pieces per loader wave
   static constexpr int kPiecesA = kBytesA / 1024 / kLoaders;
-  static constexpr int kScalesPerLoader = kBM / kLoaders;     // activation scales per loader wave
-  static_assert(kScalesPerLoader <= 64 && kBM % kLoaders == 0, "activation scales: one per lane");
-  static constexpr int kLoadsPerStage = kPiecesB + kPiecesA + 2;  // + sa, sb (per loader wave)
+  static constexpr int kPieces = kPiecesB + kPiecesA;         // operand pieces per loader wave
+  static constexpr int kScaleLoaders = kBM / 64;              // loaders 0.. each fetch 64 activation scales
+  static_assert(kScaleLoaders <= kLoaders && kBM % 64 == 0, "activation scales: one per lane");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-using CfgLarge = TileCfg<256, 8, 2, 4>;
+using CfgLarge = TileCfg<256, 8, 2, 8>;
 using CfgSmall = TileCfg<128, 4, 3, 4>;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
@@ -105,33 +104,51 @@ struct TileJob {
   int KB;
 };
 
-// Raw buffer resources of one tile's operands.  num_records bounds each one to
-// the tile's valid rows, so a load past them returns zeros (those products only
-// reach masked outputs) and never touches memory outside the tensors.
+// Raw buffer resources of the tile's scale vectors.  num_records bounds each
+// one to the tile's valid rows, so a load past them returns zeros (those
+// products only reach masked outputs) and never touches memory outside the
+// tensors.
 struct TileRsrc {
-  __amdgpu_buffer_rsrc_t b, a, sa, sb;
+  __amdgpu_buffer_rsrc_t sa, sb;
 };
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit buffer access
 
 __device__ __forceinline__ TileRsrc make_rsrc(const TileJob &t) {
   TileRsrc r;
-  r.b = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_q, (short)0, (int)(t.n_valid * t.K), kRsrcWord3);
-  r.a = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_q, (short)0, (int)(t.m_valid * t.K), kRsrcWord3);
   r.sa = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_s, (short)0, t.m_valid * t.KB * 4, kRsrcWord3);
   r.sb = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_s, (short)0, ((t.n_valid + 127) >> 7) * t.KB * 4,
                                            kRsrcWord3);
   return r;
 }
 
+// Resource of one 8-row DMA piece of an operand tile: based at row 8*piece and
+// byte kbyte of the row, bounded to the piece's valid rows (0..8), so rows
+// past the tile's last valid one read zeros exactly as with one resource per
+// tile.  Its inputs are wave-uniform, so it is built in scalar registers and a
+// lane's offset is only (row in piece)*K + chunk.  (The raw-buffer bound does
+// not cover the scalar offset operand, which is why the row offset goes into
+// the base rather than there.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t piece_rsrc(const uint8_t *rows, int valid_rows, int64_t K,
+                                                              int piece, uint32_t kbyte) {
+  int nr = valid_rows - 8 * piece;
+  nr = nr < 0 ? 0 : (nr > 8 ? 8 : nr);
+  const uint64_t base = (uint64_t)(uintptr_t)(rows + (int64_t)(8 * piece) * K + kbyte);
+  // Uniform by construction; readfirstlane tells the compiler so (it would
+  // otherwise wrap each load in a loop over distinct resource values).
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(nr * (int)K);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcWord3);
+}
+
 // Per-lane byte offsets of the DMA pattern (constant over K blocks).  Piece p
 // of a tile holds rows 8p .. 8p+7; lane l fills row 8p + l/8, LDS slot l%8,
 // which holds logical chunk c = (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (p%2).
 struct DmaLane {
-  uint32_t b[2];  // weight tile, even / odd pieces (without the piece's row offset)
-  uint32_t a[2];  // token tile
-  uint32_t sa;    // activation-scale row of this lane (lanes 0..31)
-  uint32_t sb;    // weight-scale row (lanes 0..1)
+  uint32_t rc[2];  // (row in piece)*K + chunk offset, even / odd pieces
+  uint32_t sa;     // activation-scale row of this lane (lanes 0..31)
+  uint32_t sb;     // weight-scale row (lanes 0..1)
 };
 
 template <class C>
@@ -141,51 +158,60 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
   const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t K = (uint32_t)t.K;
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    d.b[par] = row * K + ((c0 ^ par) << 4);
-    d.a[par] = d.b[par];
-  }
+  for (int par = 0; par < 2; ++par) d.rc[par] = row * K + ((c0 ^ par) << 4);
   const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
-  d.sa = (uint32_t)sa_row_of_pos(l * C::kScalesPerLoader + lane % C::kScalesPerLoader) * (uint32_t)t.KB * 4u;
+  d.sa = (uint32_t)sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane) * (uint32_t)t.KB * 4u;
   d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
   return d;
 }
 
-// The DMA of K block k into one stage buffer is kLoadsPerStage vector-memory
-// instructions per wave: kPiecesB + kPiecesA 16-byte pieces (1 KB each), one
-// 4-byte activation-scale load (32 lanes) and one weight-scale load (2 lanes).
-// issue_piece(q) issues instruction q; issue_stage issues all of them.
+// The DMA of K block k into one stage buffer: kPieces 16-byte operand pieces
+// (1 KB each) per loader wave, plus the scales -- one 64-lane activation-scale
+// load on each of the first kScaleLoaders loaders and one 2-lane weight-scale
+// load on the first.  Each load is one vector-memory instruction; a CU's
+// vector-memory path takes about one such 1 KB load every 20 clocks, so the
+// count per stage is kept at the minimum the bytes need.
 template <class C>
-__device__ __forceinline__ void issue_piece(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
-                                            uint8_t *buf, int wave, int lane, int q) {
+__device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, int k, uint8_t *buf, int wave,
+                                            int q) {
   const uint32_t kbyte = (uint32_t)k * kBK;
-  const uint32_t K8 = (uint32_t)t.K * 8u;
   const int l = wave - C::kFirstLoader;  // loader index
   if (q < C::kPiecesB) {
     const int piece = l * C::kPiecesB + q;
-    const uint32_t voff = d.b[piece & 1] + (uint32_t)piece * K8 + kbyte;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.b, (lds_void_t *)(buf + piece * 1024), 16, voff, 0, 0, 0);
-  } else if (q < C::kPiecesB + C::kPiecesA) {
-    const int piece = l * C::kPiecesA + (q - C::kPiecesB);
-    const uint32_t voff = d.a[piece & 1] + (uint32_t)piece * K8 + kbyte;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.a, (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, voff, 0, 0,
-                                             0);
-  } else if (q == C::kPiecesB + C::kPiecesA) {
-    if (lane < C::kScalesPerLoader)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * C::kScalesPerLoader * 4),
-                                               4, d.sa + (uint32_t)k * 4u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.b_q, t.n_valid, t.K, piece, kbyte),
+                                             (lds_void_t *)(buf + piece * 1024), 16, d.rc[piece & 1], 0, 0, 0);
   } else {
-    if (lane < 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + l * 8), 4,
-                                               d.sb + (uint32_t)k * 4u, 0, 0, 0);
+    const int piece = l * C::kPiecesA + (q - C::kPiecesB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.a_q, t.m_valid, t.K, piece, kbyte),
+                                             (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, d.rc[piece & 1], 0,
+                                             0, 0);
   }
+}
+
+// Number of vector-memory instructions a wave issues for one stage.
+template <class C>
+__host__ __device__ constexpr int loads_per_stage(int l) {
+  return C::kPieces + (l < C::kScaleLoaders ? 1 : 0) + (l == 0 ? 1 : 0);
+}
+
+template <class C>
+__device__ __forceinline__ void issue_scales(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
+                                             uint8_t *buf, int wave, int lane) {
+  const int l = wave - C::kFirstLoader;
+  if (l < C::kScaleLoaders)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
+                                             d.sa + (uint32_t)k * 4u, 0, 0, 0);
+  if (l == 0 && lane < 2)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
+                                             0, 0, 0);
 }
 
 template <class C>
 __device__ __forceinline__ void issue_stage(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
                                             uint8_t *buf, int wave, int lane) {
+  issue_scales<C>(t, rs, d, k, buf, wave, lane);
 #pragma unroll
-  for (int q = 0; q < C::kLoadsPerStage; ++q) issue_piece<C>(t, rs, d, k, buf, wave, lane, q);
+  for (int q = 0; q < C::kPieces; ++q) issue_piece<C>(t, d, k, buf, wave, q);
 }
 
 // The DMA of a stage that the next block issues, right after its first LDS
@@ -374,11 +400,19 @@ __device__ __forceinline__ void barrier_nofence() {
 // Wait until the DMA of block kk has landed in every wave's view: at most the
 // later blocks already issued (kk+1 .. kk+kStages-2) may still be in flight.
 template <class C>
-__device__ __forceinline__ void wait_block(int kk, int KB) {
-  if (kk + C::kStages - 2 < KB)
-    wait_vmcnt<C::kLoadsPerStage * (C::kStages - 2)>();
-  else
+__device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
+  constexpr int n = C::kStages - 2;  // stages issued after block kk's
+  const int l = wave - C::kFirstLoader;
+  if (n > 0 && kk + n < KB && l >= 0) {
+    if (l == 0)
+      wait_vmcnt<loads_per_stage<C>(0) * n>();
+    else if (l < C::kScaleLoaders)
+      wait_vmcnt<loads_per_stage<C>(1) * n>();
+    else
+      wait_vmcnt<loads_per_stage<C>(C::kScaleLoaders) * n>();
+  } else {
     wait_vmcnt<0>();
+  }
   barrier_nofence();
 }
 
@@ -388,7 +422,7 @@ template <class C, bool kPow2>
 __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict__ y, int64_t N,
                                           uint8_t *lds) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
   const int wn = wave & 1, wm = wave >> 1;
   const int KB = t.KB;
 
@@ -406,7 +440,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
   for (int s = 0; s < C::kStages - 1; ++s)
     if (s < KB && wave >= C::kFirstLoader) issue_stage<C>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
 
-  wait_block<C>(0, KB);
+  wait_block<C>(0, KB, wave);
   BlockFrags f;
   f.bad = 0;
   load_block<C, kPow2>(lds, wave, wn, wm, lane, f);
@@ -422,7 +456,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
     if (k + 1 < KB) {
       // Block k's buffer is free once every wave is past this barrier; it
       // receives block k + kStages.
-      wait_block<C>(k + 1, KB);
+      wait_block<C>(k + 1, KB, wave);
       // block k + kStages goes into block k's buffer during the next block
       dma.k = k + C::kStages;
       dma.buf = lds + cur * C::kStageBytes;
@@ -436,6 +470,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
       fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
     }
   }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   // A scale outside the power-of-two contract turns the outputs that depend
   // on it into NaN rather than into a silently wrong product.
   if (kPow2 && f.bad) {
