@@ -542,11 +542,40 @@ __device__ __forceinline__ int64_t clamp_off(const int32_t *off, int32_t g, int6
   return v < 0 ? 0 : (v > M ? M : v);
 }
 
+// Group of m slot tm: the largest g in [0, G) with S_g = floor(off[g] / kBM) + g
+// <= tm.  S is non-decreasing for valid offsets, so g is the number of groups
+// with S_g <= tm, less one.  Each lane tests one group per round of 64 and the
+// rounds' loads go out together, so a tile finds its group in one memory round
+// trip for G <= 256 (a binary search costs one dependent round trip per
+// halving -- seven for 128 experts -- before the tile's first DMA can go out).
+// The result is clamped to [0, G), which keeps every access in bounds even for
+// malformed offsets.
+template <class C>
+__device__ __forceinline__ int32_t group_of(const GemmParams &p, int64_t tm) {
+  const int lane = threadIdx.x & 63;
+  int32_t cnt = 0;
+  for (int32_t base = 0; base < p.G; base += 256) {
+    int32_t v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t g = base + r * 64 + lane;
+      v[r] = g < p.G ? p.offsets[g] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t g = base + r * 64 + lane;
+      const int64_t o = v[r] < 0 ? 0 : (v[r] > p.M ? p.M : (int64_t)v[r]);
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(g < p.G && o / C::kBM + g <= tm));
+    }
+  }
+  const int32_t g = cnt - 1;
+  return g < 0 ? 0 : (g >= p.G ? p.G - 1 : g);
+}
+
 // Dense: m slot = m tile.  Grouped: group g owns the m slots [S_g, S_{g+1})
 // with S_g = floor(off[g] / kBM) + g, which always holds ceil(rows_g / kBM)
-// tiles; a slot beyond its group's rows exits at once.  The group of a slot is
-// found by binary search over S (wave-uniform, scalar loads), so no prefix sums
-// or workspace are needed and the offsets never leave the device.
+// tiles; a slot beyond its group's rows exits at once.  No prefix sums or
+// workspace are needed and the offsets never leave the device.
 template <class C, bool kGrouped, bool kPow2>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -564,13 +593,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     m0 = tm * C::kBM;
     m_end = p.M;
   } else {
-    int32_t lo = 0, hi = p.G;  // largest g in [0, G) with S_g <= tm
-    while (hi - lo > 1) {
-      const int32_t mid = (lo + hi) >> 1;
-      const int64_t s = clamp_off(p.offsets, mid, p.M) / C::kBM + mid;
-      if (s <= tm) lo = mid; else hi = mid;
-    }
-    const int32_t g = lo;
+    const int32_t g = group_of<C>(p, tm);
     const int64_t g0 = clamp_off(p.offsets, g, p.M);
     const int64_t g1 = clamp_off(p.offsets, g + 1, p.M);
     m0 = g0 + (tm - (g0 / C::kBM + g)) * C::kBM;
