@@ -117,8 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,recal,moe,bf16,cpu",
-                    help="extra measurements after the step (comma list of pow2, recal, moe, bf16, cpu)")
+    ap.add_argument("--sections", default="pow2,fused,recal,moe,bf16,cpu",
+                    help="extra measurements after the step (comma list of pow2, fused, recal, moe, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -283,6 +283,8 @@ def main():
     sections = set() if args.skip_extras else set(args.sections.split(","))
     if "pow2" in sections:
         result["pow2"] = pow2_gemm(fp8q, layers, torch, M, reps)
+    if "fused" in sections:
+        result["fused_output_quant"] = fused_output_quant(fp8q, layers, torch, M, reps)
     if "recal" in sections:
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
     if "moe" in sections:
@@ -326,6 +328,39 @@ def pow2_gemm(fp8q, layers, torch, M, reps):
     del ops
     return {"gemm_tflops": round(tf, 1), "gemm_frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
             "step_tflops": round(g_f / t_step / 1e12, 1), "per_layer": per}
+
+
+def fused_output_quant(fp8q, layers, torch, M, reps):
+    """Each layer's GEMM with its output quantized for the next FP8 layer (E4M3,
+    1x128 blocks): the GEMM followed by a separate activation-quantization pass
+    over its bf16 output, against the GEMM whose epilogue quantizes (one
+    kernel; the bf16 output never goes to memory).  Same bytes either way."""
+    per, t_sep, t_fus, flops = {}, 0.0, 0.0, 0.0
+    for l in layers:
+        aq, as_, bq, bs, y = l["aq"], l["as_"], l["bq"], l["bs"], l["y"]
+        yq = torch.empty((M, l["N"]), dtype=torch.uint8, device=y.device)
+        ys = torch.empty((M, l["N"] // 128), dtype=torch.float32, device=y.device)
+
+        def separate():
+            fp8q.fp8_blockscaled_gemm(aq, as_, bq, bs, out=y)
+            fp8q.fp8_quant_act_1x128(y, "amax", out=(yq, ys))
+
+        def fused():
+            fp8q.fp8_blockscaled_gemm_quant(aq, as_, bq, bs, "amax", out=(yq, ys))
+        separate()
+        fused()
+        ts = time_loop(separate, reps, torch)
+        tf = time_loop(fused, reps, torch)
+        f = 2.0 * M * l["N"] * l["K"]
+        t_sep += ts
+        t_fus += tf
+        flops += f
+        per[l["name"]] = {"separate_us": round(ts * 1e6, 2), "fused_us": round(tf * 1e6, 2),
+                          "fused_tflops": round(f / tf / 1e12, 1), "speedup": round(ts / tf, 3)}
+        del yq, ys
+    log(f"fused output quant: {flops / t_fus / 1e12:.1f} TFLOP/s vs {flops / t_sep / 1e12:.1f} separate")
+    return {"fused_tflops": round(flops / t_fus / 1e12, 1), "separate_tflops": round(flops / t_sep / 1e12, 1),
+            "speedup": round(t_sep / t_fus, 3), "per_layer": per}
 
 
 def recalibration(fp8q, synth, torch, dev, copy_gbs=None):

@@ -25,7 +25,7 @@ _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
-           "fp8_grouped_gemm_pow2", "abi_version", "library_path"]
+           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "abi_version", "library_path"]
 
 
 def library_path():
@@ -129,6 +129,33 @@ def fp8_blockscaled_gemm_pow2(a_q, a_s, b_q, b_s, out=None):
     """As fp8_blockscaled_gemm, for scales that are all powers of two (the
     matrix cores apply them); an output that depends on any other scale is NaN."""
     return _gemm("fp8_blockscaled_gemm_pow2", a_q, a_s, b_q, b_s, out)
+
+
+def fp8_blockscaled_gemm_quant(a_q, a_s, b_q, b_s, mode="amax", out=None):
+    """The GEMM with its output quantized for the next FP8 layer:
+    (y_q uint8 [M, N] E4M3 codes, y_s fp32 [M, N/128]), equal to
+    fp8_quant_act_1x128(fp8_blockscaled_gemm(...), mode)."""
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 2)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 2)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K or tuple(a_s.shape) != (M, K // 128) or tuple(b_s.shape) != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        yq = torch.empty((M, N), dtype=torch.uint8, device=a_q.device)
+        ys = torch.empty((M, N // 128), dtype=torch.float32, device=a_q.device)
+    else:
+        yq, ys = out
+    yq, pyq = _as_bytes(yq, "y_q", 2)
+    pys = _dev(ys, "y_s", torch.float32, 2)
+    if tuple(yq.shape) != (M, N) or tuple(ys.shape) != (M, N // 128):
+        raise ValueError("output shapes do not match")
+    _lib.check("fp8_blockscaled_gemm_quant",
+               _lib.load().fp8_blockscaled_gemm_quant(pa, pas, pb, pbs, pyq, pys, M, N, K, _mode(mode),
+                                                      _stream(a_q)))
+    return yq, ys
 
 
 def _grouped(fn, a_q, a_s, b_q, b_s, group_offsets, out):

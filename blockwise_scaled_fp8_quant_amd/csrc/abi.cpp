@@ -113,6 +113,26 @@ fp8q_status gemm_entry(const char *fn, const uint8_t *a_q, const float *a_s, con
   return launched(fp8q::launch_blockscaled_gemm(a_q, a_s, b_q, b_s, y, M, N, K, pow2, (hipStream_t)stream), fn);
 }
 
+fp8q_status gemm_quant_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                             const float *b_s, uint8_t *y_q, float *y_s, int64_t M, int64_t N, int64_t K, int mode,
+                             void *stream) {
+  g_last_error.clear();
+  if (mode != FP8Q_SCALE_AMAX && mode != FP8Q_SCALE_POW2) return fail(FP8Q_EINVAL, fn, "unknown mode");
+  if (!(M >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (N % 128 != 0) return fail(FP8Q_ESHAPE, fn, "N must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31)) return fail(FP8Q_EINVAL, fn, "M or N too large");
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (!(a_q && a_s && b_q && b_s && y_q && y_s)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y_q) && aligned16(y_s)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(
+      fp8q::launch_blockscaled_gemm_quant(a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, (hipStream_t)stream), fn);
+}
+
 fp8q_status grouped_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
                           const float *b_s, const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N,
                           int64_t K, uint16_t *y, bool pow2, void *stream) {
@@ -150,6 +170,12 @@ fp8q_status fp8_blockscaled_gemm_pow2(const uint8_t *a_q, const float *a_s, cons
                                       const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
                                       void *stream) {
   return gemm_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, true, stream);
+}
+
+fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                       const float *b_s, uint8_t *y_q, float *y_s, int64_t M, int64_t N,
+                                       int64_t K, int mode, void *stream) {
+  return gemm_quant_entry(__func__, a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, stream);
 }
 
 fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,

@@ -22,6 +22,13 @@ hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
                                    uint16_t *y, int64_t M, int64_t N, int64_t K,
                                    bool pow2, hipStream_t stream);
 
+// The same GEMM with its output quantized to E4M3 in 1x128 blocks along N
+// (mode: scale rule of those blocks), equal to quantizing the bf16 output.
+hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
+                                         const uint8_t *b_q, const float *b_s,
+                                         uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
+                                         int mode, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const uint8_t *b_q, const float *b_s,
                                const int32_t *group_offsets, int32_t G,

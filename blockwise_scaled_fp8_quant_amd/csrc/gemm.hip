@@ -416,11 +416,20 @@ __device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
   barrier_nofence();
 }
 
+// Output of a tile: bf16 Y, or Y quantized to E4M3 in 1x128 blocks along N
+// with the activation quantizer's rule (kOut = its scale mode).
+constexpr int kOutBf16 = -1;
+
+struct TileOut {
+  uint16_t *y;   // bf16: tile origin of Y [M][N]
+  uint8_t *yq;   // E4M3: tile origin of Yq [M][N]
+  float *ys;     // E4M3: tile origin of the scales [M][N/128]
+};
+
 // One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
-// n_valid), written to y (row stride N) at y[0][0].
-template <class C, bool kPow2>
-__device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict__ y, int64_t N,
-                                          uint8_t *lds) {
+// n_valid), written at the tile origins in o (row stride N).
+template <class C, bool kPow2, int kOut>
+__device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
   const int wn = wave & 1, wm = wave >> 1;
@@ -482,20 +491,64 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, uint16_t *__restrict
         for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
   }
 
-  // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.
+  if constexpr (kOut == kOutBf16) {
+    // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.
+    uint16_t *__restrict__ y = o.y;
 #pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) {
-    const int r = wm * 64 + mi * 16 + (lane & 15);
-    if (r < t.m_valid) {
-      uint16_t *yrow = y + (int64_t)r * N;
+    for (int mi = 0; mi < kSubM; ++mi) {
+      const int r = wm * 64 + mi * 16 + (lane & 15);
+      if (r < t.m_valid) {
+        uint16_t *yrow = y + (int64_t)r * N;
 #pragma unroll
-      for (int ni = 0; ni < kSubN; ++ni) {
-        const int nn = wn * 128 + ni * 16 + 4 * (lane >> 4);
-        if (nn < t.n_valid) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
-          o.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
-          *reinterpret_cast<uint2 *>(yrow + nn) = o;
+        for (int ni = 0; ni < kSubN; ++ni) {
+          const int nn = wn * 128 + ni * 16 + 4 * (lane >> 4);
+          if (nn < t.n_valid) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+            w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+            *reinterpret_cast<uint2 *>(yrow + nn) = w;
+          }
+        }
+      }
+    }
+  } else {
+    // Quantized epilogue (the activation quantization of the next layer, done
+    // by the producer instead of by a separate pass over bf16 Y; page 1,
+    // "Leistungsgewinne in der Praxis", names quantization-kernel overhead as
+    // part of the gap to the ideal speedup).  Each value is first rounded to
+    // bf16 exactly as the bf16 epilogue rounds it; a wave's 128 columns are
+    // one 1x128 block of each of its rows, held by the lanes l, l^16, l^32,
+    // l^48.  Block |max|, scale and element rule are those of the activation
+    // quantizer, so the result equals quantizing the bf16 output bit for bit.
+    if (wn * 128 < t.n_valid) {
+      const int64_t nbo = N >> 7;  // scale blocks per output row
+#pragma unroll
+      for (int mi = 0; mi < kSubM; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        uint32_t h[kSubN][2];
+        float amax = 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) {
+          h[ni][0] = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+          h[ni][1] = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+          amax = max3_abs(amax, bf16_lo(h[ni][0]), bf16_hi(h[ni][0]));
+          amax = max3_abs(amax, bf16_lo(h[ni][1]), bf16_hi(h[ni][1]));
+        }
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+        const BlockQ bq = block_params<kOut>(amax);
+        if (r < t.m_valid) {
+          if ((lane >> 4) == 0) o.ys[(int64_t)r * nbo + wn] = bq.s;
+          uint8_t *qrow = o.yq + (int64_t)r * N + wn * 128 + 4 * (lane >> 4);
+#pragma unroll
+          for (int ni = 0; ni < kSubN; ++ni) {
+            const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
+            float qv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+            *reinterpret_cast<uint32_t *>(qrow + ni * 16) = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+          }
         }
       }
     }
@@ -529,7 +582,9 @@ struct GemmParams {
   const uint8_t *b_q;
   const float *b_s;
   const int32_t *offsets;  // grouped: [G+1] on the device; dense: unused
-  uint16_t *y;
+  uint16_t *y;             // bf16 output
+  uint8_t *yq;             // E4M3 output (quantized epilogue)
+  float *ys;               // its 1x128 scales
   int64_t M;  // dense: M; grouped: M_total
   int64_t N, K;
   int64_t slots_m;
@@ -576,7 +631,7 @@ __device__ __forceinline__ int32_t group_of(const GemmParams &p, int64_t tm) {
 // with S_g = floor(off[g] / kBM) + g, which always holds ceil(rows_g / kBM)
 // tiles; a slot beyond its group's rows exits at once.  No prefix sums or
 // workspace are needed and the offsets never leave the device.
-template <class C, bool kGrouped, bool kPow2>
+template <class C, bool kGrouped, bool kPow2, int kOut>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -612,38 +667,46 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   t.b_s = bs + (n0 >> 7) * t.KB;
   t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
   t.n_valid = n_valid;
-  gemm_tile<C, kPow2>(t, p.y + m0 * p.N + n0, p.N, lds);
+  TileOut o{nullptr, nullptr, nullptr};
+  if constexpr (kOut == kOutBf16)
+    o.y = p.y + m0 * p.N + n0;
+  else {
+    o.yq = p.yq + m0 * p.N + n0;
+    o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
+  }
+  gemm_tile<C, kPow2, kOut>(t, o, p.N, lds);
 }
 
-template <class C, bool kGrouped, bool kPow2>
+template <class C, bool kGrouped, bool kPow2, int kOut = kOutBf16>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2, kOut>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t grid = p.slots_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2>), dim3((unsigned)grid), dim3(C::kThreads),
+  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2, kOut>), dim3((unsigned)grid), dim3(C::kThreads),
                      C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
-template <bool kPow2>
+template <bool kPow2, int kOut = kOutBf16>
 static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
-                        uint16_t *y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                        uint16_t *y, uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
+                        hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, M, N, K, 0, 1, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, M, N, K, 0, 1, tiles_n};
   // Large tiles when they still give at least one tile per CU.
   const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
   if (large_tiles >= 256) {
     p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
-    return launch<CfgLarge, false, kPow2>(p, stream);
+    return launch<CfgLarge, false, kPow2, kOut>(p, stream);
   }
   p.slots_m = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  return launch<CfgSmall, false, kPow2>(p, stream);
+  return launch<CfgSmall, false, kPow2, kOut>(p, stream);
 }
 
 template <bool kPow2>
@@ -652,7 +715,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
                           uint16_t *y, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, M_total, N, K, 0, G, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, M_total, N, K, 0, G, tiles_n};
   // 256-row tiles once the average group fills one; their ragged last tile
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
@@ -667,8 +730,16 @@ hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
                                    const uint8_t *b_q, const float *b_s,
                                    uint16_t *y, int64_t M, int64_t N, int64_t K,
                                    bool pow2, hipStream_t stream) {
-  return pow2 ? dense<true>(a_q, a_s, b_q, b_s, y, M, N, K, stream)
-              : dense<false>(a_q, a_s, b_q, b_s, y, M, N, K, stream);
+  return pow2 ? dense<true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream)
+              : dense<false>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream);
+}
+
+hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
+                                         const uint8_t *b_q, const float *b_s,
+                                         uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
+                                         int mode, hipStream_t stream) {
+  return mode == kModePow2 ? dense<false, kModePow2>(a_q, a_s, b_q, b_s, nullptr, yq, ys, M, N, K, stream)
+                           : dense<false, kModeAmax>(a_q, a_s, b_q, b_s, nullptr, yq, ys, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,

@@ -115,6 +115,27 @@ fp8q_status fp8_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
                                  void *stream);
 
 /*
+ * The same GEMM with its output quantized for the next FP8 layer: Y is
+ * computed and rounded to bf16 exactly as by fp8_blockscaled_gemm, and then
+ * quantized in 1x128 blocks along N exactly as fp8_quant_act_1x128 quantizes
+ * a bf16 input -- in the GEMM's epilogue, so the bf16 Y never goes to memory
+ * and no separate quantization pass reads it back (page 1, "Leistungsgewinne
+ * in der Praxis": quantization-kernel overhead is part of the gap between the
+ * FP8 linear layers' gain and the ideal 2x).
+ *   a_q, a_s, b_q, b_s as for fp8_blockscaled_gemm
+ *   y_q [M][N] E4M3 bytes (out)
+ *   y_s [M][N/128] fp32 (out): block (m, nb) covers Y[m][128*nb .. 128*nb+127]
+ *   mode fp8q_scale_mode of the output blocks
+ * y_q and y_s are bit-identical to fp8_quant_act_1x128(mode) applied to the
+ * y of fp8_blockscaled_gemm on the same inputs.
+ */
+fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
+                                       const uint8_t *b_q, const float *b_s,
+                                       uint8_t *y_q, float *y_s,
+                                       int64_t M, int64_t N, int64_t K, int mode,
+                                       void *stream);
+
+/*
  * Grouped block-scaled FP8 GEMM for mixture-of-experts layers (the recipe's
  * MoE models on page 1, "Leistungsgewinne in der Praxis" and "Warum dies fuer
  * die KI-Oekonomie wichtig ist"): group g owns rows

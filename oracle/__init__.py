@@ -14,6 +14,8 @@ from .oracle import (  # noqa: F401
     quant_act_1x128,
     quant_weight_128x128,
     gemm_f64,
+    round_bf16,
+    gemm_quant_1x128,
     gemm_sampled_f64,
     grouped_gemm_f64,
     grouped_gemm_sampled_f64,

@@ -140,6 +140,26 @@ def gemm_f64(aq, as_, bq, bs):
     return y
 
 
+def round_bf16(y):
+    """fp64 values -> bf16 bit patterns (uint16), rounded once to the nearest
+    bf16 with ties to an even mantissa (IEEE-754 round-to-nearest-even at 8
+    significant bits; below 2^-126 the bf16 spacing is 2^-133).  Finite
+    inputs of magnitude below the bf16 overflow threshold."""
+    y = np.asarray(y, dtype=np.float64)
+    _, e = np.frexp(y)                        # |y| = m * 2^e, 0.5 <= m < 1
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))   # bf16 spacing at |y|
+    r = np.round(y / step) * step             # exact quotient; round half to even
+    r = np.where(y == 0.0, y, r)              # keeps -0.0
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gemm_quant_1x128(aq, as_, bq, bs, mode=MODE_AMAX):
+    """The GEMM output Y = dequant(aq, as_) @ dequant(bq, bs)^T, rounded once to
+    bf16, then quantized for the next layer in 1x128 blocks along N by the same
+    rule as quant_act_1x128.  Returns (q uint8 [M, N], s f32 [M, N/128])."""
+    return quant_act_1x128(round_bf16(gemm_f64(aq, as_, bq, bs)), mode)
+
+
 def gemm_sampled_f64(aq, as_, bq, bs, ms, ns):
     aq = _c(aq, np.uint8)
     bq = _c(bq, np.uint8)

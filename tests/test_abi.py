@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
+              "fp8_blockscaled_gemm_quant",
               "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
@@ -82,6 +83,19 @@ def test_gemm_argument_errors(lib, fn):
     assert f(None, None, None, None, None, 0, 128, 128, None) == 0
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, None) == 2   # K too large
     assert "K" in _err(lib)
+
+
+def test_gemm_quant_argument_errors(lib):
+    f = lib.fp8_blockscaled_gemm_quant
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 128, 7, None) == 1      # unknown mode
+    assert "mode" in _err(lib)
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, 0, None) == 2      # K not a multiple of 128
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 100, 128, 1, None) == 2      # N not a multiple of 128
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 128, 128, 0, None) == 1
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 128, 128, 0, None) == 1      # null scales out
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 64, 128, 128, 0, None) == 3       # misaligned y_q
+    assert f(None, None, None, None, None, None, 0, 128, 128, 0, None) == 0       # empty call
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, 0, None) == 2
 
 
 @pytest.mark.parametrize("fn", ["fp8_grouped_gemm", "fp8_grouped_gemm_pow2"])
