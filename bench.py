@@ -117,8 +117,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,recal,moe,bf16,cpu",
-                    help="extra measurements after the step (comma list of pow2, fused, recal, moe, bf16, cpu)")
+    ap.add_argument("--sections", default="pow2,fused,recal,moe,dispatch,bf16,cpu",
+                    help="extra measurements after the step "
+                         "(comma list of pow2, fused, recal, moe, dispatch, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -289,6 +290,8 @@ def main():
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
     if "moe" in sections:
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
+    if "dispatch" in sections:
+        result["moe_dispatch"] = dispatch(fp8q, synth, torch, dev, reps)
     if "bf16" in sections:
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
     if "cpu" in sections:
@@ -422,6 +425,67 @@ def moe(fp8q, synth, torch, dev, reps):
             log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}")
             del x, bq, bs, aq, as_, y
             torch.cuda.empty_cache()
+    return out
+
+
+def dispatch(fp8q, synth, torch, dev, reps):
+    """MoE gate_up layer with the tokens quantized before dispatch (quantize T
+    token rows once, then the grouped GEMM gathers each routed row's FP8 bytes
+    by index) against quantizing after dispatch (gather the bf16 rows, quantize
+    all M_total routed rows, grouped GEMM).  The bf16 gather is torch's index
+    copy, standing in for the dispatch of bf16 rows on one GPU."""
+    out = {}
+    for shape in (synth.QWEN3, synth.MOONLIGHT):
+        xt, row_token, w, off = synth.moe_dispatch_inputs(shape, device=dev)
+        G, N, K = w.shape
+        T, Mt = xt.shape[0], row_token.size
+        bq = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+        bs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for g in range(G):
+            fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
+        del w
+        offd = torch.from_numpy(off).to(dev)
+        idx64 = torch.from_numpy(row_token).to(dev)
+        idx = idx64.to(torch.int32)
+        xr = torch.empty((Mt, K), dtype=torch.bfloat16, device=dev)
+        aq_r = torch.empty((Mt, K), dtype=torch.uint8, device=dev)
+        as_r = torch.empty((Mt, K // 128), dtype=torch.float32, device=dev)
+        aq_t = torch.empty((T, K), dtype=torch.uint8, device=dev)
+        as_t = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+
+        def after():
+            torch.index_select(xt, 0, idx64, out=xr)
+            fp8q.fp8_quant_act_1x128(xr, out=(aq_r, as_r))
+            fp8q.fp8_grouped_gemm(aq_r, as_r, bq, bs, offd, out=y)
+
+        def before():
+            fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t))
+            fp8q.fp8_grouped_gemm_gather(aq_t, as_t, bq, bs, offd, idx, out=y)
+
+        after()
+        before()
+        t_after = time_loop(after, reps, torch)
+        t_before = time_loop(before, reps, torch)
+        t_copy = time_loop(lambda: torch.index_select(xt, 0, idx64, out=xr), reps, torch)
+        t_qr = time_loop(lambda: fp8q.fp8_quant_act_1x128(xr, out=(aq_r, as_r)), reps, torch)
+        t_qt = time_loop(lambda: fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t)), reps, torch)
+        t_gr = time_loop(lambda: fp8q.fp8_grouped_gemm(aq_r, as_r, bq, bs, offd, out=y), reps, torch)
+        t_gg = time_loop(lambda: fp8q.fp8_grouped_gemm_gather(aq_t, as_t, bq, bs, offd, idx, out=y), reps, torch)
+        us = lambda t: round(t * 1e6, 2)
+        out[shape.name] = {
+            "tokens": T, "rows": Mt, "groups": G, "N": N, "K": K,
+            "after_us": us(t_after), "before_us": us(t_before),
+            "before_speedup": round(t_after / t_before, 3),
+            "bf16_gather_copy_us": us(t_copy), "quant_routed_rows_us": us(t_qr), "quant_tokens_us": us(t_qt),
+            "grouped_gemm_us": us(t_gr), "gather_gemm_us": us(t_gg),
+            "gather_gemm_over_grouped": round(t_gg / t_gr, 3),
+            "dispatched_bytes_bf16": Mt * K * 2, "dispatched_bytes_fp8": Mt * K + Mt * (K // 128) * 4,
+        }
+        log(f"dispatch {shape.name}: after {t_after * 1e6:.1f} us, before {t_before * 1e6:.1f} us "
+            f"(gather GEMM {t_gg * 1e6:.1f} vs grouped {t_gr * 1e6:.1f} us)")
+        del xt, bq, bs, xr, aq_r, as_r, aq_t, as_t, y
+        torch.cuda.empty_cache()
     return out
 
 

@@ -25,7 +25,8 @@ _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
-           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "abi_version", "library_path"]
+           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "abi_version",
+           "library_path"]
 
 
 def library_path():
@@ -191,3 +192,36 @@ def fp8_grouped_gemm(a_q, a_s, b_q, b_s, group_offsets, out=None):
 def fp8_grouped_gemm_pow2(a_q, a_s, b_q, b_s, group_offsets, out=None):
     """As fp8_grouped_gemm, for scales that are all powers of two."""
     return _grouped("fp8_grouped_gemm_pow2", a_q, a_s, b_q, b_s, group_offsets, out)
+
+
+def fp8_grouped_gemm_gather(a_q, a_s, b_q, b_s, group_offsets, row_index, mode="amax", out=None):
+    """Grouped GEMM over routed rows gathered from a quantized token matrix.
+
+    a_q [T, K], a_s [T, K/128] (the tokens, quantized once before dispatch),
+    b_q [G, N, K], b_s [G, N/128, K/128], group_offsets int32 [G+1] and
+    row_index int32 [M_total] in device memory: routed row r reads token
+    row_index[r] (rows with an index outside [0, T) come out as zeros).
+    mode 'amax' for any scales, 'pow2' for power-of-two scales.
+    Returns Y bf16 [M_total, N], equal to fp8_grouped_gemm on a_q[row_index].
+    """
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 3)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 3)
+    poff = _dev(group_offsets, "group_offsets", torch.int32, 1)
+    pidx = _dev(row_index, "row_index", torch.int32, 1)
+    T, K = a_q.shape
+    G, N, Kb = b_q.shape
+    M = row_index.numel()
+    if Kb != K or tuple(a_s.shape) != (T, K // 128) or tuple(b_s.shape) != (G, N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    if group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must have G+1 entries")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
+    py = _dev(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_grouped_gemm_gather",
+               _lib.load().fp8_grouped_gemm_gather(pa, pas, T, pb, pbs, poff, pidx, G, M, N, K, py,
+                                                   _mode(mode), _stream(a_q)))
+    return y

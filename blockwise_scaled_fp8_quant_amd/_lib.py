@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "FP8Q_OK", 1: "FP8Q_EINVAL", 2: "FP8Q_ESHAPE", 3: "FP8Q_EALIG
                 4: "FP8Q_EDEVICE", 5: "FP8Q_EHIP"}
 ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-                "fp8_blockscaled_gemm_quant",
+                "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
                 "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version")
 
 _lib = None
@@ -49,6 +49,8 @@ def load():
     for name in ("fp8_grouped_gemm", "fp8_grouped_gemm_pow2"):
         getattr(lib, name).argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, p]
         getattr(lib, name).restype = ci
+    lib.fp8_grouped_gemm_gather.argtypes = [p, p, i64, p, p, p, p, i32, i64, i64, i64, p, ci, p]
+    lib.fp8_grouped_gemm_gather.restype = ci
     lib.fp8q_status_string.argtypes = [ci]
     lib.fp8q_status_string.restype = ctypes.c_char_p
     lib.fp8q_last_error.argtypes = []

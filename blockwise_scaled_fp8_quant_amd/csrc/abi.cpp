@@ -156,6 +156,34 @@ fp8q_status grouped_entry(const char *fn, const uint8_t *a_q, const float *a_s, 
                   fn);
 }
 
+fp8q_status gather_entry(const char *fn, const uint8_t *a_q, const float *a_s, int64_t T, const uint8_t *b_q,
+                         const float *b_s, const int32_t *group_offsets, const int32_t *row_index, int32_t G,
+                         int64_t M_total, int64_t N, int64_t K, uint16_t *y, int mode, void *stream) {
+  g_last_error.clear();
+  if (mode != FP8Q_SCALE_AMAX && mode != FP8Q_SCALE_POW2) return fail(FP8Q_EINVAL, fn, "unknown mode");
+  if (G < 1) return fail(FP8Q_EINVAL, fn, "G must be >= 1");
+  if (!(T >= 0 && M_total >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (N % 128 != 0) return fail(FP8Q_ESHAPE, fn, "N must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M_total < ((int64_t)1 << 31) && N <= ((int64_t)1 << 31)))
+    return fail(FP8Q_EINVAL, fn, "M_total or N too large");
+  // Gathered rows are addressed by 32-bit byte offsets into the token matrix.
+  if (T >= ((int64_t)1 << 31) / K) return fail(FP8Q_ESHAPE, fn, "token matrix T*K must be below 2^31 bytes");
+  if (M_total == 0 || N == 0) return FP8Q_OK;
+  if (T == 0) return fail(FP8Q_EINVAL, fn, "T must be positive when there are routed rows");
+  if (!(a_q && a_s && b_q && b_s && y && group_offsets && row_index))
+    return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y) &&
+        aligned16(group_offsets) && aligned16(row_index)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_grouped_gemm_gather(a_q, a_s, T, b_q, b_s, group_offsets, row_index, G, M_total, N,
+                                                   K, y, mode == FP8Q_SCALE_POW2, (hipStream_t)stream),
+                  fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +216,14 @@ fp8q_status fp8_grouped_gemm_pow2(const uint8_t *a_q, const float *a_s, const ui
                                   const float *b_s, const int32_t *group_offsets, int32_t G,
                                   int64_t M_total, int64_t N, int64_t K, uint16_t *y, void *stream) {
   return grouped_entry(__func__, a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, true, stream);
+}
+
+fp8q_status fp8_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T, const uint8_t *b_q,
+                                    const float *b_s, const int32_t *group_offsets, const int32_t *row_index,
+                                    int32_t G, int64_t M_total, int64_t N, int64_t K, uint16_t *y, int mode,
+                                    void *stream) {
+  return gather_entry(__func__, a_q, a_s, T, b_q, b_s, group_offsets, row_index, G, M_total, N, K, y, mode,
+                      stream);
 }
 
 const char *fp8q_status_string(int status) {

@@ -35,4 +35,12 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                int64_t M_total, int64_t N, int64_t K,
                                uint16_t *y, bool pow2, hipStream_t stream);
 
+// Grouped GEMM whose token rows are gathered: routed row r reads token row
+// row_index[r] of a_q [T][K] / a_s [T][K/128] (quantize before dispatch).
+hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T,
+                                      const uint8_t *b_q, const float *b_s,
+                                      const int32_t *group_offsets, const int32_t *row_index, int32_t G,
+                                      int64_t M_total, int64_t N, int64_t K, uint16_t *y, bool pow2,
+                                      hipStream_t stream);
+
 }  // namespace fp8q

@@ -94,8 +94,10 @@ __device__ __forceinline__ int sa_row_of_pos(int p) {
 }
 
 struct TileJob {
-  const uint8_t *a_q;  // row 0 of the token tile
-  const float *a_s;    // scale row of token row 0
+  const uint8_t *a_q;  // row 0 of the token tile (gathered: the token matrix)
+  const float *a_s;    // scale row of token row 0 (gathered: the scale matrix)
+  const int32_t *gidx; // gathered: source token row of each tile row; else null
+  int64_t T;           // gathered: rows of the token matrix
   const uint8_t *b_q;  // row 0 of the weight tile
   const float *b_s;    // weight-scale row of the tile's first 128 rows
   int m_valid;         // token rows in the tile (1..kBM)
@@ -114,9 +116,12 @@ struct TileRsrc {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit buffer access
 
+template <bool kGather = false>
 __device__ __forceinline__ TileRsrc make_rsrc(const TileJob &t) {
   TileRsrc r;
-  r.sa = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_s, (short)0, t.m_valid * t.KB * 4, kRsrcWord3);
+  // gathered: bounded to the whole scale matrix (the lanes' offsets select rows)
+  r.sa = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_s, (short)0,
+                                           kGather ? (int)(t.T * t.KB * 4) : t.m_valid * t.KB * 4, kRsrcWord3);
   r.sb = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_s, (short)0, ((t.n_valid + 127) >> 7) * t.KB * 4,
                                            kRsrcWord3);
   return r;
@@ -142,6 +147,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t piece_rsrc(const uint8_t *rows
   return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcWord3);
 }
 
+constexpr int kMaxPiecesA = 4;
+// An offset at or past every gathered resource's bound (token matrices are
+// limited to fewer than 2^31 bytes).
+constexpr uint32_t kGatherOOB = 0x80000000u;
+
+// Resource over a whole gathered token matrix [T][K], based at byte kbyte of
+// row 0; each lane's offset selects its row.  The bound T*K - kbyte (at least
+// 128, as T >= 1) makes a valid row's 16 bytes always in range and kGatherOOB
+// always out of it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gather_rsrc(const uint8_t *a, int64_t T, int64_t K,
+                                                               uint32_t kbyte) {
+  const uint64_t base = (uint64_t)(uintptr_t)(a + kbyte);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(T * K - (int64_t)kbyte));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcWord3);
+}
+
 // Per-lane byte offsets of the DMA pattern (constant over K blocks).  Piece p
 // of a tile holds rows 8p .. 8p+7; lane l fills row 8p + l/8, LDS slot l%8,
 // which holds logical chunk c = (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (p%2).
@@ -149,9 +172,14 @@ struct DmaLane {
   uint32_t rc[2];  // (row in piece)*K + chunk offset, even / odd pieces
   uint32_t sa;     // activation-scale row of this lane (lanes 0..31)
   uint32_t sb;     // weight-scale row (lanes 0..1)
+  // Gathered token rows: this lane's byte offset in the token matrix for each
+  // of its loader's token pieces, and of its scale row; kGatherOOB for a row
+  // past the tile or an index outside [0, T), which then reads zeros.
+  uint32_t ga[kMaxPiecesA];
+  uint32_t gsa;
 };
 
-template <class C>
+template <class C, bool kGather = false>
 __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane) {
   DmaLane d;
   const uint32_t row = (uint32_t)(lane >> 3);
@@ -162,6 +190,22 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
   const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
   d.sa = (uint32_t)sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane) * (uint32_t)t.KB * 4u;
   d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
+  if constexpr (kGather) {
+    static_assert(C::kPiecesA <= kMaxPiecesA, "gather offsets per lane");
+    auto src = [&](int r) -> int64_t {  // source token row of tile row r, or -1
+      if (l < 0 || r >= t.m_valid) return -1;
+      const int64_t s = t.gidx[r];
+      return (s >= 0 && s < t.T) ? s : -1;
+    };
+#pragma unroll
+    for (int i = 0; i < C::kPiecesA; ++i) {
+      const int piece = l * C::kPiecesA + i;
+      const int64_t s = src(8 * piece + (int)row);
+      d.ga[i] = s < 0 ? kGatherOOB : (uint32_t)s * K + ((c0 ^ (uint32_t)(piece & 1)) << 4);
+    }
+    const int64_t s = src(sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane));
+    d.gsa = s < 0 ? kGatherOOB : (uint32_t)s * (uint32_t)t.KB * 4u;
+  }
   return d;
 }
 
@@ -171,7 +215,7 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
 // load on the first.  Each load is one vector-memory instruction; a CU's
 // vector-memory path takes about one such 1 KB load every 20 clocks, so the
 // count per stage is kept at the minimum the bytes need.
-template <class C>
+template <class C, bool kGather>
 __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, int k, uint8_t *buf, int wave,
                                             int q) {
   const uint32_t kbyte = (uint32_t)k * kBK;
@@ -182,9 +226,14 @@ __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, 
                                              (lds_void_t *)(buf + piece * 1024), 16, d.rc[piece & 1], 0, 0, 0);
   } else {
     const int piece = l * C::kPiecesA + (q - C::kPiecesB);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.a_q, t.m_valid, t.K, piece, kbyte),
-                                             (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, d.rc[piece & 1], 0,
-                                             0, 0);
+    if constexpr (kGather)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gather_rsrc(t.a_q, t.T, t.K, kbyte),
+                                               (lds_void_t *)(buf + C::kOffA + piece * 1024), 16,
+                                               d.ga[q - C::kPiecesB], 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.a_q, t.m_valid, t.K, piece, kbyte),
+                                               (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, d.rc[piece & 1],
+                                               0, 0, 0);
   }
 }
 
@@ -194,24 +243,24 @@ __host__ __device__ constexpr int loads_per_stage(int l) {
   return C::kPieces + (l < C::kScaleLoaders ? 1 : 0) + (l == 0 ? 1 : 0);
 }
 
-template <class C>
+template <class C, bool kGather>
 __device__ __forceinline__ void issue_scales(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
                                              uint8_t *buf, int wave, int lane) {
   const int l = wave - C::kFirstLoader;
   if (l < C::kScaleLoaders)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
-                                             d.sa + (uint32_t)k * 4u, 0, 0, 0);
+                                             (kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
   if (l == 0 && lane < 2)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
                                              0, 0, 0);
 }
 
-template <class C>
+template <class C, bool kGather>
 __device__ __forceinline__ void issue_stage(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
                                             uint8_t *buf, int wave, int lane) {
-  issue_scales<C>(t, rs, d, k, buf, wave, lane);
+  issue_scales<C, kGather>(t, rs, d, k, buf, wave, lane);
 #pragma unroll
-  for (int q = 0; q < C::kPieces; ++q) issue_piece<C>(t, d, k, buf, wave, q);
+  for (int q = 0; q < C::kPieces; ++q) issue_piece<C, kGather>(t, d, k, buf, wave, q);
 }
 
 // The DMA of a stage that the next block issues, right after its first LDS
@@ -339,7 +388,7 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 // E8M0 scale operands of each MFMA carry the weight block's and the token
 // row's exponents, and the MFMA accumulates straight into acc -- no partial
 // products and no folds.
-template <class C, bool kPow2>
+template <class C, bool kPow2, bool kGather>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const StageDma &dma) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -355,7 +404,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       __builtin_amdgcn_sched_barrier(0);
       if (ni + kWAhead < kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * 128 + (ni + kWAhead) * 16, lane);
       if (ni == 0 && dma.on && dma.wave >= C::kFirstLoader)
-        issue_stage<C>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
+        issue_stage<C, kGather>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kPow2) {
@@ -428,7 +477,7 @@ struct TileOut {
 
 // One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
 // n_valid), written at the tile origins in o (row stride N).
-template <class C, bool kPow2, int kOut>
+template <class C, bool kPow2, int kOut, bool kGather>
 __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
@@ -441,13 +490,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  const TileRsrc rs = make_rsrc(t);
-  const DmaLane dl = dma_lane<C>(t, wave, lane);
+  const TileRsrc rs = make_rsrc<kGather>(t);
+  const DmaLane dl = dma_lane<C, kGather>(t, wave, lane);
 
   // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < KB && wave >= C::kFirstLoader) issue_stage<C>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
+    if (s < KB && wave >= C::kFirstLoader)
+      issue_stage<C, kGather>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
 
   wait_block<C>(0, KB, wave);
   BlockFrags f;
@@ -459,7 +509,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
   StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
                C::kStages - 1 < KB};
   for (int k = 0; k < KB; ++k) {
-    mma_steps<C, kPow2>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
+    mma_steps<C, kPow2, kGather>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
     const float s30 = f.scl[(kMfmaPerBlock - 2) % kSubM];
     const float s31 = f.scl[(kMfmaPerBlock - 1) % kSubM];
     if (k + 1 < KB) {
@@ -489,6 +539,19 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
       if (f.bad & ((1u << mi) | 16u))
 #pragma unroll
         for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
+  }
+  if constexpr (kGather) {
+    // A routed row whose token index is outside [0, T) read zeros; its output
+    // is zero in both scale modes (the power-of-two check above sees its zero
+    // scale and would have made it NaN).
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) {
+      const int r = wm * 64 + mi * 16 + (lane & 15);
+      const int64_t s = r < t.m_valid ? (int64_t)t.gidx[r] : 0;
+      if (!(s >= 0 && s < t.T))
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   if constexpr (kOut == kOutBf16) {
@@ -585,6 +648,8 @@ struct GemmParams {
   uint16_t *y;             // bf16 output
   uint8_t *yq;             // E4M3 output (quantized epilogue)
   float *ys;               // its 1x128 scales
+  const int32_t *gather;   // grouped with gathered token rows: [M] source rows; else null
+  int64_t T;               // rows of the gathered token matrix
   int64_t M;  // dense: M; grouped: M_total
   int64_t N, K;
   int64_t slots_m;
@@ -631,7 +696,7 @@ __device__ __forceinline__ int32_t group_of(const GemmParams &p, int64_t tm) {
 // with S_g = floor(off[g] / kBM) + g, which always holds ceil(rows_g / kBM)
 // tiles; a slot beyond its group's rows exits at once.  No prefix sums or
 // workspace are needed and the offsets never leave the device.
-template <class C, bool kGrouped, bool kPow2, int kOut>
+template <class C, bool kGrouped, bool kPow2, int kOut, bool kGather>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -661,8 +726,17 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   TileJob t;
   t.KB = (int)(p.K / kBK);
   t.K = p.K;
-  t.a_q = p.a_q + m0 * p.K;
-  t.a_s = p.a_s + m0 * t.KB;
+  if constexpr (kGather) {  // rows m0.. of the group are token rows gather[m0..]
+    t.a_q = p.a_q;
+    t.a_s = p.a_s;
+    t.gidx = p.gather + m0;
+    t.T = p.T;
+  } else {
+    t.a_q = p.a_q + m0 * p.K;
+    t.a_s = p.a_s + m0 * t.KB;
+    t.gidx = nullptr;
+    t.T = 0;
+  }
   t.b_q = bq + n0 * p.K;
   t.b_s = bs + (n0 >> 7) * t.KB;
   t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
@@ -674,20 +748,20 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     o.yq = p.yq + m0 * p.N + n0;
     o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
   }
-  gemm_tile<C, kPow2, kOut>(t, o, p.N, lds);
+  gemm_tile<C, kPow2, kOut, kGather>(t, o, p.N, lds);
 }
 
-template <class C, bool kGrouped, bool kPow2, int kOut = kOutBf16>
+template <class C, bool kGrouped, bool kPow2, int kOut = kOutBf16, bool kGather = false>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2, kOut>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2, kOut, kGather>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t grid = p.slots_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2, kOut>), dim3((unsigned)grid), dim3(C::kThreads),
+  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2, kOut, kGather>), dim3((unsigned)grid), dim3(C::kThreads),
                      C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
@@ -698,7 +772,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
                         hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, M, N, K, 0, 1, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n};
   // Large tiles when they still give at least one tile per CU.
   const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
   if (large_tiles >= 256) {
@@ -709,21 +783,21 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   return launch<CfgSmall, false, kPow2, kOut>(p, stream);
 }
 
-template <bool kPow2>
+template <bool kPow2, bool kGather = false>
 static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                           const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N, int64_t K,
-                          uint16_t *y, hipStream_t stream) {
+                          uint16_t *y, const int32_t *gather, int64_t T, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, M_total, N, K, 0, G, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n};
   // 256-row tiles once the average group fills one; their ragged last tile
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
     p.slots_m = M_total / CfgLarge::kBM + G;
-    return launch<CfgLarge, true, kPow2>(p, stream);
+    return launch<CfgLarge, true, kPow2, kOutBf16, kGather>(p, stream);
   }
   p.slots_m = M_total / CfgSmall::kBM + G;
-  return launch<CfgSmall, true, kPow2>(p, stream);
+  return launch<CfgSmall, true, kPow2, kOutBf16, kGather>(p, stream);
 }
 
 hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
@@ -747,8 +821,17 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const int32_t *group_offsets, int32_t G,
                                int64_t M_total, int64_t N, int64_t K,
                                uint16_t *y, bool pow2, hipStream_t stream) {
-  return pow2 ? grouped<true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, stream)
-              : grouped<false>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, stream);
+  return pow2 ? grouped<true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, nullptr, 0, stream)
+              : grouped<false>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, nullptr, 0, stream);
+}
+
+hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T,
+                                      const uint8_t *b_q, const float *b_s,
+                                      const int32_t *group_offsets, const int32_t *row_index, int32_t G,
+                                      int64_t M_total, int64_t N, int64_t K, uint16_t *y, bool pow2,
+                                      hipStream_t stream) {
+  return pow2 ? grouped<true, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, row_index, T, stream)
+              : grouped<false, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, row_index, T, stream);
 }
 
 }  // namespace fp8q

@@ -183,6 +183,34 @@ fp8q_status fp8_grouped_gemm_pow2(const uint8_t *a_q, const float *a_s,
                                   int64_t M_total, int64_t N, int64_t K,
                                   uint16_t *y, void *stream);
 
+/*
+ * Grouped GEMM of a mixture-of-experts layer whose activations were quantized
+ * before dispatch (page 1, "Leistungsgewinne in der Praxis": the recipe's MoE
+ * models; quantizing each token once, ahead of routing, means the FP8 bytes,
+ * half the size of bf16, are what gets dispatched).  Routed row r of group g
+ * (group_offsets[g] <= r < group_offsets[g+1]) is token row row_index[r] of
+ * the quantized token matrix, read directly by the GEMM's loads; no gathered
+ * copy of the activations is made:
+ *   y[r][n] = sum_kb a_s[i][kb] * b_s[g][n/128][kb] *
+ *             sum_{k in block kb} dec(a_q[i][k]) * dec(b_q[g][n][k]),  i = row_index[r]
+ *   a_q [T][K] E4M3, a_s [T][K/128] fp32  (fp8_quant_act_1x128 of the T tokens)
+ *   b_q, b_s, group_offsets, G, M_total, N, K, y as for fp8_grouped_gemm
+ *   row_index [M_total] int32, DEVICE memory.  A row whose index lies outside
+ *             [0, T) is written as zeros (no memory outside a_q/a_s is read).
+ *   mode  FP8Q_SCALE_AMAX: any finite scales (the arithmetic of
+ *         fp8_grouped_gemm); FP8Q_SCALE_POW2: power-of-two scales (that of
+ *         fp8_grouped_gemm_pow2, with its NaN rule for other scale values).
+ * The result equals fp8_grouped_gemm(_pow2) on the gathered rows a_q[row_index],
+ * a_s[row_index] bit for bit.  Requires T*K < 2^31 (byte offsets into a_q are
+ * 32-bit); larger token matrices return FP8Q_ESHAPE.  T = 0 with routed rows
+ * (M_total > 0, N > 0) returns FP8Q_EINVAL.
+ */
+fp8q_status fp8_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T,
+                                    const uint8_t *b_q, const float *b_s,
+                                    const int32_t *group_offsets, const int32_t *row_index,
+                                    int32_t G, int64_t M_total, int64_t N, int64_t K,
+                                    uint16_t *y, int mode, void *stream);
+
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -17,7 +17,7 @@ __all__ = [
     "TINY", "LLAMA_TOKENS", "LLAMA_LAYERS", "LLAMA_NUM_LAYERS", "QWEN3", "MOONLIGHT",
     "MoEShape", "seed_of", "normal_bf16", "bf16_bits", "outlier_channels",
     "tiny_inputs", "llama_layer_inputs", "llama_weight", "moe_routing",
-    "moe_group_offsets", "moe_inputs",
+    "moe_group_offsets", "moe_inputs", "moe_dispatch_inputs",
 ]
 
 # Tiny linear layer: X 256x512 ~ N(0,1), W 256x512 ~ N(0, 0.02).
@@ -178,3 +178,20 @@ def moe_inputs(shape: MoEShape, layer, device="cpu"):
         x = normal_bf16((shape.rows, K), 1.0, seed_of(wid, li, 0), device, outlier_frac=outl)
     w = normal_bf16((shape.groups, N, K), 0.02, seed_of(wid, li, 1), device)
     return x.contiguous(), w, offsets
+
+
+def moe_dispatch_inputs(shape: MoEShape, device="cpu"):
+    """The expert gate_up layer before dispatch: the token matrix and the
+    routed row -> token map instead of the gathered rows.
+
+    Returns (XT bf16 [tokens, hidden], row_token int64 [rows], W bf16
+    [G, N, K], offsets int32 [G+1]); XT[row_token] is exactly the X that
+    moe_inputs(shape, "gate_up") returns, and W and offsets are its own.
+    """
+    wid = 4 if shape.zipf_alpha > 0 else 5
+    offsets, row_token = moe_group_offsets(shape, moe_routing(shape))
+    outl = 0.01 if shape.zipf_alpha == 0 else 0.0
+    _, N, K = shape.layers()[0]
+    xt = normal_bf16((shape.tokens, K), 1.0, seed_of(wid, 0, 0), device, outlier_frac=outl)
+    w = normal_bf16((shape.groups, N, K), 0.02, seed_of(wid, 0, 1), device)
+    return xt, row_token, w, offsets

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-              "fp8_blockscaled_gemm_quant",
+              "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
               "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
@@ -107,6 +107,24 @@ def test_grouped_argument_errors(lib, fn):
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, None) == 3
     assert f(None, None, None, None, None, 3, 0, 128, 128, None, None) == 0
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, (1 << 22) + 128, GOOD, None) == 2
+
+
+def test_gather_argument_errors(lib):
+    f = lib.fp8_grouped_gemm_gather
+    #      a_q   a_s   T    b_q   b_s   off   idx   G  M   N    K    y     mode
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 128, GOOD, 5, None) == 1    # unknown mode
+    assert "mode" in _err(lib)
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, GOOD, 0, 64, 128, 128, GOOD, 0, None) == 1    # G < 1
+    assert f(GOOD, GOOD, -1, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 128, GOOD, 0, None) == 1    # T < 0
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 100, GOOD, 0, None) == 2    # K % 128
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, GOOD, 2, 64, 100, 128, GOOD, 1, None) == 2    # N % 128
+    assert f(GOOD, GOOD, 1 << 24, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 128, GOOD, 0, None) == 2   # T*K = 2^31
+    assert "2^31" in _err(lib)
+    assert f(GOOD, GOOD, (1 << 24) - 1, GOOD, GOOD, GOOD, None, 2, 64, 128, 128, GOOD, 0, None) == 1  # null idx
+    assert f(GOOD, GOOD, 0, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, 128, GOOD, 0, None) == 1     # no tokens
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, 0, None) == 3     # misaligned idx
+    assert f(None, None, 0, None, None, None, None, 3, 0, 128, 128, None, 0, None) == 0      # empty call
+    assert f(GOOD, GOOD, 10, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, (1 << 22) + 128, GOOD, 0, None) == 2
 
 
 def test_valid_call_without_gpu_reports_device_error(lib):
