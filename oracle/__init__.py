@@ -19,5 +19,11 @@ from .oracle import (  # noqa: F401
     gemm_sampled_f64,
     grouped_gemm_f64,
     grouped_gemm_sampled_f64,
+    quant_act_colwise_t,
+    quant_weight_128x128_t,
+    gemm_dgrad_f64,
+    gemm_dgrad_sampled_f64,
+    gemm_wgrad_f64,
+    gemm_wgrad_sampled_f64,
     num_threads,
 )

@@ -204,3 +204,88 @@ def grouped_gemm_sampled_f64(aq, as_, bq, bs, groups, ms, ns):
     _load().oracle_grouped_gemm_sampled_f64(_ptr(aq), _ptr(as_), _ptr(bq), _ptr(bs), N, K,
                                             _ptr(grp), _ptr(ms), _ptr(ns), ms.size, _ptr(y))
     return y
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the linear layer Y = X W^T.  Page 1 trains end to end in FP8
+# ("Der technische Durchbruch": FP8 applied in generation and in training
+# alike) with E4M3 blocks of 1x128 for activations and 128x128 for weights,
+# and prints no other layout for the gradient GEMMs.  The reading taken here
+# puts every scale block along the contraction dimension of its GEMM, as in
+# the forward pass, so one scale pair factors out of each 128-long partial
+# sum:
+#   dX = dY W    dY in 1x128 blocks along N (its rows); W in its 128x128 tiles.
+#   dW = dY^T X  dY and X in blocks of 128 tokens x 1 channel (128x1, along M),
+#                stored transposed ([channels][Mp]) so that the contraction
+#                runs along rows; Mp = M rounded up to a multiple of 128, the
+#                padding holding zero codes.
+# ---------------------------------------------------------------------------
+
+def quant_act_colwise_t(x_bits, mode=MODE_AMAX):
+    """Blocks of 128 rows x 1 column of x [M, K] (bf16 bits), stored transposed.
+
+    Column k, rows 128*mb .. 128*mb+127 form one block, quantized by the same
+    rule as a 1x128 activation block; rows past M count as +0.  Written out:
+    the block is row k, block mb of the zero-padded transpose of x.
+    Returns (q_t uint8 [K, Mp], s_t f32 [K, Mp/128]).
+    """
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    Mp = -(-M // 128) * 128
+    xt = np.zeros((K, Mp), dtype=np.uint16)
+    xt[:, :M] = x.T
+    return quant_act_1x128(xt, mode)
+
+
+def quant_weight_128x128_t(w_bits, mode=MODE_AMAX):
+    """The 128x128-tile quantization of w [N, K] in the transposed layout the
+    data-gradient GEMM reads: (q_t uint8 [K, N], s_t f32 [K/128, N/128]) with
+    q_t = q^T and s_t = s^T (a tile and its transpose hold the same values)."""
+    q, s = quant_weight_128x128(w_bits, mode)
+    return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
+
+
+def gemm_dgrad_f64(gq, gs, wq, ws):
+    """dX [M, K] (fp64) = dequant(gq, gs) @ dequant(wq, ws).
+
+    gq [M, N] with scales gs [M, N/128] (1x128 along N); wq [N, K] with scales
+    ws [N/128, K/128] (the forward weight tiles).  Written as the block-scaled
+    GEMM with the weight operand transposed: operand row k of W^T is column k
+    of W, and tile (kb, nb) of W^T has the scale of tile (nb, kb) of W.
+    """
+    return gemm_f64(gq, gs, np.ascontiguousarray(_c(wq, np.uint8).T),
+                    np.ascontiguousarray(_c(ws, np.float32).T))
+
+
+def gemm_dgrad_sampled_f64(gq, gs, wq, ws, ms, ks):
+    """dX[ms[i], ks[i]] of gemm_dgrad_f64, for outputs chosen one by one."""
+    return gemm_sampled_f64(gq, gs, np.ascontiguousarray(_c(wq, np.uint8).T),
+                            np.ascontiguousarray(_c(ws, np.float32).T), ms, ks)
+
+
+def _dequant_rows(q, s):
+    """fp64 values of codes q [R, C] with one scale per 1x128 block of a row,
+    s [R, C/128] (exact: 4-bit times 24-bit significands)."""
+    table = e4m3_decode_table()
+    return table[_c(q, np.uint8)] * np.repeat(_c(s, np.float32).astype(np.float64), 128, axis=1)
+
+
+def gemm_wgrad_f64(gtq, gts, xtq, xts):
+    """dW [N, K] (fp64) = dequant(gtq, gts) @ dequant(xtq, xts)^T.
+
+    gtq [N, Mp], gts [N, Mp/128]: dY^T in 128-token blocks; xtq [K, Mp],
+    xts [K, Mp/128]: X^T in 128-token blocks.  Every operand row has its own
+    scale per block, on both sides:
+        dW[n][k] = sum_mb gts[n][mb] * xts[k][mb] * sum_{m in mb} dec(gtq[n][m]) * dec(xtq[k][m]).
+    Dequantization is exact in fp64; numpy's float64 matmul does the sums.
+    """
+    return _dequant_rows(gtq, gts) @ _dequant_rows(xtq, xts).T
+
+
+def gemm_wgrad_sampled_f64(gtq, gts, xtq, xts, ns, ks):
+    """dW[ns[i], ks[i]] of gemm_wgrad_f64, for outputs chosen one by one."""
+    ns = np.asarray(ns, dtype=np.int64)
+    ks = np.asarray(ks, dtype=np.int64)
+    a = _dequant_rows(_c(gtq, np.uint8)[ns], _c(gts, np.float32)[ns])
+    b = _dequant_rows(_c(xtq, np.uint8)[ks], _c(xts, np.float32)[ks])
+    return np.einsum("ij,ij->i", a, b)
