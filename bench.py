@@ -117,9 +117,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,recal,moe,dispatch,bf16,cpu",
+    ap.add_argument("--sections", default="pow2,fused,backward,recal,moe,dispatch,bf16,cpu",
                     help="extra measurements after the step "
-                         "(comma list of pow2, fused, recal, moe, dispatch, bf16, cpu)")
+                         "(comma list of pow2, fused, backward, recal, moe, dispatch, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -290,6 +290,8 @@ def main():
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
     if "moe" in sections:
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
+    if "backward" in sections:
+        result["backward"] = backward(fp8q, synth, layers, torch, dev, M, reps)
     if "dispatch" in sections:
         result["moe_dispatch"] = dispatch(fp8q, synth, torch, dev, reps)
     if "bf16" in sections:
@@ -425,6 +427,70 @@ def moe(fp8q, synth, torch, dev, reps):
             log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}")
             del x, bq, bs, aq, as_, y
             torch.cuda.empty_cache()
+    return out
+
+
+def backward(fp8q, synth, layers, torch, dev, M, reps):
+    """Backward pass of the four Llama-shaped layers at 4096 tokens (training
+    end to end in FP8): per layer, dY [M, N] ~ N(0, 1e-3) quantized in both
+    layouts in one pass, X in 128-token column blocks (its row blocks are the
+    forward pass's), W's tiles in both layouts, then the data gradient
+    dX = dY W (dense GEMM on W's transposed tiles) and the weight gradient
+    dW = dY^T X (1x128 blocks on both operands)."""
+    out, tot = {}, {"dgrad_s": 0.0, "wgrad_s": 0.0, "quant_s": 0.0, "flops": 0.0}
+    for i, l in enumerate(layers):
+        N, K = l["N"], l["K"]
+        Mp = (M + 127) // 128 * 128
+        g = synth.normal_bf16((M, N), 1e-3, synth.seed_of(16, i, 2), device=dev)
+        gq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        gs = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        gtq = torch.empty((N, Mp), dtype=torch.uint8, device=dev)
+        gts = torch.empty((N, Mp // 128), dtype=torch.float32, device=dev)
+        xtq = torch.empty((K, Mp), dtype=torch.uint8, device=dev)
+        xts = torch.empty((K, Mp // 128), dtype=torch.float32, device=dev)
+        wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+        wtq = torch.empty((K, N), dtype=torch.uint8, device=dev)
+        wts = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        qg = lambda: fp8q.fp8_quant_act_dual(g, out=(gq, gs, gtq, gts))
+        qx = lambda: fp8q.fp8_quant_act_dual(l["x"], out=(None, None, xtq, xts))
+        qw = lambda: fp8q.fp8_quant_weight_128x128_dual(l["w"], out=(wq, ws, wtq, wts))
+        dg = lambda: fp8q.fp8_blockscaled_gemm(gq, gs, wtq, wts, out=dx)
+        wg = lambda: fp8q.fp8_blockscaled_gemm_wgrad(gtq, gts, xtq, xts, out=dw)
+        for f in (qg, qx, qw, dg, wg):
+            f()
+        t_qg, t_qx, t_qw = (time_loop(f, reps, torch) for f in (qg, qx, qw))
+        t_dg, t_wg = time_loop(dg, reps, torch), time_loop(wg, reps, torch)
+        f_dg, f_wg = 2.0 * M * N * K, 2.0 * N * K * Mp
+        b_qg = M * N * 4 + 2 * M * (N // 128) * 4         # bf16 in, two code layouts, two scale sets
+        b_qx = M * K * 3 + K * (Mp // 128) * 4
+        b_qw = N * K * 4 + 2 * (N // 128) * (K // 128) * 4
+        out[l["name"]] = {
+            "dgrad_tflops": round(f_dg / t_dg / 1e12, 1), "wgrad_tflops": round(f_wg / t_wg / 1e12, 1),
+            "dgrad_us": round(t_dg * 1e6, 2), "wgrad_us": round(t_wg * 1e6, 2),
+            "quant_dy_dual_gbs": round(b_qg / t_qg / 1e9, 1), "quant_x_colwise_gbs": round(b_qx / t_qx / 1e9, 1),
+            "quant_w_dual_gbs": round(b_qw / t_qw / 1e9, 1),
+            "quant_dy_us": round(t_qg * 1e6, 2), "quant_x_us": round(t_qx * 1e6, 2),
+            "quant_w_us": round(t_qw * 1e6, 2)}
+        log(f"backward {l['name']}: dgrad {f_dg / t_dg / 1e12:.1f} TFLOP/s, wgrad {f_wg / t_wg / 1e12:.1f} "
+            f"TFLOP/s, dY dual {b_qg / t_qg / 1e9:.0f} GB/s, X colwise {b_qx / t_qx / 1e9:.0f} GB/s, "
+            f"W dual {b_qw / t_qw / 1e9:.0f} GB/s")
+        tot["dgrad_s"] += t_dg
+        tot["wgrad_s"] += t_wg
+        tot["quant_s"] += t_qg + t_qx
+        tot["flops"] += f_dg + f_wg
+        del g, gq, gs, gtq, gts, xtq, xts, wq, ws, wtq, wts, dx, dw
+        torch.cuda.empty_cache()
+    step_s = tot["dgrad_s"] + tot["wgrad_s"] + tot["quant_s"]
+    out["total"] = {
+        "backward_step_ms": round(step_s * 1e3, 3),
+        "backward_step_tflops": round(tot["flops"] / step_s / 1e12, 1),
+        "dgrad_wgrad_tflops": round(tot["flops"] / (tot["dgrad_s"] + tot["wgrad_s"]) / 1e12, 1),
+        "note": "step = quantize dY (both layouts) + X (column blocks) + dgrad + wgrad per layer; "
+                "W's transposed tiles are made once per weight update (quant_w_dual)"}
+    log(f"backward step {step_s * 1e3:.3f} ms, {tot['flops'] / step_s / 1e12:.1f} TFLOP/s")
     return out
 
 

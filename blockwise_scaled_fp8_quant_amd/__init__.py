@@ -25,8 +25,9 @@ _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
-           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "abi_version",
-           "library_path"]
+           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
+           "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
+           "abi_version", "library_path"]
 
 
 def library_path():
@@ -224,4 +225,72 @@ def fp8_grouped_gemm_gather(a_q, a_s, b_q, b_s, group_offsets, row_index, mode="
     _lib.check("fp8_grouped_gemm_gather",
                _lib.load().fp8_grouped_gemm_gather(pa, pas, T, pb, pbs, poff, pidx, G, M, N, K, py,
                                                    _mode(mode), _stream(a_q)))
+    return y
+
+
+def _dual(fn, x, rows_mult, mode, rowwise, out):
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if rows_mult and M % 128:
+        raise ValueError("N must be a multiple of 128")
+    Mp = (M + 127) // 128 * 128
+    tile = fn == "fp8_quant_weight_128x128_dual"
+    s_shape = (M // 128, K // 128) if tile else (M, K // 128)
+    st_shape = (K // 128, Mp // 128) if tile else (K, Mp // 128)
+    if out is None:
+        dev = x.device
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev) if rowwise else None
+        s = torch.empty(s_shape, dtype=torch.float32, device=dev) if rowwise else None
+        qt = torch.empty((K, Mp), dtype=torch.uint8, device=dev)
+        st = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    else:
+        q, s, qt, st = out
+    pq = ps = None
+    if q is not None:
+        q, pq = _as_bytes(q, "q", 2)
+        ps = _dev(s, "scales", torch.float32, 2)
+        if tuple(q.shape) != (M, K) or tuple(s.shape) != s_shape:
+            raise ValueError("row-major output shapes do not match the input")
+    qt, pqt = _as_bytes(qt, "q_t", 2)
+    pst = _dev(st, "scales_t", torch.float32, 2)
+    if tuple(qt.shape) != (K, Mp) or tuple(st.shape) != st_shape:
+        raise ValueError("transposed output shapes do not match the input")
+    _lib.check(fn, getattr(_lib.load(), fn)(px, M, K, pq, ps, pqt, pst, _mode(mode), _stream(x)))
+    return q, s, qt, st
+
+
+def fp8_quant_act_dual(x, mode="amax", rowwise=True, out=None):
+    """x bf16 [M, K] -> (q [M, K], s [M, K/128], q_t [K, Mp], s_t [K, Mp/128]).
+
+    q, s: the 1x128 row blocks (as fp8_quant_act_1x128; None with
+    rowwise=False).  q_t, s_t: blocks of 128 rows x 1 column, transposed, for
+    the weight-gradient GEMM; Mp = M rounded up to 128, padding codes 0.
+    """
+    return _dual("fp8_quant_act_dual", x, False, mode, rowwise, out)
+
+
+def fp8_quant_weight_128x128_dual(w, mode="amax", rowwise=True, out=None):
+    """w bf16 [N, K] -> (q [N, K], s [N/128, K/128], q_t [K, N], s_t [K/128, N/128]):
+    the 128x128-tile quantization and its transpose (for the data gradient)."""
+    return _dual("fp8_quant_weight_128x128_dual", w, True, mode, rowwise, out)
+
+
+def fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out=None):
+    """Y [M, N] bf16 = dequant(a_q, a_s) @ dequant(b_q, b_s)^T with 1x128 scale
+    blocks on both operands: a_s [M, K/128], b_s [N, K/128].  The weight
+    gradient dW = dY^T X from the transposed outputs of fp8_quant_act_dual."""
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 2)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 2)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K or tuple(a_s.shape) != (M, K // 128) or tuple(b_s.shape) != (N, K // 128):
+        raise ValueError("operand shapes do not match")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
+    py = _dev(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_blockscaled_gemm_wgrad",
+               _lib.load().fp8_blockscaled_gemm_wgrad(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
     return y

@@ -91,6 +91,43 @@ fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, ui
                   __func__);
 }
 
+fp8q_status fp8_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *scales,
+                               uint8_t *q_t, float *scales_t, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(M >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  FP8Q_REQUIRE((q == nullptr) == (scales == nullptr), FP8Q_EINVAL,
+               "q and scales must both be given or both be null");
+  if (M == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(x && q_t && scales_t, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(x) && aligned16(q) && aligned16(scales) && aligned16(q_t) && aligned16(scales_t),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(
+      fp8q::launch_quant_dual(x, M, K, q, scales, q_t, scales_t, mode, false, (hipStream_t)stream), __func__);
+}
+
+fp8q_status fp8_quant_weight_128x128_dual(const uint16_t *w, int64_t N, int64_t K, uint8_t *q, float *scales,
+                                          uint8_t *q_t, float *scales_t, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(N >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  FP8Q_REQUIRE(N % 128 == 0, FP8Q_ESHAPE, "N must be a multiple of 128");
+  FP8Q_REQUIRE((q == nullptr) == (scales == nullptr), FP8Q_EINVAL,
+               "q and scales must both be given or both be null");
+  if (N == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(w && q_t && scales_t, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(w) && aligned16(q) && aligned16(scales) && aligned16(q_t) && aligned16(scales_t),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(
+      fp8q::launch_quant_dual(w, N, K, q, scales, q_t, scales_t, mode, true, (hipStream_t)stream), __func__);
+}
+
 }  // extern "C"
 
 namespace {
@@ -131,6 +168,23 @@ fp8q_status gemm_quant_entry(const char *fn, const uint8_t *a_q, const float *a_
   if (st != FP8Q_OK) return st;
   return launched(
       fp8q::launch_blockscaled_gemm_quant(a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, (hipStream_t)stream), fn);
+}
+
+fp8q_status wgrad_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                        const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K, void *stream) {
+  g_last_error.clear();
+  if (!(M >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (N % 128 != 0) return fail(FP8Q_ESHAPE, fn, "N must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31)) return fail(FP8Q_EINVAL, fn, "M or N too large");
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (!(a_q && a_s && b_q && b_s && y)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(y)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, y, M, N, K, (hipStream_t)stream), fn);
 }
 
 fp8q_status grouped_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
@@ -204,6 +258,12 @@ fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s, con
                                        const float *b_s, uint8_t *y_q, float *y_s, int64_t M, int64_t N,
                                        int64_t K, int mode, void *stream) {
   return gemm_quant_entry(__func__, a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, stream);
+}
+
+fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                       const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                       void *stream) {
+  return wgrad_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, stream);
 }
 
 fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,

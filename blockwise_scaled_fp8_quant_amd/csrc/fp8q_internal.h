@@ -35,6 +35,21 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                int64_t M_total, int64_t N, int64_t K,
                                uint16_t *y, bool pow2, hipStream_t stream);
 
+// GEMM with 1x128 scale blocks on both operands: a_s [M][K/128] and one
+// scale per row and 128-block of K for b as well, b_s [N][K/128] (the weight
+// gradient from 128-token column blocks of dY and X).
+hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
+                                         const uint8_t *b_q, const float *b_s,
+                                         uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                         hipStream_t stream);
+
+// Row-major and transposed codes of x [M][K] in one pass.  tile: one scale per
+// 128x128 tile (weights; M % 128 == 0), q_t [K][M], s_t [K/128][M/128].
+// Otherwise 1x128 row blocks (q, s; may be null) and 128x1 column blocks
+// stored transposed, q_t [K][Mp], s_t [K][Mp/128], Mp = M rounded up to 128.
+hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
+                             float *st, int mode, bool tile, hipStream_t stream);
+
 // Grouped GEMM whose token rows are gathered: routed row r reads token row
 // row_index[r] of a_q [T][K] / a_s [T][K/128] (quantize before dispatch).
 hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T,

@@ -48,6 +48,28 @@ constexpr int kSubM = 4;  // 16-col MFMA sub-tiles per wave along m (64 rows)
 constexpr int kNumXcd = 8;
 constexpr int kGroupN = 4;  // weight panels per rasterization group
 
+// Output of a tile: bf16 Y, or Y quantized to E4M3 in 1x128 blocks along N
+// with the activation quantizer's rule (kOut = its scale mode).
+constexpr int kOutBf16 = -1;
+
+// What a kernel instance computes:
+//   kGrouped  groups of rows, each with its own weight matrix (device offsets)
+//   kPow2     power-of-two scales, applied by the matrix cores (E8M0)
+//   kOut      bf16 output, or the output quantized in the epilogue
+//   kGather   grouped rows read by index from a token matrix
+//   kBRow     the weight-side operand carries one scale per row and 128-block
+//             of K (1x128 blocks on both operands) instead of 128x128 tiles
+template <bool kGrouped_, bool kPow2_, int kOut_ = kOutBf16, bool kGather_ = false, bool kBRow_ = false>
+struct Variant {
+  static constexpr bool kGrouped = kGrouped_;
+  static constexpr bool kPow2 = kPow2_;
+  static constexpr int kOut = kOut_;
+  static constexpr bool kGather = kGather_;
+  static constexpr bool kBRow = kBRow_;
+  static_assert(!(kGather && !kGrouped), "gathered rows belong to groups");
+  static_assert(!(kBRow && (kPow2 || kGrouped)), "per-row weight-side scales: dense, VALU fold");
+};
+
 template <int kBM_, int kWaves_, int kStages_, int kLoaders_>
 struct TileCfg {
   static constexpr int kBM = kBM_;
@@ -62,7 +84,7 @@ struct TileCfg {
   static constexpr int kBytesB = kBN * kBK;        // weight tile
   static constexpr int kBytesA = kBM * kBK;        // token tile
   static constexpr int kBytesSA = kBM * 4;         // activation scales
-  static constexpr int kBytesSB = 8;               // weight scales of the tile's two 128-row blocks
+  static constexpr int kBytesSB = kBN * 4;         // weight-side scales: per 128-row block or per row
   static constexpr int kOffA = kBytesB;
   static constexpr int kOffSA = kOffA + kBytesA;
   static constexpr int kOffSB = kOffSA + kBytesSA;
@@ -116,14 +138,15 @@ struct TileRsrc {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) 32-bit buffer access
 
-template <bool kGather = false>
+template <class V>
 __device__ __forceinline__ TileRsrc make_rsrc(const TileJob &t) {
+  constexpr bool kGather = V::kGather;
   TileRsrc r;
   // gathered: bounded to the whole scale matrix (the lanes' offsets select rows)
   r.sa = __builtin_amdgcn_make_buffer_rsrc((void *)t.a_s, (short)0,
                                            kGather ? (int)(t.T * t.KB * 4) : t.m_valid * t.KB * 4, kRsrcWord3);
-  r.sb = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_s, (short)0, ((t.n_valid + 127) >> 7) * t.KB * 4,
-                                           kRsrcWord3);
+  r.sb = __builtin_amdgcn_make_buffer_rsrc((void *)t.b_s, (short)0,
+                                           (V::kBRow ? t.n_valid : (t.n_valid + 127) >> 7) * t.KB * 4, kRsrcWord3);
   return r;
 }
 
@@ -171,7 +194,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gather_rsrc(const uint8_t *a, 
 struct DmaLane {
   uint32_t rc[2];  // (row in piece)*K + chunk offset, even / odd pieces
   uint32_t sa;     // activation-scale row of this lane (lanes 0..31)
-  uint32_t sb;     // weight-scale row (lanes 0..1)
+  uint32_t sb;     // weight-scale row (lanes 0..1; per-row scales: row lane of each 64)
   // Gathered token rows: this lane's byte offset in the token matrix for each
   // of its loader's token pieces, and of its scale row; kGatherOOB for a row
   // past the tile or an index outside [0, T), which then reads zeros.
@@ -179,8 +202,9 @@ struct DmaLane {
   uint32_t gsa;
 };
 
-template <class C, bool kGather = false>
+template <class C, class V>
 __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane) {
+  constexpr bool kGather = V::kGather;
   DmaLane d;
   const uint32_t row = (uint32_t)(lane >> 3);
   const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 3));
@@ -189,7 +213,7 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
   for (int par = 0; par < 2; ++par) d.rc[par] = row * K + ((c0 ^ par) << 4);
   const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
   d.sa = (uint32_t)sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane) * (uint32_t)t.KB * 4u;
-  d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
+  d.sb = (uint32_t)(V::kBRow ? lane : (lane & 1)) * (uint32_t)t.KB * 4u;
   if constexpr (kGather) {
     static_assert(C::kPiecesA <= kMaxPiecesA, "gather offsets per lane");
     auto src = [&](int r) -> int64_t {  // source token row of tile row r, or -1
@@ -215,9 +239,10 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
 // load on the first.  Each load is one vector-memory instruction; a CU's
 // vector-memory path takes about one such 1 KB load every 20 clocks, so the
 // count per stage is kept at the minimum the bytes need.
-template <class C, bool kGather>
+template <class C, class V>
 __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, int k, uint8_t *buf, int wave,
                                             int q) {
+  constexpr bool kGather = V::kGather;
   const uint32_t kbyte = (uint32_t)k * kBK;
   const int l = wave - C::kFirstLoader;  // loader index
   if (q < C::kPiecesB) {
@@ -238,29 +263,48 @@ __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, 
 }
 
 // Number of vector-memory instructions a wave issues for one stage.
-template <class C>
-__host__ __device__ constexpr int loads_per_stage(int l) {
-  return C::kPieces + (l < C::kScaleLoaders ? 1 : 0) + (l == 0 ? 1 : 0);
+// Weight-side scale loads of loader l: with tile scales one 2-lane load on
+// the first loader; with per-row scales kBN/64 loads of 64 rows, load j on
+// loader (kScaleLoaders + j) % kLoaders.
+template <class C, class V>
+__host__ __device__ constexpr int sb_loads(int l) {
+  if (!V::kBRow) return l == 0 ? 1 : 0;
+  int n = 0;
+  for (int j = 0; j < kBN / 64; ++j) n += ((C::kScaleLoaders + j) % C::kLoaders == l) ? 1 : 0;
+  return n;
 }
 
-template <class C, bool kGather>
+template <class C, class V>
+__host__ __device__ constexpr int loads_per_stage(int l) {
+  return C::kPieces + (l < C::kScaleLoaders ? 1 : 0) + sb_loads<C, V>(l);
+}
+
+template <class C, class V>
 __device__ __forceinline__ void issue_scales(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
                                              uint8_t *buf, int wave, int lane) {
   const int l = wave - C::kFirstLoader;
   if (l < C::kScaleLoaders)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
-                                             (kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
-  if (l == 0 && lane < 2)
+                                             (V::kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
+  if constexpr (V::kBRow) {
+    // rows 64j .. 64j+63 of the weight-side scales, in row order
+#pragma unroll
+    for (int j = 0; j < kBN / 64; ++j)
+      if ((C::kScaleLoaders + j) % C::kLoaders == l)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + j * 256), 4,
+                                                 d.sb + (uint32_t)(j * 64 * t.KB * 4) + (uint32_t)k * 4u, 0, 0,
+                                                 0);
+  } else if (l == 0 && lane < 2)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
                                              0, 0, 0);
 }
 
-template <class C, bool kGather>
+template <class C, class V>
 __device__ __forceinline__ void issue_stage(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
                                             uint8_t *buf, int wave, int lane) {
-  issue_scales<C, kGather>(t, rs, d, k, buf, wave, lane);
+  issue_scales<C, V>(t, rs, d, k, buf, wave, lane);
 #pragma unroll
-  for (int q = 0; q < C::kPieces; ++q) issue_piece<C, kGather>(t, d, k, buf, wave, q);
+  for (int q = 0; q < C::kPieces; ++q) issue_piece<C, V>(t, d, k, buf, wave, q);
 }
 
 // The DMA of a stage that the next block issues, right after its first LDS
@@ -322,9 +366,10 @@ __device__ __forceinline__ uint32_t e8m0_of(float s, uint32_t &bad, uint32_t bit
   return e & 0xFFu;
 }
 
-template <class C, bool kPow2>
+template <class C, class V>
 __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
                                            BlockFrags &f) {
+  constexpr bool kPow2 = V::kPow2;
   const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
 #pragma unroll
@@ -335,6 +380,13 @@ __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn,
     f.ea = e8m0_of(sa4.x, f.bad, 1u) | (e8m0_of(sa4.y, f.bad, 2u) << 8) | (e8m0_of(sa4.z, f.bad, 4u) << 16) |
            (e8m0_of(sa4.w, f.bad, 8u) << 24);
     f.eb = e8m0_of(sb, f.bad, 16u);
+  } else if constexpr (V::kBRow) {
+    // the weight-side scale differs between a lane's four outputs: the folds
+    // multiply it in
+    f.scl[0] = sa4.x;
+    f.scl[1] = sa4.y;
+    f.scl[2] = sa4.z;
+    f.scl[3] = sa4.w;
   } else {
     f.scl[0] = sa4.x * sb;
     f.scl[1] = sa4.y * sb;
@@ -378,6 +430,15 @@ __device__ __forceinline__ void fold1(v4f &acc, const v4f &p, float s) {
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], s, acc[r]);
 }
 
+// The fold with per-row weight-side scales: a lane's four outputs are four
+// weight-side rows, each with its own scale sb.
+__device__ __forceinline__ void fold_rows(v4f &acc, const v4f &p, float sa, const float4 &sb) {
+  acc[0] = __builtin_fmaf(p[0], sa * sb.x, acc[0]);
+  acc[1] = __builtin_fmaf(p[1], sa * sb.y, acc[1]);
+  acc[2] = __builtin_fmaf(p[2], sa * sb.z, acc[2]);
+  acc[3] = __builtin_fmaf(p[3], sa * sb.w, acc[3]);
+}
+
 // Keeps a value's computation above this point: without it the compiler may
 // sink the MFMAs and folds of a block past the block-boundary branch, away
 // from the schedule laid out here.
@@ -388,9 +449,15 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 // E8M0 scale operands of each MFMA carry the weight block's and the token
 // row's exponents, and the MFMA accumulates straight into acc -- no partial
 // products and no folds.
-template <class C, bool kPow2, bool kGather>
+//
+// With per-row weight-side scales (kBRow) the four scales of sub-tile row ni
+// are read with its weight fragment (a ring of two rows, as a fold trails its
+// MFMA by two) and each fold multiplies them in.
+template <class C, class V>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
-                                          v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const StageDma &dma) {
+                                          v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], float4 (&sbq)[2],
+                                          const StageDma &dma) {
+  constexpr bool kPow2 = V::kPow2;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int R = kWAhead + 1;
   v8i wf[R];
@@ -403,8 +470,10 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       // the reads of sub-tile ni+kWAhead go out before any MFMA of row ni
       __builtin_amdgcn_sched_barrier(0);
       if (ni + kWAhead < kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * 128 + (ni + kWAhead) * 16, lane);
+      if constexpr (V::kBRow)
+        sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
       if (ni == 0 && dma.on && dma.wave >= C::kFirstLoader)
-        issue_stage<C, kGather>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
+        issue_stage<C, V>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kPow2) {
@@ -416,8 +485,13 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if (j >= 2) {
       const int jj = j - 2;
-      fold1(acc[jj / kSubM][jj % kSubM], p[jj % kRing], f.scl[jj % kSubM]);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      if constexpr (V::kBRow) {
+        fold_rows(acc[jj / kSubM][jj % kSubM], p[jj % kRing], f.scl[jj % kSubM], sbq[(jj / kSubM) & 1]);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+      } else {
+        fold1(acc[jj / kSubM][jj % kSubM], p[jj % kRing], f.scl[jj % kSubM]);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -448,26 +522,38 @@ __device__ __forceinline__ void barrier_nofence() {
 
 // Wait until the DMA of block kk has landed in every wave's view: at most the
 // later blocks already issued (kk+1 .. kk+kStages-2) may still be in flight.
-template <class C>
+// vmcnt wait for loader l (each loader's own count of loads per stage).
+template <class C, class V, int L = 0>
+__device__ __forceinline__ void wait_loader(int l) {
+  constexpr int n = C::kStages - 2;
+  if constexpr (L + 1 < C::kLoaders) {
+    if (l == L)
+      wait_vmcnt<loads_per_stage<C, V>(L) * n>();
+    else
+      wait_loader<C, V, L + 1>(l);
+  } else {
+    wait_vmcnt<loads_per_stage<C, V>(L) * n>();
+  }
+}
+
+template <class C, class V>
 __device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
   constexpr int n = C::kStages - 2;  // stages issued after block kk's
   const int l = wave - C::kFirstLoader;
   if (n > 0 && kk + n < KB && l >= 0) {
-    if (l == 0)
-      wait_vmcnt<loads_per_stage<C>(0) * n>();
+    if constexpr (V::kBRow)
+      wait_loader<C, V>(l);
+    else if (l == 0)
+      wait_vmcnt<loads_per_stage<C, V>(0) * n>();
     else if (l < C::kScaleLoaders)
-      wait_vmcnt<loads_per_stage<C>(1) * n>();
+      wait_vmcnt<loads_per_stage<C, V>(1) * n>();
     else
-      wait_vmcnt<loads_per_stage<C>(C::kScaleLoaders) * n>();
+      wait_vmcnt<loads_per_stage<C, V>(C::kScaleLoaders) * n>();
   } else {
     wait_vmcnt<0>();
   }
   barrier_nofence();
 }
-
-// Output of a tile: bf16 Y, or Y quantized to E4M3 in 1x128 blocks along N
-// with the activation quantizer's rule (kOut = its scale mode).
-constexpr int kOutBf16 = -1;
 
 struct TileOut {
   uint16_t *y;   // bf16: tile origin of Y [M][N]
@@ -477,8 +563,11 @@ struct TileOut {
 
 // One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
 // n_valid), written at the tile origins in o (row stride N).
-template <class C, bool kPow2, int kOut, bool kGather>
+template <class C, class V>
 __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds) {
+  constexpr bool kPow2 = V::kPow2;
+  constexpr int kOut = V::kOut;
+  constexpr bool kGather = V::kGather;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
   const int wn = wave & 1, wm = wave >> 1;
@@ -490,43 +579,49 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-  const TileRsrc rs = make_rsrc<kGather>(t);
-  const DmaLane dl = dma_lane<C, kGather>(t, wave, lane);
+  const TileRsrc rs = make_rsrc<V>(t);
+  const DmaLane dl = dma_lane<C, V>(t, wave, lane);
 
   // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s)
     if (s < KB && wave >= C::kFirstLoader)
-      issue_stage<C, kGather>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
+      issue_stage<C, V>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
 
-  wait_block<C>(0, KB, wave);
+  wait_block<C, V>(0, KB, wave);
   BlockFrags f;
   f.bad = 0;
-  load_block<C, kPow2>(lds, wave, wn, wm, lane, f);
+  load_block<C, V>(lds, wave, wn, wm, lane, f);
 
   v4f p[kRing];
+  float4 sbq[2];  // per-row weight-side scales of two sub-tile rows (kBRow)
   int cur = 0;  // stage buffer of block k
   StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
                C::kStages - 1 < KB};
   for (int k = 0; k < KB; ++k) {
-    mma_steps<C, kPow2, kGather>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, dma);
+    mma_steps<C, V>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma);
     const float s30 = f.scl[(kMfmaPerBlock - 2) % kSubM];
     const float s31 = f.scl[(kMfmaPerBlock - 1) % kSubM];
     if (k + 1 < KB) {
       // Block k's buffer is free once every wave is past this barrier; it
       // receives block k + kStages.
-      wait_block<C>(k + 1, KB, wave);
+      wait_block<C, V>(k + 1, KB, wave);
       // block k + kStages goes into block k's buffer during the next block
       dma.k = k + C::kStages;
       dma.buf = lds + cur * C::kStageBytes;
       dma.on = k + C::kStages < KB;
       cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-      load_block<C, kPow2>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
+      load_block<C, V>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
     }
     if constexpr (!kPow2) {
       constexpr int j30 = kMfmaPerBlock - 2, j31 = kMfmaPerBlock - 1;
-      fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
-      fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
+      if constexpr (V::kBRow) {
+        fold_rows(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30, sbq[(j30 / kSubM) & 1]);
+        fold_rows(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31, sbq[(j31 / kSubM) & 1]);
+      } else {
+        fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
+        fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
+      }
     }
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
@@ -696,8 +791,11 @@ __device__ __forceinline__ int32_t group_of(const GemmParams &p, int64_t tm) {
 // with S_g = floor(off[g] / kBM) + g, which always holds ceil(rows_g / kBM)
 // tiles; a slot beyond its group's rows exits at once.  No prefix sums or
 // workspace are needed and the offsets never leave the device.
-template <class C, bool kGrouped, bool kPow2, int kOut, bool kGather>
+template <class C, class V>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
+  constexpr bool kGrouped = V::kGrouped;
+  constexpr int kOut = V::kOut;
+  constexpr bool kGather = V::kGather;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -719,7 +817,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     m0 = g0 + (tm - (g0 / C::kBM + g)) * C::kBM;
     m_end = g1;
     bq += (int64_t)g * p.N * p.K;
-    bs += (int64_t)g * (p.N / 128) * (p.K / kBK);
+    bs += (int64_t)g * (V::kBRow ? p.N : p.N / 128) * (p.K / kBK);
   }
   if (m0 >= m_end || m0 < 0) return;
 
@@ -738,7 +836,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     t.T = 0;
   }
   t.b_q = bq + n0 * p.K;
-  t.b_s = bs + (n0 >> 7) * t.KB;
+  t.b_s = bs + (V::kBRow ? n0 : (n0 >> 7)) * t.KB;
   t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
   t.n_valid = n_valid;
   TileOut o{nullptr, nullptr, nullptr};
@@ -748,28 +846,29 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     o.yq = p.yq + m0 * p.N + n0;
     o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
   }
-  gemm_tile<C, kPow2, kOut, kGather>(t, o, p.N, lds);
+  gemm_tile<C, V>(t, o, p.N, lds);
 }
 
-template <class C, bool kGrouped, bool kPow2, int kOut = kOutBf16, bool kGather = false>
+template <class C, class V>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, kGrouped, kPow2, kOut, kGather>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, V>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t grid = p.slots_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<C, kGrouped, kPow2, kOut, kGather>), dim3((unsigned)grid), dim3(C::kThreads),
+  hipLaunchKernelGGL((gemm_kernel<C, V>), dim3((unsigned)grid), dim3(C::kThreads),
                      C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
-template <bool kPow2, int kOut = kOutBf16>
+template <bool kPow2, int kOut = kOutBf16, bool kBRow = false>
 static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                         uint16_t *y, uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
                         hipStream_t stream) {
+  using V = Variant<false, kPow2, kOut, false, kBRow>;
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n};
@@ -777,16 +876,17 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
   if (large_tiles >= 256) {
     p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
-    return launch<CfgLarge, false, kPow2, kOut>(p, stream);
+    return launch<CfgLarge, V>(p, stream);
   }
   p.slots_m = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  return launch<CfgSmall, false, kPow2, kOut>(p, stream);
+  return launch<CfgSmall, V>(p, stream);
 }
 
 template <bool kPow2, bool kGather = false>
 static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                           const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N, int64_t K,
                           uint16_t *y, const int32_t *gather, int64_t T, hipStream_t stream) {
+  using V = Variant<true, kPow2, kOutBf16, kGather>;
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n};
@@ -794,10 +894,10 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
     p.slots_m = M_total / CfgLarge::kBM + G;
-    return launch<CfgLarge, true, kPow2, kOutBf16, kGather>(p, stream);
+    return launch<CfgLarge, V>(p, stream);
   }
   p.slots_m = M_total / CfgSmall::kBM + G;
-  return launch<CfgSmall, true, kPow2, kOutBf16, kGather>(p, stream);
+  return launch<CfgSmall, V>(p, stream);
 }
 
 hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
@@ -814,6 +914,13 @@ hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
                                          int mode, hipStream_t stream) {
   return mode == kModePow2 ? dense<false, kModePow2>(a_q, a_s, b_q, b_s, nullptr, yq, ys, M, N, K, stream)
                            : dense<false, kModeAmax>(a_q, a_s, b_q, b_s, nullptr, yq, ys, M, N, K, stream);
+}
+
+hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
+                                         const uint8_t *b_q, const float *b_s,
+                                         uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                         hipStream_t stream) {
+  return dense<false, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,

@@ -1,6 +1,7 @@
-// Activation (1x128) and weight (128x128) quantizers for gfx950.
+// Activation (1x128) and weight (128x128) quantizers for gfx950, and the
+// two-layout quantizer of the backward GEMMs.
 //
-// Both are HBM streams: 2 bytes of bf16 read and 1 byte of E4M3 written per
+// All are HBM streams: 2 bytes of bf16 read and 1 byte of E4M3 written per
 // element, plus one fp32 scale per block.  Loads are 16 bytes per lane and
 // cover whole 128-byte lines; the block |max| is reduced in registers and
 // through DPP lane exchanges, never through memory.
@@ -130,6 +131,171 @@ hipError_t launch_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
   else
     hipLaunchKernelGGL(quant_weight_128x128_kernel<kModePow2>, dim3((unsigned)tiles), dim3(kWThreads), 0,
                        stream, w, q, s, K, KB);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Both layouts in one pass, for the backward GEMMs of training end to end in
+// FP8 (page 1, "Der technische Durchbruch": FP8 in training as in generation).
+// Each GEMM wants its scale blocks along its contraction dimension, so the
+// weight gradient dW = dY^T X reads dY and X in blocks of 128 tokens x 1
+// channel, transposed ([channels][Mp], Mp = M rounded up to 128), and the data
+// gradient dX = dY W reads W's 128x128 tiles transposed ([K][N]).
+//
+// One workgroup of 256 lanes per 128x128 tile of a row-major [M][K] bf16
+// matrix.  Lane t owns the 8x8 sub-block rows 8*(t/16) .. +7, columns
+// 8*(t%16) .. +7: eight 16-byte loads, 16 lanes covering a 256-byte row
+// segment.
+//  - kTile (weights): one |max| and scale per tile, used for the row-major
+//    codes q [M][K] (scales [M/128][K/128]) and the transposed codes q_t [K][M]
+//    (scales [K/128][M/128]).
+//  - activations: the 1x128 row blocks (q [M][K], scales [M][K/128]; optional)
+//    and the 128x1 column blocks, transposed (q_t [K][Mp], scales [K][Mp/128]);
+//    rows past M read as +0, so the padding of q_t holds +0 codes and does not
+//    change a scale.
+// Row maxima reduce over the 16 lanes of a row segment (DPP), column maxima
+// over the four lanes of a wave that share a column (lane shuffles) and then
+// over the four waves (LDS).  The transposed codes are staged in LDS so that
+// each lane stores 16 contiguous bytes and a wave stores whole 128-byte lines.
+// ---------------------------------------------------------------------------
+constexpr int kDThreads = 256;
+constexpr int kTPitch = 128 + 16;  // LDS row pitch (bytes) of the transposed tile
+
+__device__ __forceinline__ float elem(const uint4 &v, int j) {
+  const uint32_t w = j < 2 ? v.x : (j < 4 ? v.y : (j < 6 ? v.z : v.w));
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+template <int kMode>
+__device__ __forceinline__ float quot(const BlockQ &p, float x) {
+  return (kMode == kModeAmax && p.slow) ? x / p.s : quotient<kMode>(p, x);
+}
+
+template <int kMode, bool kTile, bool kRowOut>
+__global__ __launch_bounds__(kDThreads) void quant_dual_kernel(
+    const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t Mp, uint8_t *__restrict__ q,
+    float *__restrict__ s, uint8_t *__restrict__ qt, float *__restrict__ st) {
+  __shared__ float red[4][128];
+  __shared__ __align__(16) uint8_t tq[128 * kTPitch];
+  const int64_t KB = K >> 7, MB = Mp >> 7;
+  const int64_t mb = blockIdx.x / KB, kb = blockIdx.x - mb * KB;
+  const int t = threadIdx.x, c = t & 15, g = t >> 4, wave = t >> 6;
+  const int64_t m0 = mb * 128, k0 = kb * 128;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + 8 * g + i;
+    v[i] = m < M ? load_stream16(x + m * K + k0 + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  float ra[8], ca[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ra[i] = chunk_absmax(v[i], 0.0f);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) a = max3_abs(a, elem(v[i], j), elem(v[i + 1], j));
+    ca[j] = a;
+  }
+
+  float tmax = 0.0f;  // kTile: the tile |max|
+  if constexpr (kTile) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tmax = __builtin_fmaxf(tmax, ra[i]);
+    tmax = group16_max(tmax);
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+    if ((t & 63) == 0) red[0][wave] = tmax;
+    __syncthreads();
+    tmax = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
+  } else {
+    if constexpr (kRowOut) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ra[i] = group16_max(ra[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ca[j] = __builtin_fmaxf(ca[j], __shfl_xor(ca[j], 16));
+      ca[j] = __builtin_fmaxf(ca[j], __shfl_xor(ca[j], 32));
+    }
+    if ((t & 63) < 16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][8 * c + j] = ca[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ca[j] = __builtin_fmaxf(__builtin_fmaxf(red[0][8 * c + j], red[1][8 * c + j]),
+                              __builtin_fmaxf(red[2][8 * c + j], red[3][8 * c + j]));
+  }
+
+  // Transposed codes: column j of the lane's sub-block is 8 consecutive bytes
+  // of row 8c+j of the transposed tile.
+  const BlockQ pt = block_params<kMode>(tmax);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const BlockQ pc = kTile ? pt : block_params<kMode>(ca[j]);
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = quot<kMode>(pc, elem(v[i], j));
+    uint2 o;
+    o.x = pack4_e4m3(r[0], r[1], r[2], r[3]);
+    o.y = pack4_e4m3(r[4], r[5], r[6], r[7]);
+    *reinterpret_cast<uint2 *>(tq + (8 * c + j) * kTPitch + 8 * g) = o;
+    if (!kTile && g == 0) st[(k0 + 8 * c + j) * MB + mb] = pc.s;
+  }
+  if (kTile && t == 0) st[kb * MB + mb] = pt.s;
+
+  if constexpr (kRowOut || kTile) {
+    if constexpr (kRowOut) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + 8 * g + i;
+        if (m < M) {
+          const BlockQ pr = kTile ? pt : block_params<kMode>(ra[i]);
+          *reinterpret_cast<uint2 *>(q + m * K + k0 + 8 * c) = quant_chunk<kMode>(pr, v[i]);
+          if (!kTile && c == 0) s[m * KB + kb] = pr.s;
+        }
+      }
+      if (kTile && t == 0) s[mb * KB + kb] = pt.s;
+    }
+  }
+
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = u * kDThreads + t;  // 16-byte chunk of the 128x128 transposed tile
+    const int row = id >> 3, part = id & 7;
+    const uint4 w = *reinterpret_cast<const uint4 *>(tq + row * kTPitch + part * 16);
+    *reinterpret_cast<uint4 *>(qt + (k0 + row) * Mp + m0 + part * 16) = w;
+  }
+}
+
+template <int kMode, bool kTile>
+static void launch_dual(const uint16_t *x, int64_t M, int64_t K, int64_t Mp, uint8_t *q, float *s, uint8_t *qt,
+                        float *st, hipStream_t stream) {
+  const int64_t tiles = (Mp / 128) * (K / 128);
+  if (q)
+    hipLaunchKernelGGL((quant_dual_kernel<kMode, kTile, true>), dim3((unsigned)tiles), dim3(kDThreads), 0, stream,
+                       x, M, K, Mp, q, s, qt, st);
+  else
+    hipLaunchKernelGGL((quant_dual_kernel<kMode, kTile, false>), dim3((unsigned)tiles), dim3(kDThreads), 0,
+                       stream, x, M, K, Mp, q, s, qt, st);
+}
+
+hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
+                             float *st, int mode, bool tile, hipStream_t stream) {
+  const int64_t Mp = (M + 127) / 128 * 128;
+  if (Mp == 0 || K == 0) return hipSuccess;
+  if (mode == kModeAmax) {
+    if (tile) launch_dual<kModeAmax, true>(x, M, K, Mp, q, s, qt, st, stream);
+    else launch_dual<kModeAmax, false>(x, M, K, Mp, q, s, qt, st, stream);
+  } else {
+    if (tile) launch_dual<kModePow2, true>(x, M, K, Mp, q, s, qt, st, stream);
+    else launch_dual<kModePow2, false>(x, M, K, Mp, q, s, qt, st, stream);
+  }
   return hipGetLastError();
 }
 

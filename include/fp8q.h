@@ -98,6 +98,49 @@ fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
                                      void *stream);
 
 /*
+ * Both quantized layouts of an activation (or activation gradient) in one
+ * pass, for training end to end in FP8 (page 1, title and "Der technische
+ * Durchbruch": FP8 in training as well as in generation).  Each GEMM takes its
+ * scale blocks along its contraction dimension: the forward product and the
+ * data gradient read 1x128 blocks along a row; the weight gradient
+ * dW = dY^T X contracts over the tokens and reads blocks of 128 tokens x 1
+ * channel, stored transposed so that they too are contiguous rows.
+ *   x         [M][K] bf16 bits (in), M >= 0 any, K a multiple of 128
+ *   q         [M][K] E4M3 (out) and scales [M][K/128] (out): exactly the
+ *             outputs of fp8_quant_act_1x128.  Both may be NULL (then only the
+ *             transposed layout is written).
+ *   q_t       [K][Mp] E4M3 (out), Mp = M rounded up to a multiple of 128:
+ *             q_t[k][m] is x[m][k] quantized with the scale of its block of
+ *             rows 128*(m/128) .. +127 of column k; for m >= M it is 0x00.
+ *   scales_t  [K][Mp/128] fp32 (out): block (k, mb) covers x[128*mb ..][k]
+ *             (the rows below M only; rows past M count as zeros).
+ *   mode      fp8q_scale_mode, for both layouts
+ * Each 128x1 block follows exactly the rule of a 1x128 block of
+ * fp8_quant_act_1x128 (amax, scale, element rule).
+ */
+fp8q_status fp8_quant_act_dual(const uint16_t *x, int64_t M, int64_t K,
+                               uint8_t *q, float *scales,
+                               uint8_t *q_t, float *scales_t, int mode,
+                               void *stream);
+
+/*
+ * Both layouts of a quantized weight in one pass (the data gradient
+ * dX = dY W reads W's 128x128 tiles with N as its contraction dimension,
+ * i.e. W^T row-major; a tile of W^T holds the values of one tile of W).
+ *   w         [N][K] bf16 bits (in), N and K multiples of 128
+ *   q, scales exactly the outputs of fp8_quant_weight_128x128 (both may be NULL)
+ *   q_t       [K][N] E4M3 (out): q_t[k][n] = q[n][k]
+ *   scales_t  [K/128][N/128] fp32 (out): scales_t[kb][nb] = scales[nb][kb]
+ *   mode      fp8q_scale_mode
+ * With q_t and scales_t, dX = fp8_blockscaled_gemm(dY_q, dY_s, q_t, scales_t)
+ * with M = tokens, N = K of the layer, K = N of the layer.
+ */
+fp8q_status fp8_quant_weight_128x128_dual(const uint16_t *w, int64_t N, int64_t K,
+                                          uint8_t *q, float *scales,
+                                          uint8_t *q_t, float *scales_t, int mode,
+                                          void *stream);
+
+/*
  * Block-scaled FP8 GEMM of a linear layer, Y = X * W^T (page 1, "Der
  * technische Durchbruch"; the GEMM outputs feed bf16 operators):
  *   Y[m][n] = sum_kb a_s[m][kb] * b_s[n/128][kb] *
@@ -133,6 +176,27 @@ fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
                                        const uint8_t *b_q, const float *b_s,
                                        uint8_t *y_q, float *y_s,
                                        int64_t M, int64_t N, int64_t K, int mode,
+                                       void *stream);
+
+/*
+ * Block-scaled FP8 GEMM with 1x128 blocks on both operands: the weight
+ * gradient of a linear layer (training end to end in FP8, page 1, title and
+ * "Der technische Durchbruch"), dW = dY^T X, contracted over the tokens:
+ *   Y[m][n] = sum_kb a_s[m][kb] * b_s[n][kb] *
+ *                    sum_{k in block kb} dec(a_q[m][k]) * dec(b_q[n][k])
+ *   a_q [M][K], a_s [M][K/128]   (dY^T: q_t and scales_t of fp8_quant_act_dual
+ *                                 of dY; M = output features)
+ *   b_q [N][K], b_s [N][K/128]   (X^T: the same of X; N = input features, a
+ *                                 multiple of 128)
+ *   y   [M][N] bf16 bits (out)   (dW, in the layout of W)
+ *   K   tokens rounded up to a multiple of 128 (Mp of fp8_quant_act_dual)
+ * fp32 accumulation, one bf16 rounding (nearest even) at the end; the
+ * summation order is fixed but unspecified.  The only difference from
+ * fp8_blockscaled_gemm is b_s: one scale per row of b and block of K.
+ */
+fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
+                                       const uint8_t *b_q, const float *b_s,
+                                       uint16_t *y, int64_t M, int64_t N, int64_t K,
                                        void *stream);
 
 /*

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-              "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
+              "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
+              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
               "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
@@ -107,6 +108,34 @@ def test_grouped_argument_errors(lib, fn):
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, None) == 3
     assert f(None, None, None, None, None, 3, 0, 128, 128, None, None) == 0
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, (1 << 22) + 128, GOOD, None) == 2
+
+
+@pytest.mark.parametrize("fn", ["fp8_quant_act_dual", "fp8_quant_weight_128x128_dual"])
+def test_dual_quantizer_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    #        x     M    K    q     s     q_t   s_t   mode
+    assert f(GOOD, 128, 100, GOOD, GOOD, GOOD, GOOD, 0, None) == 2       # K % 128
+    assert f(GOOD, -1, 128, GOOD, GOOD, GOOD, GOOD, 0, None) == 1        # negative size
+    assert f(GOOD, 128, 128, GOOD, GOOD, GOOD, GOOD, 3, None) == 1       # unknown mode
+    assert f(GOOD, 128, 128, GOOD, None, GOOD, GOOD, 0, None) == 1       # q without scales
+    assert "both" in _err(lib)
+    assert f(GOOD, 128, 128, None, None, None, GOOD, 0, None) == 1       # no transposed output
+    assert f(GOOD, 128, 128, None, None, GOOD, ODD, 0, None) == 3        # misaligned scales_t
+    assert f(GOOD, 128, 128, ODD, GOOD, GOOD, GOOD, 0, None) == 3        # misaligned q
+    assert f(None, 0, 128, None, None, None, None, 0, None) == 0         # empty call
+    if fn == "fp8_quant_weight_128x128_dual":
+        assert f(GOOD, 100, 128, GOOD, GOOD, GOOD, GOOD, 0, None) == 2   # N % 128
+
+
+def test_wgrad_argument_errors(lib):
+    f = lib.fp8_blockscaled_gemm_wgrad
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, None) == 2      # K % 128
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 100, 128, None) == 2      # N % 128
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, -1, 128, 128, None) == 1
+    assert f(GOOD, GOOD, GOOD, None, GOOD, 64, 128, 128, None) == 1      # null pointer
+    assert f(GOOD, GOOD, ODD, GOOD, GOOD, 64, 128, 128, None) == 3
+    assert f(None, None, None, None, None, 0, 128, 128, None) == 0       # empty call
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, None) == 2
 
 
 def test_gather_argument_errors(lib):
