@@ -431,6 +431,7 @@ def moe(fp8q, synth, torch, dev, reps):
 
 
 def backward(fp8q, synth, layers, torch, dev, M, reps):
+    import numpy as np
     """Backward pass of the four Llama-shaped layers at 4096 tokens (training
     end to end in FP8): per layer, dY [M, N] ~ N(0, 1e-3) quantized in both
     layouts in one pass, X in 128-token column blocks (its row blocks are the
@@ -483,6 +484,37 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
         tot["flops"] += f_dg + f_wg
         del g, gq, gs, gtq, gts, xtq, xts, wq, ws, wtq, wts, dx, dw
         torch.cuda.empty_cache()
+    # The two-layout activation quantizer on >= 1.2 GB of rotating inputs per
+    # shape (the 256 MB last-level cache cannot hold them), as the 1x128
+    # quantizer is timed: its HBM rate, comparable with the copy kernel's.
+    q_s, q_b = 0.0, 0.0
+    Mp = (M + 127) // 128 * 128
+    for l in layers:
+        K = l["K"]
+        nrot = max(1, int(np.ceil(1.2e9 / (M * K * 4))))
+        xs = [l["x"]] + [torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+                         for _ in range(nrot - 1)]
+        bufs = (torch.empty((M, K), dtype=torch.uint8, device=dev),
+                torch.empty((M, K // 128), dtype=torch.float32, device=dev),
+                torch.empty((K, Mp), dtype=torch.uint8, device=dev),
+                torch.empty((K, Mp // 128), dtype=torch.float32, device=dev))
+        ctr = [0]
+
+        def qd(xs=xs, bufs=bufs, ctr=ctr):
+            fp8q.fp8_quant_act_dual(xs[ctr[0] % len(xs)], out=bufs)
+            ctr[0] += 1
+        qd()
+        t = time_loop(qd, reps * len(xs), torch)
+        b = M * K * 4 + M * (K // 128) * 4 + K * (Mp // 128) * 4
+        q_s += t
+        q_b += b
+        out[l["name"]]["quant_x_dual_rotating_gbs"] = round(b / t / 1e9, 1)
+        del xs, bufs
+        torch.cuda.empty_cache()
+    out["act_dual_rotating"] = {"gbs": round(q_b / q_s / 1e9, 1), "frac_hbm": round(q_b / q_s / 1e9 / HBM_PEAK_GBS, 4),
+                                "bytes_per_element": "2 read + 1 + 1 written, + 2 scale sets"}
+    log(f"act dual quant (rotating inputs) {q_b / q_s / 1e9:.1f} GB/s")
+
     step_s = tot["dgrad_s"] + tot["wgrad_s"] + tot["quant_s"]
     out["total"] = {
         "backward_step_ms": round(step_s * 1e3, 3),

@@ -166,123 +166,251 @@ __device__ __forceinline__ float elem(const uint4 &v, int j) {
   return (j & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
+// Eight values of one block -> eight E4M3 bytes.  The block's parameters may
+// differ between lanes.  Every pow2 block, and every amax block with a normal
+// scale on the fast path, has |x / s| <= 448 * (1 + 2^-23), which the
+// conversion rounds to at most 448 by itself; blocks with a subnormal scale or
+// on the exact-division path (amax below 2^-100) take the clamped path.  The
+// choice is one wave-uniform branch, so the common case has no per-element
+// branches or clamps.
 template <int kMode>
-__device__ __forceinline__ float quot(const BlockQ &p, float x) {
-  return (kMode == kModeAmax && p.slow) ? x / p.s : quotient<kMode>(p, x);
+__device__ __forceinline__ uint2 quant8(const BlockQ &p, const float (&f)[8]) {
+  float r[8];
+  const bool plain = kMode == kModePow2 || (!p.slow && p.s >= 0x1p-126f);
+  if (__ballot(!plain) == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = quotient<kMode>(p, f[i]);
+    uint2 o;
+    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], o.x, true);
+    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
+    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], o.y, true);
+    return o;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float d = f[i] / p.s;
+    const float e = quotient<kMode>(p, f[i]);
+    r[i] = (kMode == kModeAmax && p.slow) ? d : e;
+  }
+  uint2 o;
+  o.x = pack4_e4m3(r[0], r[1], r[2], r[3]);
+  o.y = pack4_e4m3(r[4], r[5], r[6], r[7]);
+  return o;
+}
+
+// Block parameters shared through LDS: (s, y) with y = RN(1/s) negated on the
+// exact-division path (amax mode), or (s, e) (pow2 mode).
+template <int kMode>
+__device__ __forceinline__ float2 pack_params(const BlockQ &p) {
+  return kMode == kModeAmax ? make_float2(p.s, p.slow ? -p.y : p.y) : make_float2(p.s, __int_as_float(p.e));
+}
+
+template <int kMode>
+__device__ __forceinline__ BlockQ unpack_params(float2 v) {
+  BlockQ p;
+  p.s = v.x;
+  if (kMode == kModeAmax) {
+    p.y = __builtin_fabsf(v.y);
+    p.slow = v.y < 0.0f;
+    p.e = 0;
+  } else {
+    p.y = 0.0f;
+    p.slow = false;
+    p.e = __float_as_int(v.y);
+  }
+  return p;
+}
+
+// Marks the packed values as redefined, so the fp32 values unpacked from them
+// in one phase are not kept alive (in 64 registers) for the next phase.
+__device__ __forceinline__ void repack(uint4 (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+}
+
+// Block maxima on magnitude bits: |x| of a bf16 orders like the integer
+// (bits & 0x7FFF), so two magnitudes per word reduce with one packed 16-bit
+// integer max; a maximum m converts back to fp32 exactly as m << 16.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pkmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ float mag_lo(uint32_t m) { return __uint_as_float(m << 16); }
+__device__ __forceinline__ float mag_hi(uint32_t m) { return __uint_as_float(m & 0xFFFF0000u); }
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_pkmax(uint32_t v) {
+  return pkmax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t group16_pkmax(uint32_t v) {
+  v = dpp_pkmax<kDppQuadSwap1>(v);
+  v = dpp_pkmax<kDppQuadSwap2>(v);
+  v = dpp_pkmax<kDppHalfMirror>(v);
+  return dpp_pkmax<kDppMirror>(v);
+}
+
+struct DualArgs {
+  const uint16_t *x;
+  int64_t M, K, Mp, KB, MB;
+  uint8_t *q;
+  float *s;
+  uint8_t *qt;
+  float *st;
+};
+
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only
+// (its global stores need not have completed).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int kMode, bool kTile, bool kRowOut>
-__global__ __launch_bounds__(kDThreads) void quant_dual_kernel(
-    const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t Mp, uint8_t *__restrict__ q,
-    float *__restrict__ s, uint8_t *__restrict__ qt, float *__restrict__ st) {
-  __shared__ float red[4][128];
+__global__ __launch_bounds__(kDThreads) void quant_dual_kernel(DualArgs a) {
+  __shared__ uint32_t red[4][64];               // per wave: column-pair maxima
+  __shared__ __align__(16) float2 colp[128];  // parameters of the tile's 128 column blocks
+  __shared__ __align__(16) float2 rowp[128];  // and of its 128 row blocks
   __shared__ __align__(16) uint8_t tq[128 * kTPitch];
-  const int64_t KB = K >> 7, MB = Mp >> 7;
+  const int64_t KB = a.KB, MB = a.MB, M = a.M, K = a.K, Mp = a.Mp;
   const int64_t mb = blockIdx.x / KB, kb = blockIdx.x - mb * KB;
   const int t = threadIdx.x, c = t & 15, g = t >> 4, wave = t >> 6;
   const int64_t m0 = mb * 128, k0 = kb * 128;
 
+  // Branch-free loads: a row past M reads row M-1 (M >= 1), then becomes zeros.
   uint4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t m = m0 + 8 * g + i;
-    v[i] = m < M ? load_stream16(x + m * K + k0 + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    v[i] = load_stream16(a.x + (m < M ? m : M - 1) * K + k0 + 8 * c);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (m0 + 8 * g + i >= M) v[i] = make_uint4(0u, 0u, 0u, 0u);
 
-  float ra[8], ca[8];
+  // Magnitude maxima: cm[d] holds columns 8c+2d (low half) and 8c+2d+1 (high)
+  // over the lane's 8 rows; rp[k] rows 8g+2k (low) and 8g+2k+1 (high) over
+  // the lane's 8 columns.
+  uint32_t cm[4] = {0u, 0u, 0u, 0u}, rp[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ra[i] = chunk_absmax(v[i], 0.0f);
+  for (int k = 0; k < 4; ++k) {
+    uint32_t rm[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) a = max3_abs(a, elem(v[i], j), elem(v[i + 1], j));
-    ca[j] = a;
-  }
-
-  float tmax = 0.0f;  // kTile: the tile |max|
-  if constexpr (kTile) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tmax = __builtin_fmaxf(tmax, ra[i]);
-    tmax = group16_max(tmax);
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-    if ((t & 63) == 0) red[0][wave] = tmax;
-    __syncthreads();
-    tmax = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
-  } else {
-    if constexpr (kRowOut) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ra[i] = group16_max(ra[i]);
+    for (int h = 0; h < 2; ++h) {
+      const uint4 &w = v[2 * k + h];
+      const uint32_t m_0 = w.x & 0x7FFF7FFFu, m_1 = w.y & 0x7FFF7FFFu;
+      const uint32_t m_2 = w.z & 0x7FFF7FFFu, m_3 = w.w & 0x7FFF7FFFu;
+      cm[0] = pkmax(cm[0], m_0);
+      cm[1] = pkmax(cm[1], m_1);
+      cm[2] = pkmax(cm[2], m_2);
+      cm[3] = pkmax(cm[3], m_3);
+      rm[h] = pkmax(pkmax(m_0, m_1), pkmax(m_2, m_3));
     }
+    // low halves of both rows side by side, then the high halves
+    rp[k] = pkmax((rm[0] & 0xFFFFu) | (rm[1] << 16), (rm[0] >> 16) | (rm[1] & 0xFFFF0000u));
+  }
+
+  BlockQ pt;  // kTile: the tile's parameters (every lane computes them)
+  if constexpr (kTile) {
+    uint32_t m2 = pkmax(pkmax(rp[0], rp[1]), pkmax(rp[2], rp[3]));
+    m2 = group16_pkmax(m2);
+    float m = __builtin_fmaxf(mag_lo(m2), mag_hi(m2));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    if ((t & 63) == 0) red[0][wave] = __float_as_uint(m);
+    lds_barrier();
+    m = __builtin_fmaxf(__builtin_fmaxf(__uint_as_float(red[0][0]), __uint_as_float(red[0][1])),
+                        __builtin_fmaxf(__uint_as_float(red[0][2]), __uint_as_float(red[0][3])));
+    pt = block_params<kMode>(m);
+    if (t == 0) {
+      a.st[kb * MB + mb] = pt.s;
+      if (kRowOut) a.s[mb * KB + kb] = pt.s;
+    }
+  } else {
+    // Column blocks: the four lanes of a wave that share a column, then the
+    // four waves; lane t < 128 then computes column t's parameters once.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ca[j] = __builtin_fmaxf(ca[j], __shfl_xor(ca[j], 16));
-      ca[j] = __builtin_fmaxf(ca[j], __shfl_xor(ca[j], 32));
+    for (int d = 0; d < 4; ++d) {
+      cm[d] = pkmax(cm[d], (uint32_t)__shfl_xor((int)cm[d], 16));
+      cm[d] = pkmax(cm[d], (uint32_t)__shfl_xor((int)cm[d], 32));
     }
     if ((t & 63) < 16) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) red[wave][8 * c + j] = ca[j];
+      for (int d = 0; d < 4; ++d) red[wave][4 * c + d] = cm[d];
     }
-    __syncthreads();
+    if constexpr (kRowOut) {
+      // Row blocks: the 16 lanes of a row segment; lane c < 8 of the segment
+      // then computes the parameters of row 8g + c.
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ca[j] = __builtin_fmaxf(__builtin_fmaxf(red[0][8 * c + j], red[1][8 * c + j]),
-                              __builtin_fmaxf(red[2][8 * c + j], red[3][8 * c + j]));
+      for (int k = 0; k < 4; ++k) rp[k] = group16_pkmax(rp[k]);
+      const int ck = (c >> 1) & 3;
+      const uint32_t w = ck == 0 ? rp[0] : (ck == 1 ? rp[1] : (ck == 2 ? rp[2] : rp[3]));
+      if (c < 8) {
+        const BlockQ pr = block_params<kMode>((c & 1) ? mag_hi(w) : mag_lo(w));
+        rowp[8 * g + c] = pack_params<kMode>(pr);
+        const int64_t m = m0 + 8 * g + c;
+        if (m < M) a.s[m * KB + kb] = pr.s;
+      }
+    }
+    lds_barrier();
+    if (t < 128) {
+      const uint32_t w = pkmax(pkmax(red[0][t >> 1], red[1][t >> 1]), pkmax(red[2][t >> 1], red[3][t >> 1]));
+      const BlockQ pc = block_params<kMode>((t & 1) ? mag_hi(w) : mag_lo(w));
+      colp[t] = pack_params<kMode>(pc);
+      a.st[(k0 + t) * MB + mb] = pc.s;
+    }
+    lds_barrier();
   }
 
   // Transposed codes: column j of the lane's sub-block is 8 consecutive bytes
   // of row 8c+j of the transposed tile.
-  const BlockQ pt = block_params<kMode>(tmax);
+  repack(v);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const BlockQ pc = kTile ? pt : block_params<kMode>(ca[j]);
-    float r[8];
+    const BlockQ pc = kTile ? pt : unpack_params<kMode>(colp[8 * c + j]);
+    float f[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = quot<kMode>(pc, elem(v[i], j));
-    uint2 o;
-    o.x = pack4_e4m3(r[0], r[1], r[2], r[3]);
-    o.y = pack4_e4m3(r[4], r[5], r[6], r[7]);
-    *reinterpret_cast<uint2 *>(tq + (8 * c + j) * kTPitch + 8 * g) = o;
-    if (!kTile && g == 0) st[(k0 + 8 * c + j) * MB + mb] = pc.s;
+    for (int i = 0; i < 8; ++i) f[i] = elem(v[i], j);
+    *reinterpret_cast<uint2 *>(tq + (8 * c + j) * kTPitch + 8 * g) = quant8<kMode>(pc, f);
   }
-  if (kTile && t == 0) st[kb * MB + mb] = pt.s;
 
-  if constexpr (kRowOut || kTile) {
-    if constexpr (kRowOut) {
+  if constexpr (kRowOut) {
+    repack(v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + 8 * g + i;
-        if (m < M) {
-          const BlockQ pr = kTile ? pt : block_params<kMode>(ra[i]);
-          *reinterpret_cast<uint2 *>(q + m * K + k0 + 8 * c) = quant_chunk<kMode>(pr, v[i]);
-          if (!kTile && c == 0) s[m * KB + kb] = pr.s;
-        }
-      }
-      if (kTile && t == 0) s[mb * KB + kb] = pt.s;
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + 8 * g + i;
+      const BlockQ pr = kTile ? pt : unpack_params<kMode>(rowp[8 * g + i]);
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = elem(v[i], j);
+      const uint2 o = quant8<kMode>(pr, f);
+      if (m < M) *reinterpret_cast<uint2 *>(a.q + m * K + k0 + 8 * c) = o;
     }
   }
 
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int id = u * kDThreads + t;  // 16-byte chunk of the 128x128 transposed tile
     const int row = id >> 3, part = id & 7;
     const uint4 w = *reinterpret_cast<const uint4 *>(tq + row * kTPitch + part * 16);
-    *reinterpret_cast<uint4 *>(qt + (k0 + row) * Mp + m0 + part * 16) = w;
+    *reinterpret_cast<uint4 *>(a.qt + (k0 + row) * Mp + m0 + part * 16) = w;
   }
 }
 
 template <int kMode, bool kTile>
 static void launch_dual(const uint16_t *x, int64_t M, int64_t K, int64_t Mp, uint8_t *q, float *s, uint8_t *qt,
                         float *st, hipStream_t stream) {
-  const int64_t tiles = (Mp / 128) * (K / 128);
+  const DualArgs a{x, M, K, Mp, K / 128, Mp / 128, q, s, qt, st};
+  const int64_t tiles = a.MB * a.KB;
   if (q)
     hipLaunchKernelGGL((quant_dual_kernel<kMode, kTile, true>), dim3((unsigned)tiles), dim3(kDThreads), 0, stream,
-                       x, M, K, Mp, q, s, qt, st);
+                       a);
   else
     hipLaunchKernelGGL((quant_dual_kernel<kMode, kTile, false>), dim3((unsigned)tiles), dim3(kDThreads), 0,
-                       stream, x, M, K, Mp, q, s, qt, st);
+                       stream, a);
 }
 
 hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
