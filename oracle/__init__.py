@@ -25,5 +25,7 @@ from .oracle import (  # noqa: F401
     gemm_dgrad_sampled_f64,
     gemm_wgrad_f64,
     gemm_wgrad_sampled_f64,
+    kv_cache_append,
+    attention_decode_f64,
     num_threads,
 )

@@ -289,3 +289,63 @@ def gemm_wgrad_sampled_f64(gtq, gts, xtq, xts, ns, ks):
     a = _dequant_rows(_c(gtq, np.uint8)[ns], _c(gts, np.float32)[ns])
     b = _dequant_rows(_c(xtq, np.uint8)[ks], _c(xts, np.float32)[ks])
     return np.einsum("ij,ij->i", a, b)
+
+
+# ---------------------------------------------------------------------------
+# FP8 KV cache and FP8 attention (page 1, "Leistungsgewinne in der Praxis":
+# extending FP8 to the KV cache and to attention raises the end-to-end gain
+# to about 48%).  The pages give no layout; the reading taken here applies
+# the recipe's activation rule: every key and value row of one token and one
+# key/value head (head dimension 128) is one 1x128 block with its own scale,
+# and so is every query row of one query head.  Decode attention is the
+# standard softmax(q k^T / sqrt(D)) v over the cached tokens, with grouped
+# query heads (query head h reads key/value head h // (Hq / Hkv)).
+# ---------------------------------------------------------------------------
+
+def kv_cache_append(new_bits, pos, cache_q, cache_s, mode=MODE_AMAX):
+    """Quantize one new row per sequence and key/value head and store it at
+    token position pos[b]: new_bits uint16 [B, Hkv, D] (bf16), cache_q uint8
+    [B, Hkv, S, D], cache_s f32 [B, Hkv, S] (updated in place and returned).
+    A position outside [0, S) stores nothing."""
+    new = _c(new_bits, np.uint16)
+    B, H, D = new.shape
+    q, s = quant_act_1x128(new.reshape(B * H, D), mode)
+    q, s = q.reshape(B, H, D), s.reshape(B, H)
+    for b in range(B):
+        p = int(pos[b])
+        if 0 <= p < cache_q.shape[2]:
+            cache_q[b, :, p] = q[b]
+            cache_s[b, :, p] = s[b]
+    return cache_q, cache_s
+
+
+def attention_decode_f64(qq, qs, kq, ks, vq, vs, seq_len):
+    """One query token per sequence against its cached keys and values.
+
+    qq uint8 [B, Hq, D], qs f32 [B, Hq]   query rows (1x128 blocks)
+    kq, vq uint8 [B, Hkv, S, D], ks, vs f32 [B, Hkv, S]
+    seq_len [B]: tokens 0 .. min(seq_len[b], S)-1 are attended; a sequence
+    with none gives a zero output.
+    Returns o [B, Hq, D] (fp64): every operand dequantized exactly, scores,
+    softmax and the weighted sum of values in fp64.
+    """
+    table = e4m3_decode_table()
+    qq, kq, vq = _c(qq, np.uint8), _c(kq, np.uint8), _c(vq, np.uint8)
+    B, Hq, D = qq.shape
+    Hkv, S = kq.shape[1], kq.shape[2]
+    grp = Hq // Hkv
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = min(int(seq_len[b]), S)
+        if L <= 0:
+            continue
+        q = table[qq[b]] * np.asarray(qs[b], dtype=np.float64)[:, None]
+        for g in range(Hkv):
+            k = table[kq[b, g, :L]] * np.asarray(ks[b, g, :L], dtype=np.float64)[:, None]
+            v = table[vq[b, g, :L]] * np.asarray(vs[b, g, :L], dtype=np.float64)[:, None]
+            sc = q[g * grp:(g + 1) * grp] @ k.T / np.sqrt(D)
+            sc -= sc.max(axis=1, keepdims=True)
+            p = np.exp(sc)
+            p /= p.sum(axis=1, keepdims=True)
+            o[b, g * grp:(g + 1) * grp] = p @ v
+    return o
