@@ -117,9 +117,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,backward,recal,moe,dispatch,bf16,cpu",
-                    help="extra measurements after the step "
-                         "(comma list of pow2, fused, backward, recal, moe, dispatch, bf16, cpu)")
+    ap.add_argument("--sections", default="pow2,fused,backward,recal,moe,dispatch,attention,bf16,cpu",
+                    help="extra measurements after the step (comma list of pow2, fused, backward, recal, "
+                         "moe, dispatch, attention, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -292,6 +292,8 @@ def main():
         result["moe"] = moe(fp8q, synth, torch, dev, reps)
     if "backward" in sections:
         result["backward"] = backward(fp8q, synth, layers, torch, dev, M, reps)
+    if "attention" in sections:
+        result["attention_decode"] = attention(fp8q, synth, torch, dev, reps)
     if "dispatch" in sections:
         result["moe_dispatch"] = dispatch(fp8q, synth, torch, dev, reps)
     if "bf16" in sections:
@@ -524,6 +526,50 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
                 "W's transposed tiles are made once per weight update (quant_w_dual)"}
     log(f"backward step {step_s * 1e3:.3f} ms, {tot['flops'] / step_s / 1e12:.1f} TFLOP/s")
     return out
+
+
+def attention(fp8q, synth, torch, dev, reps):
+    """FP8 decode attention over an FP8 KV cache, Llama-3.1-8B shape: 64
+    sequences, 32 query and 8 key/value heads of 128, an 8192-token cache,
+    lengths drawn uniformly in [2048, 6144] (mean about 4096); random E4M3
+    cache rows with scales in [1e-3, 1.1e-2].  HBM-bound: the figure is the
+    bytes the kernel must read (the live cache rows and their scales, the
+    queries) and write (the output) per launch over its duration."""
+    import numpy as np
+    B, Hq, Hkv, S, D = 64, 32, 8, 8192, 128
+    g = torch.Generator(device=dev).manual_seed(synth.seed_of(18, 0, 0))
+    kq = (torch.randn((B, Hkv, S, D), device=dev, generator=g) * 32).clamp(-448, 448).to(torch.float8_e4m3fn)
+    vq = (torch.randn((B, Hkv, S, D), device=dev, generator=g) * 32).clamp(-448, 448).to(torch.float8_e4m3fn)
+    ks = torch.rand((B, Hkv, S), device=dev, generator=g) * 0.01 + 0.001
+    vs = torch.rand((B, Hkv, S), device=dev, generator=g) * 0.01 + 0.001
+    cache = (kq.view(torch.uint8), ks, vq.view(torch.uint8), vs)
+    lens = np.random.default_rng(np.random.SeedSequence([18, 0, 1])).integers(2048, 6145, B).astype(np.int32)
+    dlen = torch.from_numpy(lens).to(dev)
+    q = torch.randn((B * Hq, D), device=dev, generator=g).to(torch.bfloat16)
+    q_q, q_s = fp8q.fp8_quant_act_1x128(q)
+    q_q, q_s = q_q.view(B, Hq, D), q_s.view(B, Hq)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    run = lambda: fp8q.fp8_attention_decode(q_q, q_s, cache, dlen, out=out)
+    run()
+    t = time_loop(run, reps * 5, torch)
+    kv = int(lens.sum()) * Hkv * 2 * (D + 4)
+    nbytes = kv + B * Hq * (D + 4) + B * Hq * D * 2
+    # the cache append of one decode step (one key and value row per sequence and head)
+    kn = torch.randn((B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    pos = torch.from_numpy(np.minimum(lens, S - 1)).to(dev)
+    app = lambda: fp8q.fp8_kv_cache_append(kn, vn, pos, cache)
+    app()
+    t_app = time_loop(app, reps * 5, torch)
+    res = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "cache_tokens": S,
+           "mean_len": float(lens.mean()), "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
+           "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
+           "kv_bytes_fp8": kv, "kv_bytes_bf16_equivalent": int(lens.sum()) * Hkv * 2 * D * 2,
+           "append_us": round(t_app * 1e6, 2)}
+    log(f"attention decode {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s; cache append {t_app * 1e6:.1f} us")
+    del kq, vq, ks, vs, cache
+    torch.cuda.empty_cache()
+    return res
 
 
 def dispatch(fp8q, synth, torch, dev, reps):

@@ -27,7 +27,7 @@ __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
            "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
-           "abi_version", "library_path"]
+           "fp8_kv_cache_append", "fp8_attention_decode", "abi_version", "library_path"]
 
 
 def library_path():
@@ -293,4 +293,61 @@ def fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out=None):
         raise ValueError("output shape does not match")
     _lib.check("fp8_blockscaled_gemm_wgrad",
                _lib.load().fp8_blockscaled_gemm_wgrad(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
+    return y
+
+
+def fp8_kv_cache_append(k_new, v_new, pos, cache, mode="amax"):
+    """Quantize one new key and value row per sequence and head (bf16
+    [B, Hkv, 128] each) into the FP8 cache at token positions pos (int32 [B],
+    device).  cache = (k_q uint8 [B, Hkv, S, 128], k_s f32 [B, Hkv, S],
+    v_q, v_s), updated in place."""
+    kq, ks, vq, vs = cache
+    pk = _dev(k_new, "k_new", torch.bfloat16, 3)
+    pv = _dev(v_new, "v_new", torch.bfloat16, 3)
+    ppos = _dev(pos, "pos", torch.int32, 1)
+    kq, pkq = _as_bytes(kq, "k_cache", 4)
+    vq, pvq = _as_bytes(vq, "v_cache", 4)
+    pks = _dev(ks, "k_scale", torch.float32, 3)
+    pvs = _dev(vs, "v_scale", torch.float32, 3)
+    B, H, S, Dh = kq.shape
+    if Dh != 128 or tuple(k_new.shape) != (B, H, 128) or tuple(v_new.shape) != (B, H, 128):
+        raise ValueError("new rows must be [B, Hkv, 128] matching the cache")
+    if tuple(vq.shape) != (B, H, S, 128) or tuple(ks.shape) != (B, H, S) or tuple(vs.shape) != (B, H, S):
+        raise ValueError("cache shapes do not match")
+    if pos.numel() != B:
+        raise ValueError("pos must have B entries")
+    _lib.check("fp8_kv_cache_append",
+               _lib.load().fp8_kv_cache_append(pk, pv, ppos, pkq, pks, pvq, pvs, B, H, S, _mode(mode),
+                                               _stream(k_new)))
+    return cache
+
+
+def fp8_attention_decode(q_q, q_s, cache, seq_len, out=None):
+    """Decode attention of one query token per sequence over the FP8 cache.
+    q_q uint8 [B, Hq, 128] and q_s f32 [B, Hq] (the query rows in 1x128
+    blocks), cache as for fp8_kv_cache_append, seq_len int32 [B] (device).
+    Returns bf16 [B, Hq, 128]."""
+    kq, ks, vq, vs = cache
+    q_q, pq = _as_bytes(q_q, "q_q", 3)
+    pqs = _dev(q_s, "q_s", torch.float32, 2)
+    kq, pkq = _as_bytes(kq, "k_cache", 4)
+    vq, pvq = _as_bytes(vq, "v_cache", 4)
+    pks = _dev(ks, "k_scale", torch.float32, 3)
+    pvs = _dev(vs, "v_scale", torch.float32, 3)
+    plen = _dev(seq_len, "seq_len", torch.int32, 1)
+    B, Hq, Dh = q_q.shape
+    Bk, Hkv, S, Dk = kq.shape
+    if Dh != 128 or Dk != 128 or Bk != B or tuple(q_s.shape) != (B, Hq):
+        raise ValueError("query and cache shapes do not match")
+    if tuple(vq.shape) != (B, Hkv, S, 128) or tuple(ks.shape) != (B, Hkv, S) or tuple(vs.shape) != (B, Hkv, S):
+        raise ValueError("cache shapes do not match")
+    if seq_len.numel() != B:
+        raise ValueError("seq_len must have B entries")
+    y = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=q_q.device) if out is None else out
+    py = _dev(y, "out", torch.bfloat16, 3)
+    if tuple(y.shape) != (B, Hq, 128):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_attention_decode",
+               _lib.load().fp8_attention_decode(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S,
+                                                _stream(q_q)))
     return y

@@ -1,0 +1,349 @@
+// FP8 KV cache and FP8 decode attention for gfx950.
+//
+// Page "NVIDIA NeMo RL erreicht 48% Geschwindigkeitssteigerung ...", section
+// "Leistungsgewinne in der Praxis": FP8 for the KV cache and for attention is
+// what lifts the recipe from 15-25% on the linear layers to about 48% end to
+// end.  The recipe's activation rule is applied to the cache: every key and
+// value row of one token and one key/value head (D = 128) is a 1x128 block
+// with its own fp32 scale, and so is every query row.
+//
+// Cache layout: [B][Hkv][S][128] E4M3 bytes, scales [B][Hkv][S] -- the tokens
+// of one sequence and head are contiguous 128-byte rows, the unit every load
+// below reads whole.
+#include "fp8q_device.h"
+#include "fp8q_internal.h"
+
+namespace fp8q {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+
+// ---------------------------------------------------------------------------
+// Cache append: one new key row and one new value row per sequence and head,
+// quantized with the activation rule and stored at token position pos[b].
+// Eight lanes per row (as in the activation quantizer); row r of the 2*B*Hkv
+// rows is a key row for r < B*Hkv, else a value row.
+// ---------------------------------------------------------------------------
+template <int kMode>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
+                                                        const uint16_t *__restrict__ v_new,
+                                                        const int32_t *__restrict__ pos, uint8_t *__restrict__ kc,
+                                                        float *__restrict__ ks, uint8_t *__restrict__ vc,
+                                                        float *__restrict__ vs, int32_t B, int32_t H, int64_t S) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  const int64_t rows = (int64_t)B * H;
+  if (row >= 2 * rows) return;  // uniform over the 8 lanes of a row
+  const bool is_v = row >= rows;
+  const int64_t r = is_v ? row - rows : row;  // = b * H + h
+  const int64_t b = r / H;
+  const uint4 *src = reinterpret_cast<const uint4 *>((is_v ? v_new : k_new) + r * kHeadDim);
+  const uint4 x0 = src[sub], x1 = src[sub + 8];
+  float amax = group8_max(chunk_absmax(x1, chunk_absmax(x0, 0.0f)));
+  const BlockQ p = block_params<kMode>(amax);
+  const int64_t t = pos[b];
+  if (t < 0 || t >= S) return;
+  const int64_t slot = r * S + t;  // (b, h, t)
+  uint2 *dst = reinterpret_cast<uint2 *>((is_v ? vc : kc) + slot * kHeadDim);
+  dst[sub] = quant_chunk<kMode>(p, x0);
+  dst[sub + 8] = quant_chunk<kMode>(p, x1);
+  if (sub == 0) (is_v ? vs : ks)[slot] = p.s;
+}
+
+hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, uint8_t *kc,
+                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t H, int64_t S, int mode,
+                                  hipStream_t stream) {
+  const int64_t rows = 2 * (int64_t)B * H;
+  if (rows == 0) return hipSuccess;
+  const int64_t grid = (rows + 31) / 32;
+  if (mode == kModeAmax)
+    hipLaunchKernelGGL(kv_append_kernel<kModeAmax>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, pos,
+                       kc, ks, vc, vs, B, H, S);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<kModePow2>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, pos,
+                       kc, ks, vc, vs, B, H, S);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention: one query token per sequence,
+//   o[b][h] = sum_t softmax_t(q[b][h] . k[b][g][t] / sqrt(128)) v[b][g][t],
+// g = h / GRP (GRP query heads share a key/value head), t < min(len[b], S).
+//
+// One workgroup per (sequence, key/value head); its four waves take the
+// 64-token tiles of the sequence in turn and keep their own running maximum,
+// sum and output, merged through LDS at the end.
+//  - Scores: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens, E4M3 x
+//    E4M3, with the GRP query rows as the A operand (rows of D, padded to 16
+//    with zeros) and 16 key rows, read straight from the cache, as B.  Lane l
+//    then holds the scores of token l%16 for heads 4*(l/16) .. +3.  The query
+//    and key scales and log2(e)/sqrt(128) are applied to the fp32 result.
+//  - Softmax in base 2 (v_exp_f32), online over the tiles; per-head maxima
+//    and sums reduce over the 16 lanes of a row group with DPP and are then
+//    read out as wave-uniform values.
+//  - Values: lane l accumulates dims 8*(l%16) .. +7 for every head over the
+//    tokens 16*(l/16) .. +15 of each tile (8-byte loads, a whole 128-byte row
+//    per 16 lanes), weights p * v_scale passed through LDS; fp32 FMAs on the
+//    exactly decoded E4M3 values.
+// ---------------------------------------------------------------------------
+constexpr int kAttnWaves = 4;
+constexpr int kTileTok = 64;
+
+struct AttnArgs {
+  const uint8_t *qq;
+  const float *qs;
+  const uint8_t *kc;
+  const float *ks;
+  const uint8_t *vc;
+  const float *vs;
+  const int32_t *len;
+  uint16_t *out;
+  int32_t Hq, Hkv;
+  int64_t S;
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  return __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false)));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_fadd(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+// Max / sum over each row of 16 lanes (every lane gets the result).
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_fmax<kDppQuadSwap1>(v);
+  v = dpp_fmax<kDppQuadSwap2>(v);
+  v = dpp_fmax<kDppHalfMirror>(v);
+  return dpp_fmax<kDppMirror>(v);
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_fadd<kDppQuadSwap1>(v);
+  v = dpp_fadd<kDppQuadSwap2>(v);
+  v = dpp_fadd<kDppHalfMirror>(v);
+  return dpp_fadd<kDppMirror>(v);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Eight E4M3 bytes -> eight exact fp32 values.
+__device__ __forceinline__ void dec8(uint2 w, float (&f)[8]) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+  f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+
+template <int GRP>
+struct AttnLds {
+  float w[kAttnWaves][kTileTok][GRP];          // p * v_scale of a tile, per token and head
+  float m[kAttnWaves][GRP], l[kAttnWaves][GRP];
+  float acc[kAttnWaves][GRP][kHeadDim];
+};
+
+template <int GRP>
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a) {
+  static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "query heads per key/value head");
+  constexpr int kRowsPerLane = 4;  // MFMA output rows (heads) per lane
+  __shared__ AttnLds<GRP> L;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t bg = blockIdx.x;  // b * Hkv + g
+  const int64_t b = bg / a.Hkv, g = bg - b * a.Hkv;
+  int64_t len = a.len[b];
+  len = len < 0 ? 0 : (len > a.S ? a.S : len);
+  const int ntiles = (int)((len + kTileTok - 1) / kTileTok);
+  const int64_t h0 = g * GRP;  // first query head of the group
+
+  // Query rows as the A operand: lane l gives row l%16 (head h0 + l%16, zero
+  // past GRP), bytes 32*(l/16) .. +31.
+  v8i_t qf = {0, 0, 0, 0, 0, 0, 0, 0};
+  if ((lane & 15) < GRP) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.qq + ((b * a.Hq + h0 + (lane & 15)) * kHeadDim) + 32 * (lane >> 4));
+    const uint4 x = qp[0], y = qp[1];
+    qf[0] = x.x; qf[1] = x.y; qf[2] = x.z; qf[3] = x.w;
+    qf[4] = y.x; qf[5] = y.y; qf[6] = y.z; qf[7] = y.w;
+  }
+  // Score multiplier of this lane's four output rows (heads 4*(l/16)+r):
+  // query scale * log2(e) / sqrt(128); zero for padding rows.
+  constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
+  float qmul[kRowsPerLane];
+#pragma unroll
+  for (int r = 0; r < kRowsPerLane; ++r) {
+    const int h = 4 * (lane >> 4) + r;
+    qmul[r] = h < GRP ? a.qs[b * a.Hq + h0 + h] * kL2eRsqrtD : 0.0f;
+  }
+
+  const int64_t base = bg * a.S;  // (b, g, token 0) in the cache
+  const uint8_t *kc = a.kc + base * kHeadDim;
+  const uint8_t *vc = a.vc + base * kHeadDim;
+  const float *ksc = a.ks + base;
+  const float *vsc = a.vs + base;
+
+  float m_run[GRP], l_run[GRP];  // wave-uniform running max (base 2) and sum per head
+  float acc[GRP][8];             // dims 8*(l%16) .. +7, tokens 16*(l/16) .. of each tile
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    m_run[h] = -__builtin_inff();
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
+  }
+
+  const int tg = lane >> 4;  // token group of the value pass
+  const int dq = lane & 15;  // 8-dim slice of the value pass
+  for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
+    const int64_t t0 = (int64_t)tile * kTileTok;
+    // value rows of this lane (issued first: not needed until after the softmax)
+    uint2 vb[16];
+    float vsl[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int64_t t = t0 + 16 * tg + i;
+      t = t < len ? t : len - 1;
+      vb[i] = *reinterpret_cast<const uint2 *>(vc + t * kHeadDim + 8 * dq);
+    }
+    // scores: four MFMAs of 16 tokens; B operand = key rows t0 + 16j + l%16
+    float sc[4][kRowsPerLane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t t = t0 + 16 * j + (lane & 15);
+      const bool valid = t < len;
+      t = valid ? t : len - 1;
+      const uint4 *kp = reinterpret_cast<const uint4 *>(kc + t * kHeadDim + 32 * (lane >> 4));
+      const uint4 x = kp[0], y = kp[1];
+      const v8i_t kf = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      const float kscale = ksc[t];
+      vsl[j] = vsc[t];
+      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf, kf, zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int r = 0; r < kRowsPerLane; ++r) sc[j][r] = valid ? d[r] * (qmul[r] * kscale) : -__builtin_inff();
+    }
+    // online softmax per head
+    float alpha[GRP];
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; ++r) {
+      float mt = __builtin_fmaxf(__builtin_fmaxf(sc[0][r], sc[1][r]), __builtin_fmaxf(sc[2][r], sc[3][r]));
+      mt = row16_max(mt);
+      // row group q of the lanes holds heads 4q + r
+#pragma unroll
+      for (int q = 0; q < (GRP + 3) / 4; ++q) {
+        const int h = 4 * q + r;
+        if (h < GRP) {
+          const float mnew = __builtin_fmaxf(m_run[h], readlane_f(mt, 16 * q));
+          alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - mnew);
+          m_run[h] = mnew;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerLane; ++r) {
+      const int hl = 4 * tg + r;  // head of this lane's score row r
+      float mh = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < (GRP + 3) / 4; ++q)
+        if (4 * q + r < GRP && tg == q) mh = m_run[4 * q + r];
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = hl < GRP ? __builtin_amdgcn_exp2f(sc[j][r] - mh) : 0.0f;
+        ps += p;
+        if (hl < GRP) L.w[wave][16 * j + (lane & 15)][hl] = p * vsl[j];
+      }
+      ps = row16_sum(ps);
+#pragma unroll
+      for (int q = 0; q < (GRP + 3) / 4; ++q) {
+        const int h = 4 * q + r;
+        if (h < GRP) l_run[h] = l_run[h] * alpha[h] + readlane_f(ps, 16 * q);
+      }
+    }
+    // weighted values: rescale, then this lane's 16 tokens x 8 dims
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] *= alpha[h];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's weights are in LDS
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float f[8];
+      dec8(vb[i], f);
+      const float *wr = L.w[wave][16 * tg + i];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        const float w = wr[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(w, f[e], acc[h][e]);
+      }
+    }
+    asm volatile("" ::: "memory");  // the next tile's weights overwrite these only afterwards
+  }
+
+  // Merge the four token groups of the wave (same dims, lanes l, l^16, l^32, l^48).
+#pragma unroll
+  for (int h = 0; h < GRP; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = acc[h][i];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[h][i] = v;
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) L.acc[wave][h][8 * lane + i] = acc[h][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      L.m[wave][h] = m_run[h];
+      L.l[wave][h] = l_run[h];
+    }
+  }
+  __syncthreads();
+  // Merge the waves: o = sum_w acc_w 2^(m_w - M) / sum_w l_w 2^(m_w - M).
+  for (int idx = threadIdx.x; idx < GRP * kHeadDim; idx += 64 * kAttnWaves) {
+    const int h = idx / kHeadDim, d = idx - h * kHeadDim;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = __builtin_fmaxf(M, L.m[w][h]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float c = __builtin_amdgcn_exp2f(L.m[w][h] - M);
+        num += c * L.acc[w][h][d];
+        den += c * L.l[w][h];
+      }
+    }
+    const float o = den > 0.0f ? num / den : 0.0f;
+    a.out[(b * a.Hq + h0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);  // RNE
+  }
+}
+
+hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
+                                   const uint8_t *vc, const float *vs, const int32_t *len, uint16_t *out,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const AttnArgs a{qq, qs, kc, ks, vc, vs, len, out, Hq, Hkv, S};
+  const dim3 grid((unsigned)((int64_t)B * Hkv)), block(64 * kAttnWaves);
+  switch (Hq / Hkv) {
+    case 1: hipLaunchKernelGGL(attn_decode_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attn_decode_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(attn_decode_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(attn_decode_kernel<8>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

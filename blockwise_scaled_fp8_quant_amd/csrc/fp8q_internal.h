@@ -58,4 +58,15 @@ hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int6
                                       int64_t M_total, int64_t N, int64_t K, uint16_t *y, bool pow2,
                                       hipStream_t stream);
 
+// FP8 KV cache: quantize one new key and value row per sequence and head
+// (1x128 blocks) into [B][H][S][128] caches at token position pos[b].
+hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, uint8_t *kc,
+                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t H, int64_t S, int mode,
+                                  hipStream_t stream);
+
+// Decode attention over the FP8 KV cache (Hq / Hkv in {1, 2, 4, 8}).
+hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
+                                   const uint8_t *vc, const float *vs, const int32_t *len, uint16_t *out,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, hipStream_t stream);
+
 }  // namespace fp8q

@@ -275,6 +275,52 @@ fp8q_status fp8_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_
                                     int32_t G, int64_t M_total, int64_t N, int64_t K,
                                     uint16_t *y, int mode, void *stream);
 
+/*
+ * FP8 KV cache (page 1, "Leistungsgewinne in der Praxis": FP8 for the KV cache
+ * and attention takes the end-to-end gain to about 48%).  The cache holds
+ * every key and value row of one token and one key/value head (head
+ * dimension 128) as one 1x128 block: E4M3 bytes plus one fp32 scale, the
+ * activation rule of fp8_quant_act_1x128.
+ *   k_new, v_new  [B][Hkv][128] bf16 bits (in): the new token's rows
+ *   pos           [B] int32, DEVICE memory: token position of each sequence;
+ *                 a position outside [0, S) stores nothing
+ *   k_cache, v_cache  [B][Hkv][S][128] E4M3 (in/out)
+ *   k_scale, v_scale  [B][Hkv][S] fp32 (in/out)
+ *   mode          fp8q_scale_mode
+ * The stored bytes and scales are exactly fp8_quant_act_1x128 of the rows.
+ */
+fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new,
+                                const int32_t *pos,
+                                uint8_t *k_cache, float *k_scale,
+                                uint8_t *v_cache, float *v_scale,
+                                int32_t B, int32_t Hkv, int64_t S, int mode,
+                                void *stream);
+
+/*
+ * FP8 decode attention over the FP8 KV cache (same passage): one query token
+ * per sequence,
+ *   out[b][h] = sum_t softmax_t(q[b][h] . k[b][g][t] / sqrt(128)) * v[b][g][t]
+ * over t < min(seq_len[b], S), with g = h / (Hq / Hkv) (grouped query heads)
+ * and q, k, v the dequantized rows.
+ *   q_q [B][Hq][128] E4M3, q_s [B][Hq] fp32: the query rows in 1x128 blocks
+ *       (fp8_quant_act_1x128 of q viewed as [B*Hq][128])
+ *   k_cache, k_scale, v_cache, v_scale as for fp8_kv_cache_append
+ *   seq_len [B] int32, DEVICE memory (values outside [0, S] are clamped; a
+ *       sequence with no tokens gives zeros)
+ *   out [B][Hq][128] bf16 bits (out)
+ *   Hq / Hkv must be 1, 2, 4 or 8 (FP8Q_ESHAPE otherwise).
+ * q.k runs on the matrix cores in FP8 (E4M3 x E4M3, fp32 accumulation); the
+ * softmax and the weighted sum of values run in fp32 on exactly decoded
+ * values; out is rounded once to bf16.  Results agree with the exact value
+ * to within fp32 arithmetic and that rounding.
+ */
+fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s,
+                                 const uint8_t *k_cache, const float *k_scale,
+                                 const uint8_t *v_cache, const float *v_scale,
+                                 const int32_t *seq_len, uint16_t *out,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
+                                 void *stream);
+
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);
 

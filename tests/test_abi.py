@@ -31,8 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
-              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
-              "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
+              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_kv_cache_append",
+              "fp8_attention_decode", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
 
@@ -136,6 +136,29 @@ def test_wgrad_argument_errors(lib):
     assert f(GOOD, GOOD, ODD, GOOD, GOOD, 64, 128, 128, None) == 3
     assert f(None, None, None, None, None, 0, 128, 128, None) == 0       # empty call
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, None) == 2
+
+
+def test_kv_cache_append_argument_errors(lib):
+    f = lib.fp8_kv_cache_append
+    #        k_new v_new pos   kc    ks    vc    vs    B  H  S   mode
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 8, 64, 3, None) == 1     # unknown mode
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 8, 64, 0, None) == 1    # negative size
+    assert f(GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, 2, 8, 64, 0, None) == 1     # null positions
+    assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, GOOD, 2, 8, 64, 1, None) == 3      # misaligned
+    assert f(None, None, None, None, None, None, None, 0, 8, 64, 0, None) == 0     # empty call
+
+
+def test_attention_decode_argument_errors(lib):
+    f = lib.fp8_attention_decode
+    #        qq    qs    kc    ks    vc    vs    len   out   B  Hq  Hkv S
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 6, 64, None) == 2    # Hq % Hkv
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 48, 3, 64, None) == 2    # 16 heads per group
+    assert "1, 2, 4 or 8" in _err(lib)
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 0, 64, None) == 2    # Hkv = 0
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 32, 8, 64, None) == 1   # negative size
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 2, 32, 8, 64, None) == 1    # null seq_len
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 2, 32, 8, 64, None) == 3     # misaligned out
+    assert f(None, None, None, None, None, None, None, None, 0, 32, 8, 64, None) == 0    # empty call
 
 
 def test_gather_argument_errors(lib):
