@@ -552,8 +552,24 @@ def attention(fp8q, synth, torch, dev, reps):
     run = lambda: fp8q.fp8_attention_decode(q_q, q_s, cache, dlen, out=out)
     run()
     t = time_loop(run, reps * 5, torch)
+    # the same without a workspace: one workgroup per (sequence, head), unsplit
+    run1 = lambda: fp8q.fp8_attention_decode(q_q, q_s, cache, dlen, out=out, workspace=None)
+    run1()
+    t1 = time_loop(run1, reps * 5, torch)
     kv = int(lens.sum()) * Hkv * 2 * (D + 4)
     nbytes = kv + B * Hq * (D + 4) + B * Hq * D * 2
+    # a small batch (the last sequences of a rollout): 8 sequences give 64
+    # (sequence, head) pairs, too few to fill the GPU; split vs unsplit
+    b8 = 8
+    cache8 = tuple(c[:b8] for c in cache)
+    q8, s8, d8 = q_q[:b8], q_s[:b8], dlen[:b8]
+    out8 = torch.empty((b8, Hq, D), dtype=torch.bfloat16, device=dev)
+    r8 = lambda: fp8q.fp8_attention_decode(q8, s8, cache8, d8, out=out8)
+    r8u = lambda: fp8q.fp8_attention_decode(q8, s8, cache8, d8, out=out8, workspace=None)
+    r8()
+    r8u()
+    t8, t8u = time_loop(r8, reps * 5, torch), time_loop(r8u, reps * 5, torch)
+    nb8 = int(lens[:b8].sum()) * Hkv * 2 * (D + 4) + b8 * Hq * (D + 4) + b8 * Hq * D * 2
     # the cache append of one decode step (one key and value row per sequence and head)
     kn = torch.randn((B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
     vn = torch.randn((B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
@@ -565,8 +581,13 @@ def attention(fp8q, synth, torch, dev, reps):
            "mean_len": float(lens.mean()), "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
            "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
            "kv_bytes_fp8": kv, "kv_bytes_bf16_equivalent": int(lens.sum()) * Hkv * 2 * D * 2,
-           "append_us": round(t_app * 1e6, 2)}
-    log(f"attention decode {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s; cache append {t_app * 1e6:.1f} us")
+           "append_us": round(t_app * 1e6, 2),
+           "unsplit_us": round(t1 * 1e6, 2), "unsplit_gbs": round(nbytes / t1 / 1e9, 1),
+           "batch8": {"split_us": round(t8 * 1e6, 2), "split_gbs": round(nb8 / t8 / 1e9, 1),
+                      "unsplit_us": round(t8u * 1e6, 2), "unsplit_gbs": round(nb8 / t8u / 1e9, 1)}}
+    log(f"attention decode {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s (unsplit {t1 * 1e6:.1f} us); "
+        f"8 sequences: split {t8 * 1e6:.1f} us ({nb8 / t8 / 1e9:.0f} GB/s), unsplit {t8u * 1e6:.1f} us; "
+        f"cache append {t_app * 1e6:.1f} us")
     del kq, vq, ks, vs, cache
     torch.cuda.empty_cache()
     return res

@@ -27,7 +27,8 @@ __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
            "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
-           "fp8_kv_cache_append", "fp8_attention_decode", "abi_version", "library_path"]
+           "fp8_kv_cache_append", "fp8_attention_decode", "fp8_attention_decode_workspace_size",
+           "abi_version", "library_path"]
 
 
 def library_path():
@@ -322,10 +323,16 @@ def fp8_kv_cache_append(k_new, v_new, pos, cache, mode="amax"):
     return cache
 
 
-def fp8_attention_decode(q_q, q_s, cache, seq_len, out=None):
+def fp8_attention_decode_workspace_size(B, Hq, Hkv, S):
+    return _lib.load().fp8_attention_decode_workspace_size(B, Hq, Hkv, S)
+
+
+def fp8_attention_decode(q_q, q_s, cache, seq_len, out=None, workspace="auto"):
     """Decode attention of one query token per sequence over the FP8 cache.
     q_q uint8 [B, Hq, 128] and q_s f32 [B, Hq] (the query rows in 1x128
     blocks), cache as for fp8_kv_cache_append, seq_len int32 [B] (device).
+    workspace: a device tensor of at least fp8_attention_decode_workspace_size
+    bytes, "auto" (allocated here), or None (no splitting of sequences).
     Returns bf16 [B, Hq, 128]."""
     kq, ks, vq, vs = cache
     q_q, pq = _as_bytes(q_q, "q_q", 3)
@@ -347,7 +354,16 @@ def fp8_attention_decode(q_q, q_s, cache, seq_len, out=None):
     py = _dev(y, "out", torch.bfloat16, 3)
     if tuple(y.shape) != (B, Hq, 128):
         raise ValueError("output shape does not match")
+    need = fp8_attention_decode_workspace_size(B, Hq, Hkv, S)
+    if isinstance(workspace, str) and workspace == "auto":
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_q.device) if need else None
+    if workspace is None:
+        pws, nws = None, 0
+    else:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        pws, nws = ctypes.c_void_p(int(workspace.data_ptr())), workspace.numel() * workspace.element_size()
     _lib.check("fp8_attention_decode",
-               _lib.load().fp8_attention_decode(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S,
+               _lib.load().fp8_attention_decode(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S, pws, nws,
                                                 _stream(q_q)))
     return y

@@ -16,7 +16,7 @@ ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blocksca
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
                 "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_kv_cache_append",
-                "fp8_attention_decode",
+                "fp8_attention_decode", "fp8_attention_decode_workspace_size",
                 "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version")
 
 _lib = None
@@ -58,8 +58,10 @@ def load():
     lib.fp8_grouped_gemm_gather.restype = ci
     lib.fp8_kv_cache_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i64, ci, p]
     lib.fp8_kv_cache_append.restype = ci
-    lib.fp8_attention_decode.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p]
+    lib.fp8_attention_decode.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p, i64, p]
     lib.fp8_attention_decode.restype = ci
+    lib.fp8_attention_decode_workspace_size.argtypes = [i32, i32, i32, i64]
+    lib.fp8_attention_decode_workspace_size.restype = i64
     lib.fp8q_status_string.argtypes = [ci]
     lib.fp8q_status_string.restype = ctypes.c_char_p
     lib.fp8q_last_error.argtypes = []

@@ -304,10 +304,17 @@ fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, co
                   __func__);
 }
 
+int64_t fp8_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int64_t S) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || S < 0) return 0;
+  int64_t nch, ct;
+  fp8q::attention_decode_split((int64_t)B * Hkv, S, nch, ct);
+  return nch <= 1 ? 0 : (int64_t)B * Hq * nch * (128 + 2) * (int64_t)sizeof(float);
+}
+
 fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uint8_t *k_cache,
                                  const float *k_scale, const uint8_t *v_cache, const float *v_scale,
                                  const int32_t *seq_len, uint16_t *out, int32_t B, int32_t Hq, int32_t Hkv,
-                                 int64_t S, void *stream) {
+                                 int64_t S, void *workspace, int64_t workspace_bytes, void *stream) {
   g_last_error.clear();
   FP8Q_REQUIRE(B >= 0 && Hq >= 0 && Hkv >= 0 && S >= 0, FP8Q_EINVAL, "negative size");
   FP8Q_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, FP8Q_ESHAPE, "Hq must be a positive multiple of Hkv");
@@ -317,12 +324,15 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uin
   FP8Q_REQUIRE(q_q && q_s && k_cache && k_scale && v_cache && v_scale && seq_len && out, FP8Q_EINVAL,
                "null pointer");
   FP8Q_REQUIRE(aligned16(q_q) && aligned16(q_s) && aligned16(k_cache) && aligned16(k_scale) &&
-                   aligned16(v_cache) && aligned16(v_scale) && aligned16(seq_len) && aligned16(out),
+                   aligned16(v_cache) && aligned16(v_scale) && aligned16(seq_len) && aligned16(out) &&
+                   aligned16(workspace),
                FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  FP8Q_REQUIRE(workspace == nullptr || workspace_bytes >= fp8_attention_decode_workspace_size(B, Hq, Hkv, S),
+               FP8Q_EINVAL, "workspace smaller than fp8_attention_decode_workspace_size()");
   fp8q_status st = check_device(__func__);
   if (st != FP8Q_OK) return st;
   return launched(fp8q::launch_attention_decode(q_q, q_s, k_cache, k_scale, v_cache, v_scale, seq_len, out, B, Hq,
-                                                Hkv, S, (hipStream_t)stream),
+                                                Hkv, S, static_cast<float *>(workspace), (hipStream_t)stream),
                   __func__);
 }
 

@@ -72,9 +72,15 @@ hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, 
 //   o[b][h] = sum_t softmax_t(q[b][h] . k[b][g][t] / sqrt(128)) v[b][g][t],
 // g = h / GRP (GRP query heads share a key/value head), t < min(len[b], S).
 //
-// One workgroup per (sequence, key/value head); its four waves take the
-// 64-token tiles of the sequence in turn and keep their own running maximum,
-// sum and output, merged through LDS at the end.
+// One workgroup per (sequence, key/value head, chunk of the sequence); its
+// four waves take the 64-token tiles of the chunk in turn and keep their own
+// running maximum, sum and output, merged through LDS at the end.  When the
+// (sequence, head) pairs alone cannot fill the chip (fewer than kFillWgs) and
+// a workspace is given, sequences are cut into chunks: each workgroup writes
+// its chunk's maximum, sum and unnormalized output, and a second kernel
+// merges the chunks of each sequence.  Otherwise one chunk is the whole
+// sequence (measured: splitting a batch that already fills the chip only
+// adds per-workgroup cost).
 //  - Scores: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens, E4M3 x
 //    E4M3, with the GRP query rows as the A operand (rows of D, padded to 16
 //    with zeros) and 16 key rows, read straight from the cache, as B.  Lane l
@@ -90,6 +96,8 @@ hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, 
 // ---------------------------------------------------------------------------
 constexpr int kAttnWaves = 4;
 constexpr int kTileTok = 64;
+constexpr int64_t kFillWgs = 512;  // workgroups that fill MI355X (256 CUs, two resident each)
+constexpr int kMinChunkTiles = 4;  // at least one tile per wave
 
 struct AttnArgs {
   const uint8_t *qq;
@@ -100,8 +108,12 @@ struct AttnArgs {
   const float *vs;
   const int32_t *len;
   uint16_t *out;
+  float *ws_o;    // chunked: [B][Hq][nch][128] unnormalized outputs of each chunk
+  float *ws_ml;   // chunked: [B][Hq][nch][2] maximum (base 2) and sum of each chunk
   int32_t Hq, Hkv;
   int64_t S;
+  int32_t nch;    // chunks per sequence (1: the whole sequence)
+  int32_t chunk_tiles;  // 64-token tiles per chunk (chunked)
 };
 
 template <int kCtrl>
@@ -148,18 +160,23 @@ struct AttnLds {
   float acc[kAttnWaves][GRP][kHeadDim];
 };
 
-template <int GRP>
+template <int GRP, bool kChunked>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a) {
   static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "query heads per key/value head");
   constexpr int kRowsPerLane = 4;  // MFMA output rows (heads) per lane
   __shared__ AttnLds<GRP> L;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t bg = blockIdx.x;  // b * Hkv + g
+  const int64_t bg = blockIdx.x / a.nch;  // b * Hkv + g
+  const int chunk = (int)(blockIdx.x - bg * a.nch);
   const int64_t b = bg / a.Hkv, g = bg - b * a.Hkv;
   int64_t len = a.len[b];
   len = len < 0 ? 0 : (len > a.S ? a.S : len);
   const int ntiles = (int)((len + kTileTok - 1) / kTileTok);
+  const int tile_begin = kChunked ? chunk * a.chunk_tiles : 0;
+  const int tile_end = kChunked ? (ntiles < tile_begin + a.chunk_tiles ? ntiles : tile_begin + a.chunk_tiles) : ntiles;
+  if (kChunked && tile_begin >= ntiles) return;  // past the sequence: the merge skips this chunk
+
   const int64_t h0 = g * GRP;  // first query head of the group
 
   // Query rows as the A operand: lane l gives row l%16 (head h0 + l%16, zero
@@ -199,8 +216,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
 
   const int tg = lane >> 4;  // token group of the value pass
   const int dq = lane & 15;  // 8-dim slice of the value pass
-  for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kAttnWaves) {
     const int64_t t0 = (int64_t)tile * kTileTok;
+    // the tile's 64 key and value scales, one per lane (one load instruction
+    // each; a vector-memory instruction costs the same whatever its width)
+    int64_t ts = t0 + lane;
+    ts = ts < len ? ts : len - 1;
+    const float ks_l = ksc[ts], vs_l = vsc[ts];
     // value rows of this lane (issued first: not needed until after the softmax)
     uint2 vb[16];
     float vsl[4];
@@ -220,8 +242,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
       const uint4 *kp = reinterpret_cast<const uint4 *>(kc + t * kHeadDim + 32 * (lane >> 4));
       const uint4 x = kp[0], y = kp[1];
       const v8i_t kf = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-      const float kscale = ksc[t];
-      vsl[j] = vsc[t];
+      const float kscale = __shfl(ks_l, 16 * j + (lane & 15));
+      vsl[j] = __shfl(vs_l, 16 * j + (lane & 15));
       const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf, kf, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
@@ -325,24 +347,93 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
         den += c * L.l[w][h];
       }
     }
-    const float o = den > 0.0f ? num / den : 0.0f;
-    a.out[(b * a.Hq + h0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);  // RNE
+    if constexpr (kChunked) {
+      const int64_t row = (b * a.Hq + h0 + h) * a.nch + chunk;
+      a.ws_o[row * kHeadDim + d] = num;
+      if (d == 0) {
+        a.ws_ml[2 * row] = M;
+        a.ws_ml[2 * row + 1] = den;
+      }
+    } else {
+      const float o = den > 0.0f ? num / den : 0.0f;
+      a.out[(b * a.Hq + h0 + h) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);  // RNE
+    }
   }
+}
+
+// Merge of the chunks of each (sequence, query head): one 128-lane workgroup,
+// lane d of the head dimension.  Chunks at or past the sequence's length were
+// not written and are skipped.
+__global__ __launch_bounds__(kHeadDim) void attn_merge_kernel(AttnArgs a) {
+  const int64_t bh = blockIdx.x;  // b * Hq + h
+  const int64_t b = bh / a.Hq;
+  const int d = threadIdx.x;
+  int64_t len = a.len[b];
+  len = len < 0 ? 0 : (len > a.S ? a.S : len);
+  const int64_t chunk_tok = (int64_t)a.chunk_tiles * kTileTok;
+  const int nvalid = (int)((len + chunk_tok - 1) / chunk_tok);
+  const float *ml = a.ws_ml + bh * a.nch * 2;
+  const float *o = a.ws_o + bh * a.nch * kHeadDim;
+  float M = -__builtin_inff();
+  for (int c = 0; c < nvalid; ++c) M = __builtin_fmaxf(M, ml[2 * c]);
+  float num = 0.0f, den = 0.0f;
+  if (M != -__builtin_inff()) {
+    for (int c = 0; c < nvalid; ++c) {
+      const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+      num += w * o[c * kHeadDim + d];
+      den += w * ml[2 * c + 1];
+    }
+  }
+  const float r = den > 0.0f ? num / den : 0.0f;
+  a.out[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)r);  // RNE
+}
+
+// Chunks per sequence and tiles per chunk for B*Hkv (sequence, head) pairs and
+// a cache of S tokens: enough chunks to give about kFillWgs workgroups, each
+// chunk at least kMinChunkTiles tiles.  A function of the sizes only, so the
+// workspace a call needs is known on the host.
+void attention_decode_split(int64_t pairs, int64_t S, int64_t &nch, int64_t &chunk_tiles) {
+  const int64_t tiles = (S + kTileTok - 1) / kTileTok;
+  nch = 1;
+  chunk_tiles = tiles;
+  if (pairs <= 0 || pairs >= kFillWgs || tiles <= kMinChunkTiles) return;
+  int64_t want = (kFillWgs + pairs - 1) / pairs;
+  int64_t ct = (tiles + want - 1) / want;
+  ct = ct < kMinChunkTiles ? kMinChunkTiles : ct;
+  nch = (tiles + ct - 1) / ct;
+  chunk_tiles = ct;
+}
+
+template <bool kChunked>
+static hipError_t launch_decode(const AttnArgs &a, int64_t B, hipStream_t stream) {
+  const dim3 grid((unsigned)(B * a.Hkv * a.nch)), block(64 * kAttnWaves);
+  switch (a.Hq / a.Hkv) {
+    case 1: hipLaunchKernelGGL((attn_decode_kernel<1, kChunked>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_decode_kernel<2, kChunked>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<4, kChunked>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_decode_kernel<8, kChunked>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
                                    const uint8_t *vc, const float *vs, const int32_t *len, uint16_t *out,
-                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, hipStream_t stream) {
+                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, float *workspace,
+                                   hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const AttnArgs a{qq, qs, kc, ks, vc, vs, len, out, Hq, Hkv, S};
-  const dim3 grid((unsigned)((int64_t)B * Hkv)), block(64 * kAttnWaves);
-  switch (Hq / Hkv) {
-    case 1: hipLaunchKernelGGL(attn_decode_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attn_decode_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(attn_decode_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(attn_decode_kernel<8>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  int64_t nch, ct;
+  attention_decode_split((int64_t)B * Hkv, S, nch, ct);
+  if (workspace == nullptr || nch <= 1) {
+    const AttnArgs a{qq, qs, kc, ks, vc, vs, len, out, nullptr, nullptr, Hq, Hkv, S, 1, 0};
+    return launch_decode<false>(a, B, stream);
   }
+  float *ws_o = workspace;
+  float *ws_ml = workspace + (int64_t)B * Hq * nch * kHeadDim;
+  const AttnArgs a{qq, qs, kc, ks, vc, vs, len, out, ws_o, ws_ml, Hq, Hkv, S, (int32_t)nch, (int32_t)ct};
+  hipError_t e = launch_decode<true>(a, B, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)B * Hq)), dim3(kHeadDim), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,9 +64,14 @@ hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, 
                                   float *ks, uint8_t *vc, float *vs, int32_t B, int32_t H, int64_t S, int mode,
                                   hipStream_t stream);
 
-// Decode attention over the FP8 KV cache (Hq / Hkv in {1, 2, 4, 8}).
+// Decode attention over the FP8 KV cache (Hq / Hkv in {1, 2, 4, 8}).  With a
+// workspace of B*Hq*nch*130 floats (nch from attention_decode_split) and
+// nch > 1, sequences are split into chunks merged by a second kernel;
+// otherwise one workgroup covers a whole sequence.
+void attention_decode_split(int64_t pairs, int64_t S, int64_t &nch, int64_t &chunk_tiles);
 hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
                                    const uint8_t *vc, const float *vs, const int32_t *len, uint16_t *out,
-                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, hipStream_t stream);
+                                   int32_t B, int32_t Hq, int32_t Hkv, int64_t S, float *workspace,
+                                   hipStream_t stream);
 
 }  // namespace fp8q

@@ -309,6 +309,7 @@ fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new,
  *       sequence with no tokens gives zeros)
  *   out [B][Hq][128] bf16 bits (out)
  *   Hq / Hkv must be 1, 2, 4 or 8 (FP8Q_ESHAPE otherwise).
+ *   workspace, workspace_bytes: see fp8_attention_decode_workspace_size
  * q.k runs on the matrix cores in FP8 (E4M3 x E4M3, fp32 accumulation); the
  * softmax and the weighted sum of values run in fp32 on exactly decoded
  * values; out is rounded once to bf16.  Results agree with the exact value
@@ -319,7 +320,17 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s,
                                  const uint8_t *v_cache, const float *v_scale,
                                  const int32_t *seq_len, uint16_t *out,
                                  int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
+                                 void *workspace, int64_t workspace_bytes,
                                  void *stream);
+
+/* Bytes of DEVICE workspace fp8_attention_decode needs to split sequences
+ * into chunks that run in parallel when B*Hkv (sequence, head) pairs are too
+ * few to fill the GPU (fewer than 512); 0 when no split is needed or for
+ * invalid sizes.  A function of the sizes only.  With workspace == NULL the
+ * call still works: one workgroup then covers a whole sequence.  A workspace
+ * smaller than this size is FP8Q_EINVAL.  Its contents need no
+ * initialisation; concurrent calls need their own. */
+int64_t fp8_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int64_t S);
 
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);

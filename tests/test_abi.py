@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
               "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_kv_cache_append",
-              "fp8_attention_decode", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
+              "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
 
@@ -150,15 +150,23 @@ def test_kv_cache_append_argument_errors(lib):
 
 def test_attention_decode_argument_errors(lib):
     f = lib.fp8_attention_decode
-    #        qq    qs    kc    ks    vc    vs    len   out   B  Hq  Hkv S
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 6, 64, None) == 2    # Hq % Hkv
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 48, 3, 64, None) == 2    # 16 heads per group
+    #        qq    qs    kc    ks    vc    vs    len   out   B  Hq  Hkv S   ws  bytes
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 6, 64, None, 0, None) == 2    # Hq % Hkv
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 48, 3, 64, None, 0, None) == 2    # 16 per group
     assert "1, 2, 4 or 8" in _err(lib)
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 0, 64, None) == 2    # Hkv = 0
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 32, 8, 64, None) == 1   # negative size
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 2, 32, 8, 64, None) == 1    # null seq_len
-    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 2, 32, 8, 64, None) == 3     # misaligned out
-    assert f(None, None, None, None, None, None, None, None, 0, 32, 8, 64, None) == 0    # empty call
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 0, 64, None, 0, None) == 2    # Hkv = 0
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 32, 8, 64, None, 0, None) == 1   # negative size
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 2, 32, 8, 64, None, 0, None) == 1    # null seq_len
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 2, 32, 8, 64, None, 0, None) == 3     # misaligned out
+    # 16 (sequence, head) pairs: 32 chunks of two tiles would be wanted, at
+    # least four tiles each -> 16 chunks of 4 tiles for 4096 tokens
+    need = lib.fp8_attention_decode_workspace_size(2, 32, 8, 4096)
+    assert need == 2 * 32 * 16 * 130 * 4
+    assert lib.fp8_attention_decode_workspace_size(64, 32, 8, 8192) == 0    # 512 pairs fill the GPU
+    assert lib.fp8_attention_decode_workspace_size(2, 32, 8, 256) == 0      # four tiles: one chunk
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 8, 4096, GOOD, need - 4, None) == 1
+    assert "workspace" in _err(lib)
+    assert f(None, None, None, None, None, None, None, None, 0, 32, 8, 64, None, 0, None) == 0    # empty call
 
 
 def test_gather_argument_errors(lib):

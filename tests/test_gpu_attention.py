@@ -42,10 +42,11 @@ def _query(B, Hq, seed, std=1.0, mode=0):
     return qq.reshape(B, Hq, D), qs.reshape(B, Hq)
 
 
-def _run(qq, qs, cache, seq_len):
+def _run(qq, qs, cache, seq_len, workspace="auto"):
     fp8q = lib()
     dcache = tuple(_dev(c) for c in cache)
-    y = fp8q.fp8_attention_decode(_dev(qq), _dev(qs), dcache, _dev(np.asarray(seq_len, np.int32)))
+    y = fp8q.fp8_attention_decode(_dev(qq), _dev(qs), dcache, _dev(np.asarray(seq_len, np.int32)),
+                                  workspace=workspace)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
@@ -94,6 +95,22 @@ def test_decode_ragged_lengths(grp):
     ref = oracle.attention_decode_f64(qq, qs, *cache, lens)
     assert not y[0].any(), "a sequence with no tokens gives zeros"
     gemm_tolerance_check(y, ref, f"decode grp={grp}")
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_chunk_edges(split):
+    """14 (sequence, head) pairs: with a workspace the 3000-token cache is cut
+    into 12 chunks of 256 tokens; lengths at and around tile and chunk edges,
+    with and without the split, against the oracle."""
+    require_gpu()
+    B, Hkv, Hq, S = 7, 2, 8, 3000
+    lens = np.array([0, 1, 255, 256, 257, 2500, 3000], dtype=np.int32)
+    cache = _cache(B, Hkv, S, seed=41)
+    qq, qs = _query(B, Hq, seed=41)
+    say("attention chunk edges", split)
+    y = _run(qq, qs, cache, lens, workspace="auto" if split else None)
+    gemm_tolerance_check(y, oracle.attention_decode_f64(qq, qs, *cache, lens), f"chunk edges split={split}")
+    assert not y[0].any()
 
 
 def test_decode_peaked_and_flat_scores():
