@@ -464,6 +464,15 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
         wg = lambda: fp8q.fp8_blockscaled_gemm_wgrad(gtq, gts, xtq, xts, out=dw)
         for f in (qg, qx, qw, dg, wg):
             f()
+        # power-of-two scales: the same operands quantized in pow2 mode, the
+        # weight gradient with both per-row scales on the matrix cores
+        gtq2, gts2, xtq2, xts2 = (torch.empty_like(t) for t in (gtq, gts, xtq, xts))
+        fp8q.fp8_quant_act_dual(g, mode="pow2", rowwise=False, out=(None, None, gtq2, gts2))
+        fp8q.fp8_quant_act_dual(l["x"], mode="pow2", rowwise=False, out=(None, None, xtq2, xts2))
+        wg2 = lambda: fp8q.fp8_blockscaled_gemm_wgrad_pow2(gtq2, gts2, xtq2, xts2, out=dw)
+        wg2()
+        t_wg2 = time_loop(wg2, reps, torch)
+        del gtq2, gts2, xtq2, xts2
         t_qg, t_qx, t_qw = (time_loop(f, reps, torch) for f in (qg, qx, qw))
         t_dg, t_wg = time_loop(dg, reps, torch), time_loop(wg, reps, torch)
         f_dg, f_wg = 2.0 * M * N * K, 2.0 * N * K * Mp
@@ -473,12 +482,13 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
         out[l["name"]] = {
             "dgrad_tflops": round(f_dg / t_dg / 1e12, 1), "wgrad_tflops": round(f_wg / t_wg / 1e12, 1),
             "dgrad_us": round(t_dg * 1e6, 2), "wgrad_us": round(t_wg * 1e6, 2),
+            "wgrad_pow2_tflops": round(f_wg / t_wg2 / 1e12, 1),
             "quant_dy_dual_gbs": round(b_qg / t_qg / 1e9, 1), "quant_x_colwise_gbs": round(b_qx / t_qx / 1e9, 1),
             "quant_w_dual_gbs": round(b_qw / t_qw / 1e9, 1),
             "quant_dy_us": round(t_qg * 1e6, 2), "quant_x_us": round(t_qx * 1e6, 2),
             "quant_w_us": round(t_qw * 1e6, 2)}
         log(f"backward {l['name']}: dgrad {f_dg / t_dg / 1e12:.1f} TFLOP/s, wgrad {f_wg / t_wg / 1e12:.1f} "
-            f"TFLOP/s, dY dual {b_qg / t_qg / 1e9:.0f} GB/s, X colwise {b_qx / t_qx / 1e9:.0f} GB/s, "
+            f"TFLOP/s (pow2 {f_wg / t_wg2 / 1e12:.1f}), dY dual {b_qg / t_qg / 1e9:.0f} GB/s, X colwise {b_qx / t_qx / 1e9:.0f} GB/s, "
             f"W dual {b_qw / t_qw / 1e9:.0f} GB/s")
         tot["dgrad_s"] += t_dg
         tot["wgrad_s"] += t_wg

@@ -27,6 +27,7 @@ __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
            "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
+           "fp8_blockscaled_gemm_wgrad_pow2",
            "fp8_kv_cache_append", "fp8_attention_decode", "fp8_attention_decode_workspace_size",
            "abi_version", "library_path"]
 
@@ -276,7 +277,14 @@ def fp8_quant_weight_128x128_dual(w, mode="amax", rowwise=True, out=None):
     return _dual("fp8_quant_weight_128x128_dual", w, True, mode, rowwise, out)
 
 
-def fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out=None):
+def fp8_blockscaled_gemm_wgrad_pow2(a_q, a_s, b_q, b_s, out=None):
+    """As fp8_blockscaled_gemm_wgrad, for scales that are all powers of two
+    (the matrix cores apply them); an output that depends on any other scale
+    is NaN."""
+    return fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out, _fn="fp8_blockscaled_gemm_wgrad_pow2")
+
+
+def fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out=None, _fn="fp8_blockscaled_gemm_wgrad"):
     """Y [M, N] bf16 = dequant(a_q, a_s) @ dequant(b_q, b_s)^T with 1x128 scale
     blocks on both operands: a_s [M, K/128], b_s [N, K/128].  The weight
     gradient dW = dY^T X from the transposed outputs of fp8_quant_act_dual."""
@@ -292,8 +300,7 @@ def fp8_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, out=None):
     py = _dev(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("output shape does not match")
-    _lib.check("fp8_blockscaled_gemm_wgrad",
-               _lib.load().fp8_blockscaled_gemm_wgrad(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
+    _lib.check(_fn, getattr(_lib.load(), _fn)(pa, pas, pb, pbs, py, M, N, K, _stream(a_q)))
     return y
 
 

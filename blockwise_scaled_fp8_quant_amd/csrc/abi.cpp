@@ -171,7 +171,7 @@ fp8q_status gemm_quant_entry(const char *fn, const uint8_t *a_q, const float *a_
 }
 
 fp8q_status wgrad_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
-                        const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K, void *stream) {
+                        const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2, void *stream) {
   g_last_error.clear();
   if (!(M >= 0 && N >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
   if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
@@ -184,7 +184,8 @@ fp8q_status wgrad_entry(const char *fn, const uint8_t *a_q, const float *a_s, co
     return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
   fp8q_status st = check_device(fn);
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, y, M, N, K, (hipStream_t)stream), fn);
+  return launched(fp8q::launch_blockscaled_gemm_wgrad(a_q, a_s, b_q, b_s, y, M, N, K, pow2, (hipStream_t)stream),
+                  fn);
 }
 
 fp8q_status grouped_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
@@ -263,7 +264,13 @@ fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s, con
 fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
                                        const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
                                        void *stream) {
-  return wgrad_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, stream);
+  return wgrad_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, false, stream);
+}
+
+fp8q_status fp8_blockscaled_gemm_wgrad_pow2(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                            const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                            void *stream) {
+  return wgrad_entry(__func__, a_q, a_s, b_q, b_s, y, M, N, K, true, stream);
 }
 
 fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,

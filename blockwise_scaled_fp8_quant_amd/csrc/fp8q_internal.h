@@ -40,7 +40,7 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
 // gradient from 128-token column blocks of dY and X).
 hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
                                          const uint8_t *b_q, const float *b_s,
-                                         uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                         uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2,
                                          hipStream_t stream);
 
 // Row-major and transposed codes of x [M][K] in one pass.  tile: one scale per

@@ -67,7 +67,7 @@ struct Variant {
   static constexpr bool kGather = kGather_;
   static constexpr bool kBRow = kBRow_;
   static_assert(!(kGather && !kGrouped), "gathered rows belong to groups");
-  static_assert(!(kBRow && (kPow2 || kGrouped)), "per-row weight-side scales: dense, VALU fold");
+  static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
 
 template <int kBM_, int kWaves_, int kStages_, int kLoaders_>
@@ -213,7 +213,12 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
   for (int par = 0; par < 2; ++par) d.rc[par] = row * K + ((c0 ^ par) << 4);
   const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
   d.sa = (uint32_t)sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane) * (uint32_t)t.KB * 4u;
-  d.sb = (uint32_t)(V::kBRow ? lane : (lane & 1)) * (uint32_t)t.KB * 4u;
+  // Weight-side scales.  Tile scales: rows of the two 128-row blocks (lanes
+  // 0..1).  Per-row scales, VALU fold: row order (lane of each 64).  Per-row
+  // power-of-two scales: LDS slot 128w + 8c + i holds row 128w + 16i + c, so
+  // that a lane reads the rows it supplies to the eight MFMA sub-tiles with
+  // two 16-byte reads; loader j fills slots 64j .. 64j+63.
+  d.sb = (uint32_t)(!V::kBRow ? (lane & 1) : (V::kPow2 ? (lane & 7) * 16 + (lane >> 3) : lane)) * (uint32_t)t.KB * 4u;
   if constexpr (kGather) {
     static_assert(C::kPiecesA <= kMaxPiecesA, "gather offsets per lane");
     auto src = [&](int r) -> int64_t {  // source token row of tile row r, or -1
@@ -287,13 +292,15 @@ __device__ __forceinline__ void issue_scales(const TileJob &t, const TileRsrc &r
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
                                              (V::kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
   if constexpr (V::kBRow) {
-    // rows 64j .. 64j+63 of the weight-side scales, in row order
+    // LDS slots 64j .. 64j+63 of the weight-side scales (row order, or the
+    // power-of-two layout described at dma_lane)
 #pragma unroll
-    for (int j = 0; j < kBN / 64; ++j)
+    for (int j = 0; j < kBN / 64; ++j) {
+      const int row0 = V::kPow2 ? (j >> 1) * 128 + (j & 1) * 8 : j * 64;
       if ((C::kScaleLoaders + j) % C::kLoaders == l)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + j * 256), 4,
-                                                 d.sb + (uint32_t)(j * 64 * t.KB * 4) + (uint32_t)k * 4u, 0, 0,
-                                                 0);
+                                                 d.sb + (uint32_t)(row0 * t.KB * 4) + (uint32_t)k * 4u, 0, 0, 0);
+    }
   } else if (l == 0 && lane < 2)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
                                              0, 0, 0);
@@ -353,6 +360,9 @@ struct BlockFrags {
   // the weight block's), and which of them (bit mi; bit 4: the weight
   // block's) was, in some K block so far, not a power of two in [2^-126, 2^127]
   uint32_t ea, eb;
+  // per-row power-of-two weight-side scales: this lane's row of sub-tile ni
+  // in byte ni%4 of ebr[ni/4]; a bad one sets bit 16+ni of bad
+  uint32_t ebr[2];
   uint32_t bad;
 };
 
@@ -379,7 +389,16 @@ __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn,
   if constexpr (kPow2) {
     f.ea = e8m0_of(sa4.x, f.bad, 1u) | (e8m0_of(sa4.y, f.bad, 2u) << 8) | (e8m0_of(sa4.z, f.bad, 4u) << 16) |
            (e8m0_of(sa4.w, f.bad, 8u) << 24);
-    f.eb = e8m0_of(sb, f.bad, 16u);
+    if constexpr (V::kBRow) {
+      const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
+      const float4 lo = rp[0], hi = rp[1];
+      f.ebr[0] = e8m0_of(lo.x, f.bad, 1u << 16) | (e8m0_of(lo.y, f.bad, 1u << 17) << 8) |
+                 (e8m0_of(lo.z, f.bad, 1u << 18) << 16) | (e8m0_of(lo.w, f.bad, 1u << 19) << 24);
+      f.ebr[1] = e8m0_of(hi.x, f.bad, 1u << 20) | (e8m0_of(hi.y, f.bad, 1u << 21) << 8) |
+                 (e8m0_of(hi.z, f.bad, 1u << 22) << 16) | (e8m0_of(hi.w, f.bad, 1u << 23) << 24);
+    } else {
+      f.eb = e8m0_of(sb, f.bad, 16u);
+    }
   } else if constexpr (V::kBRow) {
     // the weight-side scale differs between a lane's four outputs: the folds
     // multiply it in
@@ -413,6 +432,24 @@ constexpr int kMfmaPerBlock = kSubN * kSubM;
 template <int kSel>
 __device__ __forceinline__ v4f mfma_pow2_sel(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)eb, kSel, (int)ea);
+}
+
+// acc + A*B with per-row E8M0 scales on A as well: byte selA of the lane's
+// eb is the scale of the A row it supplies.
+template <int kSelA, int kSelB>
+__device__ __forceinline__ v4f mfma_pow2_ab(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, kSelA, (int)eb, kSelB, (int)ea);
+}
+
+template <int kSelA>
+__device__ __forceinline__ v4f mfma_pow2_rows(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea,
+                                              int selb) {
+  switch (selb) {
+    case 0: return mfma_pow2_ab<kSelA, 0>(a, b, c, eb, ea);
+    case 1: return mfma_pow2_ab<kSelA, 1>(a, b, c, eb, ea);
+    case 2: return mfma_pow2_ab<kSelA, 2>(a, b, c, eb, ea);
+    default: return mfma_pow2_ab<kSelA, 3>(a, b, c, eb, ea);
+  }
 }
 
 __device__ __forceinline__ v4f mfma_pow2(const v8i &a, const v8i &b, const v4f &c, uint32_t eb, uint32_t ea,
@@ -477,7 +514,17 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kPow2) {
-      acc[ni][mi] = mfma_pow2(wf[ni % R], f.xf[mi], acc[ni][mi], f.eb, f.ea, mi);
+      if constexpr (V::kBRow) {
+        const uint32_t eb = f.ebr[ni >> 2];
+        switch (ni & 3) {
+          case 0: acc[ni][mi] = mfma_pow2_rows<0>(wf[ni % R], f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+          case 1: acc[ni][mi] = mfma_pow2_rows<1>(wf[ni % R], f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+          case 2: acc[ni][mi] = mfma_pow2_rows<2>(wf[ni % R], f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+          default: acc[ni][mi] = mfma_pow2_rows<3>(wf[ni % R], f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+        }
+      } else {
+        acc[ni][mi] = mfma_pow2(wf[ni % R], f.xf[mi], acc[ni][mi], f.eb, f.ea, mi);
+      }
       continue;
     }
     p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni % R], f.xf[mi], zero, 0, 0, 0, 127, 0,
@@ -627,7 +674,28 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   // A scale outside the power-of-two contract turns the outputs that depend
   // on it into NaN rather than into a silently wrong product.
-  if (kPow2 && f.bad) {
+  if constexpr (kPow2 && V::kBRow) {
+    // A bad weight-side row scale is seen by the lanes that supply that row
+    // (lane % 16 of its sub-tile); the row's outputs sit in other lanes
+    // (rows 4*(lane/16) .. +3), so its bit is shared with a ballot.
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int ni = 0; ni < kSubN; ++ni) {
+      const uint64_t rb = __ballot((f.bad >> (16 + ni)) & 1u);
+      if (rb != 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((rb >> (4 * (lane >> 4) + r)) & 1u)
+#pragma unroll
+            for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi][r] = nan;
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi)
+      if (f.bad & (1u << mi))
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
+  } else if (kPow2 && f.bad) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi)
@@ -918,9 +986,10 @@ hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
 
 hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
                                          const uint8_t *b_q, const float *b_s,
-                                         uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                         uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2,
                                          hipStream_t stream) {
-  return dense<false, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream);
+  return pow2 ? dense<true, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream)
+              : dense<false, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,

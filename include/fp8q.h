@@ -200,6 +200,19 @@ fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
                                        void *stream);
 
 /*
+ * The same product for scales that are all powers of two (FP8Q_SCALE_POW2
+ * quantization; page 1, "Warum dies fuer die KI-Oekonomie wichtig ist"): the
+ * matrix cores apply both operands' per-row scales themselves (E8M0), so no
+ * per-block rescaling runs on the vector ALUs.  Same precondition and NaN rule
+ * as fp8_blockscaled_gemm_pow2: an output that depends on a scale other than
+ * 2^e, -126 <= e <= 127, is NaN.
+ */
+fp8q_status fp8_blockscaled_gemm_wgrad_pow2(const uint8_t *a_q, const float *a_s,
+                                            const uint8_t *b_q, const float *b_s,
+                                            uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                            void *stream);
+
+/*
  * Grouped block-scaled FP8 GEMM for mixture-of-experts layers (the recipe's
  * MoE models on page 1, "Leistungsgewinne in der Praxis" and "Warum dies fuer
  * die KI-Oekonomie wichtig ist"): group g owns rows

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
-              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_kv_cache_append",
+              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
+              "fp8_kv_cache_append",
               "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
@@ -127,8 +128,9 @@ def test_dual_quantizer_argument_errors(lib, fn):
         assert f(GOOD, 100, 128, GOOD, GOOD, GOOD, GOOD, 0, None) == 2   # N % 128
 
 
-def test_wgrad_argument_errors(lib):
-    f = lib.fp8_blockscaled_gemm_wgrad
+@pytest.mark.parametrize("fn", ["fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2"])
+def test_wgrad_argument_errors(lib, fn):
+    f = getattr(lib, fn)
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, None) == 2      # K % 128
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 64, 100, 128, None) == 2      # N % 128
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, -1, 128, 128, None) == 1

@@ -239,3 +239,61 @@ def test_llama_backward_full_size_sampled(layer):
     ns, ks = rng.integers(0, N, 400), rng.integers(0, K, 400)
     ref = oracle.gemm_wgrad_sampled_f64(host_u8(gtq), host_f32(gts), host_u8(xtq), host_f32(xts), ns, ks)
     gemm_tolerance_check(dw.float().cpu().numpy().astype(np.float64)[ns, ks], ref, f"{name} wgrad sampled")
+
+
+@pytest.mark.parametrize("M,N,K,rows", [(300, 256, 384, None), (128, 640, 256, None), (700, 256, 128, 200)])
+def test_wgrad_pow2(M, N, K, rows):
+    """Power-of-two scales applied by the matrix cores (per-row E8M0 on both
+    operands) against the oracle."""
+    require_gpu()
+    fp8q = lib()
+    ops = _grad_operands(M, N, K, 5 * M + N + K, mode=1)
+    (gtq, gts), (xtq, xts) = ops["gt"], ops["xt"]
+    if rows is not None:
+        gtq, gts = gtq[:rows], gts[:rows]
+    say("wgrad pow2", M, N, K)
+    y = fp8q.fp8_blockscaled_gemm_wgrad_pow2(_dev(gtq), _dev(gts), _dev(xtq), _dev(xts))
+    torch.cuda.synchronize()
+    gemm_tolerance_check(host_bf16_as_f64(y), oracle.gemm_wgrad_f64(gtq, gts, xtq, xts), f"wgrad pow2 {M}x{N}x{K}")
+
+
+def test_wgrad_pow2_exact_per_row_scales():
+    """Codes for -1/0/+1 and scales 2^e per row and block on both sides: every
+    partial sum is exact in fp32, so the bf16 output is the exact product
+    rounded once, bit for bit."""
+    require_gpu()
+    fp8q = lib()
+    rng = np.random.default_rng(91)
+    N, K, Mp = 256, 384, 384
+    lut = np.array([0xB8, 0x00, 0x38], dtype=np.uint8)
+    aq, bq = lut[rng.integers(-1, 2, size=(N, Mp)) + 1], lut[rng.integers(-1, 2, size=(K, Mp)) + 1]
+    as_ = np.exp2(rng.integers(-3, 4, size=(N, 3))).astype(np.float32)
+    bs = np.exp2(rng.integers(-3, 4, size=(K, 3))).astype(np.float32)
+    say("wgrad pow2 exact")
+    y = fp8q.fp8_blockscaled_gemm_wgrad_pow2(_dev(aq), _dev(as_), _dev(bq), _dev(bs))
+    torch.cuda.synchronize()
+    want = oracle.round_bf16(oracle.gemm_wgrad_f64(aq, as_, bq, bs))
+    assert_bytes_equal(y.cpu().contiguous().view(torch.int16).numpy().view(np.uint16), want, "wgrad pow2 exact")
+
+
+def test_wgrad_pow2_nan_rule():
+    """A scale that is not a power of two turns exactly the outputs that depend
+    on it into NaN: a dY^T row's scale its output row, an X^T row's scale its
+    output column; everything else is unchanged."""
+    require_gpu()
+    fp8q = lib()
+    ops = _grad_operands(256, 256, 384, 7, mode=1)
+    (gtq, gts), (xtq, xts) = ops["gt"], ops["xt"]
+    gts, xts = gts.copy(), xts.copy()
+    gts[37, 1] = 3.0
+    xts[200, 0] = 0.75
+    say("wgrad pow2 nan rule")
+    y = host_bf16_as_f64(fp8q.fp8_blockscaled_gemm_wgrad_pow2(_dev(gtq), _dev(gts), _dev(xtq), _dev(xts)))
+    torch.cuda.synchronize()
+    bad = np.zeros(y.shape, bool)
+    bad[37, :] = True
+    bad[:, 200] = True
+    assert np.isnan(y[bad]).all()
+    assert not np.isnan(y[~bad]).any()
+    ref = oracle.gemm_wgrad_f64(gtq, gts, xtq, xts)
+    gemm_tolerance_check(np.where(bad, 0.0, y), np.where(bad, 0.0, ref), "wgrad pow2 other outputs")
