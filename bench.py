@@ -42,17 +42,19 @@ def weight_quant_bytes(N, K):
 
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_llama4096_traffic.txt")
 GEMM_SOURCES = ("blockwise_scaled_fp8_quant_amd/csrc/gemm.hip",
-                "blockwise_scaled_fp8_quant_amd/csrc/fp8q_device.h",
-                "blockwise_scaled_fp8_quant_amd/build.py")
+                "blockwise_scaled_fp8_quant_amd/csrc/fp8q_device.h")
 
 
 def gemm_source_digest():
-    """sha256 over the GEMM kernel's sources and build flags."""
+    """sha256 over the GEMM kernel's sources and its compile flags (what
+    decides the kernel binary the counters were taken on)."""
     import hashlib
+    from blockwise_scaled_fp8_quant_amd import build as hip_build
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(repr((hip_build.ARCH, hip_build.COMMON)).encode())
     return h.hexdigest()
 
 
