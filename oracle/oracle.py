@@ -349,3 +349,43 @@ def attention_decode_f64(qq, qs, kq, ks, vq, vs, seq_len):
             p /= p.sum(axis=1, keepdims=True)
             o[b, g * grp:(g + 1) * grp] = p @ v
     return o
+
+
+# ---------------------------------------------------------------------------
+# The gate+up projection of a SwiGLU MLP with its activation and the next
+# layer's quantization fused (page 1, "Leistungsgewinne in der Praxis":
+# quantization-kernel overhead is part of the gap to 2x; the Llama and Qwen3
+# MLPs are SwiGLU).  Reading: the fused weight [2F][K] holds gate and up in
+# alternating blocks of 128 rows (block 2p = gate rows 128p.., block 2p+1 =
+# up rows 128p..), so one 256-row tile carries gate and up of the same 128
+# output columns; gate and up are the GEMM's outputs rounded to bf16 (what a
+# bf16-output GEMM would hand to a separate activation kernel); h = silu(g) * u
+# = g / (1 + exp(-g)) * u, rounded to bf16, is quantized in 1x128 blocks by
+# the activation rule.
+# ---------------------------------------------------------------------------
+
+def swiglu_split(y):
+    """Columns of the fused gate+up output y [M, 2F] -> (gate [M, F], up [M, F])
+    under the 128-block interleave."""
+    y = np.asarray(y)
+    M, N2 = y.shape
+    blocks = y.reshape(M, N2 // 256, 2, 128)
+    return blocks[:, :, 0, :].reshape(M, N2 // 2), blocks[:, :, 1, :].reshape(M, N2 // 2)
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def swiglu_h_f64(aq, as_, bq, bs):
+    """h [M, F] in fp64 from the fused gate+up GEMM: silu(bf16(gate)) * bf16(up)
+    before its final rounding."""
+    y = bf16_to_f64(round_bf16(gemm_f64(aq, as_, bq, bs)))
+    g, u = swiglu_split(y)
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def gemm_swiglu_quant(aq, as_, bq, bs, mode=MODE_AMAX):
+    """(h_q uint8 [M, F], h_s f32 [M, F/128]): h rounded to bf16 and quantized
+    in 1x128 blocks, the input of the down projection."""
+    return quant_act_1x128(round_bf16(swiglu_h_f64(aq, as_, bq, bs)), mode)
