@@ -369,7 +369,48 @@ def fused_output_quant(fp8q, layers, torch, M, reps):
         del yq, ys
     log(f"fused output quant: {flops / t_fus / 1e12:.1f} TFLOP/s vs {flops / t_sep / 1e12:.1f} separate")
     return {"fused_tflops": round(flops / t_fus / 1e12, 1), "separate_tflops": round(flops / t_sep / 1e12, 1),
-            "speedup": round(t_sep / t_fus, 3), "per_layer": per}
+            "speedup": round(t_sep / t_fus, 3), "per_layer": per,
+            "swiglu": fused_swiglu(fp8q, layers, torch, M, reps)}
+
+
+def fused_swiglu(fp8q, layers, torch, M, reps):
+    """The gate+up layer (weight rows in alternating 128-row gate/up blocks)
+    with SwiGLU and the down projection's activation quantization in its
+    epilogue, against the unfused sequence: bf16 GEMM, silu(gate) * up as
+    torch elementwise ops on the bf16 halves, then the 1x128 quantizer.  The
+    plain bf16 GEMM alone is timed too: the epilogue's cost over it."""
+    l = next(l for l in layers if l["name"] == "gate_up")
+    aq, as_, bq, bs, y = l["aq"], l["as_"], l["bq"], l["bs"], l["y"]
+    F = l["N"] // 2
+    hq = torch.empty((M, F), dtype=torch.uint8, device=y.device)
+    hs = torch.empty((M, F // 128), dtype=torch.float32, device=y.device)
+    yv = y.view(M, F // 128, 2, 128)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=y.device)
+    hv = h.view(M, F // 128, 128)
+
+    def gemm():
+        fp8q.fp8_blockscaled_gemm(aq, as_, bq, bs, out=y)
+
+    def separate():
+        gemm()
+        torch.mul(torch.nn.functional.silu(yv[:, :, 0]), yv[:, :, 1], out=hv)
+        fp8q.fp8_quant_act_1x128(h, "amax", out=(hq, hs))
+
+    def fused():
+        fp8q.fp8_blockscaled_gemm_swiglu_quant(aq, as_, bq, bs, "amax", out=(hq, hs))
+    separate()
+    fused()
+    tg = time_loop(gemm, reps, torch)
+    ts = time_loop(separate, reps, torch)
+    tf = time_loop(fused, reps, torch)
+    f = 2.0 * M * l["N"] * l["K"]
+    log(f"fused swiglu: {tf * 1e6:.1f} us ({f / tf / 1e12:.1f} TFLOP/s) vs {ts * 1e6:.1f} us separate, "
+        f"{tg * 1e6:.1f} us bf16 GEMM alone")
+    del hq, hs, h
+    return {"layer": "gate_up", "M": M, "F": F, "K": l["K"], "fused_us": round(tf * 1e6, 2),
+            "separate_us": round(ts * 1e6, 2), "gemm_alone_us": round(tg * 1e6, 2),
+            "fused_tflops": round(f / tf / 1e12, 1), "speedup": round(ts / tf, 3),
+            "epilogue_overhead": round(tf / tg - 1.0, 4)}
 
 
 def recalibration(fp8q, synth, torch, dev, copy_gbs=None):

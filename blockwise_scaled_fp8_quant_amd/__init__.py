@@ -25,7 +25,8 @@ _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
-           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather",
+           "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant",
+           "fp8_grouped_gemm_gather",
            "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
            "fp8_blockscaled_gemm_wgrad_pow2",
            "fp8_kv_cache_append", "fp8_attention_decode", "fp8_attention_decode_workspace_size",
@@ -160,6 +161,37 @@ def fp8_blockscaled_gemm_quant(a_q, a_s, b_q, b_s, mode="amax", out=None):
                _lib.load().fp8_blockscaled_gemm_quant(pa, pas, pb, pbs, pyq, pys, M, N, K, _mode(mode),
                                                       _stream(a_q)))
     return yq, ys
+
+
+def fp8_blockscaled_gemm_swiglu_quant(a_q, a_s, b_q, b_s, mode="amax", out=None):
+    """Fused gate+up projection of a SwiGLU MLP with its activation quantized:
+    b_q [2F, K] holds gate and up rows in alternating 128-row blocks; returns
+    (h_q uint8 [M, F], h_s fp32 [M, F/128]), the 1x128 quantization of the
+    bf16 h = silu(gate) * up."""
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 2)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 2)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if N % 256 != 0:
+        raise ValueError("b_q must have 2F rows, F a multiple of 128")
+    F = N // 2
+    if b_q.shape[1] != K or tuple(a_s.shape) != (M, K // 128) or tuple(b_s.shape) != (N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=a_q.device)
+        hs = torch.empty((M, F // 128), dtype=torch.float32, device=a_q.device)
+    else:
+        hq, hs = out
+    hq, phq = _as_bytes(hq, "h_q", 2)
+    phs = _dev(hs, "h_s", torch.float32, 2)
+    if tuple(hq.shape) != (M, F) or tuple(hs.shape) != (M, F // 128):
+        raise ValueError("output shapes do not match")
+    _lib.check("fp8_blockscaled_gemm_swiglu_quant",
+               _lib.load().fp8_blockscaled_gemm_swiglu_quant(pa, pas, pb, pbs, phq, phs, M, F, K, _mode(mode),
+                                                             _stream(a_q)))
+    return hq, hs
 
 
 def _grouped(fn, a_q, a_s, b_q, b_s, group_offsets, out):

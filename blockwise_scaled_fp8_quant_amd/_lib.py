@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "FP8Q_OK", 1: "FP8Q_EINVAL", 2: "FP8Q_ESHAPE", 3: "FP8Q_EALIG
                 4: "FP8Q_EDEVICE", 5: "FP8Q_EHIP"}
 ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-                "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
+                "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
                 "fp8_kv_cache_append",
                 "fp8_attention_decode", "fp8_attention_decode_workspace_size",
@@ -53,6 +53,8 @@ def load():
         getattr(lib, name).restype = ci
     lib.fp8_blockscaled_gemm_quant.argtypes = [p, p, p, p, p, p, i64, i64, i64, ci, p]
     lib.fp8_blockscaled_gemm_quant.restype = ci
+    lib.fp8_blockscaled_gemm_swiglu_quant.argtypes = [p, p, p, p, p, p, i64, i64, i64, ci, p]
+    lib.fp8_blockscaled_gemm_swiglu_quant.restype = ci
     for name in ("fp8_grouped_gemm", "fp8_grouped_gemm_pow2"):
         getattr(lib, name).argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, p]
         getattr(lib, name).restype = ci

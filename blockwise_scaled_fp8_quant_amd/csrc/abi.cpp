@@ -170,6 +170,27 @@ fp8q_status gemm_quant_entry(const char *fn, const uint8_t *a_q, const float *a_
       fp8q::launch_blockscaled_gemm_quant(a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, (hipStream_t)stream), fn);
 }
 
+fp8q_status swiglu_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                         const float *b_s, uint8_t *h_q, float *h_s, int64_t M, int64_t F, int64_t K, int mode,
+                         void *stream) {
+  g_last_error.clear();
+  if (mode != FP8Q_SCALE_AMAX && mode != FP8Q_SCALE_POW2) return fail(FP8Q_EINVAL, fn, "unknown mode");
+  if (!(M >= 0 && F >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (F % 128 != 0) return fail(FP8Q_ESHAPE, fn, "F must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M <= (int64_t)1 << 31 && F <= (int64_t)1 << 30)) return fail(FP8Q_EINVAL, fn, "M or F too large");
+  if (M == 0 || F == 0) return FP8Q_OK;
+  if (!(a_q && a_s && b_q && b_s && h_q && h_s)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(h_q) && aligned16(h_s)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(
+      fp8q::launch_blockscaled_gemm_swiglu_quant(a_q, a_s, b_q, b_s, h_q, h_s, M, F, K, mode, (hipStream_t)stream),
+      fn);
+}
+
 fp8q_status wgrad_entry(const char *fn, const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
                         const float *b_s, uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2, void *stream) {
   g_last_error.clear();
@@ -259,6 +280,12 @@ fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s, con
                                        const float *b_s, uint8_t *y_q, float *y_s, int64_t M, int64_t N,
                                        int64_t K, int mode, void *stream) {
   return gemm_quant_entry(__func__, a_q, a_s, b_q, b_s, y_q, y_s, M, N, K, mode, stream);
+}
+
+fp8q_status fp8_blockscaled_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,
+                                              const float *b_s, uint8_t *h_q, float *h_s, int64_t M, int64_t F,
+                                              int64_t K, int mode, void *stream) {
+  return swiglu_entry(__func__, a_q, a_s, b_q, b_s, h_q, h_s, M, F, K, mode, stream);
 }
 
 fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s, const uint8_t *b_q,

@@ -43,6 +43,14 @@ hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
                                          uint16_t *y, int64_t M, int64_t N, int64_t K, bool pow2,
                                          hipStream_t stream);
 
+// Fused gate+up GEMM of a SwiGLU MLP: b_q [2F][K] holds gate and up in
+// alternating 128-row blocks; writes h = silu(gate) * up quantized in 1x128
+// blocks, hq [M][F], hs [M][F/128].  F % 128 == 0.
+hipError_t launch_blockscaled_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s,
+                                                const uint8_t *b_q, const float *b_s,
+                                                uint8_t *hq, float *hs, int64_t M, int64_t F, int64_t K,
+                                                int mode, hipStream_t stream);
+
 // Row-major and transposed codes of x [M][K] in one pass.  tile: one scale per
 // 128x128 tile (weights; M % 128 == 0), q_t [K][M], s_t [K/128][M/128].
 // Otherwise 1x128 row blocks (q, s; may be null) and 128x1 column blocks

@@ -59,13 +59,18 @@ constexpr int kOutBf16 = -1;
 //   kGather   grouped rows read by index from a token matrix
 //   kBRow     the weight-side operand carries one scale per row and 128-block
 //             of K (1x128 blocks on both operands) instead of 128x128 tiles
-template <bool kGrouped_, bool kPow2_, int kOut_ = kOutBf16, bool kGather_ = false, bool kBRow_ = false>
+//   kSwiGLU   (with a quantized kOut) the weight rows alternate 128-row gate
+//             and up blocks; the epilogue writes silu(gate) * up, quantized
+template <bool kGrouped_, bool kPow2_, int kOut_ = kOutBf16, bool kGather_ = false, bool kBRow_ = false,
+          bool kSwiGLU_ = false>
 struct Variant {
   static constexpr bool kGrouped = kGrouped_;
   static constexpr bool kPow2 = kPow2_;
   static constexpr int kOut = kOut_;
   static constexpr bool kGather = kGather_;
   static constexpr bool kBRow = kBRow_;
+  static constexpr bool kSwiGLU = kSwiGLU_;
+  static_assert(!(kSwiGLU && (kOut == kOutBf16 || kGrouped || kBRow)), "SwiGLU: dense, quantized output");
   static_assert(!(kGather && !kGrouped), "gathered rows belong to groups");
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
@@ -737,6 +742,75 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
         }
       }
     }
+  } else if constexpr (V::kSwiGLU) {
+    // SwiGLU epilogue of a fused gate+up projection: the tile's weight rows
+    // are 128 gate rows (waves wn = 0) and the 128 up rows of the same output
+    // columns (waves wn = 1).  gate and up are rounded to bf16 as the bf16
+    // epilogue rounds them; the up waves pass theirs through LDS (the stage
+    // buffers are free once every wave is past the barrier), and the gate
+    // waves form h = silu(g) * u = g / (1 + e^-g) * u in fp32, round it to
+    // bf16 and quantize each row's 128 values as one 1x128 block (the
+    // activation rule), writing row r's block at column 128*(n0/256).
+    constexpr int kUpStride = 66;  // 32-bit words per LDS row (64 + 2: rows fall in different banks)
+    uint32_t *upl = reinterpret_cast<uint32_t *>(lds);
+    __syncthreads();
+    if (wn == 1) {
+#pragma unroll
+      for (int mi = 0; mi < kSubM; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) {
+          const int nn = ni * 16 + 4 * (lane >> 4);
+          uint2 w;
+          w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+          w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+          *reinterpret_cast<uint2 *>(upl + r * kUpStride + (nn >> 1)) = w;
+        }
+      }
+    }
+    __syncthreads();
+    if (wn == 0) {
+      const int64_t F = N >> 1;   // columns of h
+      const int64_t nbo = F >> 7;  // scale blocks per row of h
+#pragma unroll
+      for (int mi = 0; mi < kSubM; ++mi) {
+        const int r = wm * 64 + mi * 16 + (lane & 15);
+        uint32_t h[kSubN][2];
+        float amax = 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < kSubN; ++ni) {
+          const int nn = ni * 16 + 4 * (lane >> 4);
+          const uint2 uw = *reinterpret_cast<const uint2 *>(upl + r * kUpStride + (nn >> 1));
+          const uint32_t g01 = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+          const uint32_t g23 = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+          const float g[4] = {bf16_lo(g01), bf16_hi(g01), bf16_lo(g23), bf16_hi(g23)};
+          const float u[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
+          float hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
+          h[ni][0] = pack_bf16x2(hv[0], hv[1]);
+          h[ni][1] = pack_bf16x2(hv[2], hv[3]);
+          amax = max3_abs(amax, bf16_lo(h[ni][0]), bf16_hi(h[ni][0]));
+          amax = max3_abs(amax, bf16_lo(h[ni][1]), bf16_hi(h[ni][1]));
+        }
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+        const BlockQ bq = block_params<kOut>(amax);
+        if (r < t.m_valid) {
+          if ((lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
+          uint8_t *qrow = o.yq + (int64_t)r * F + 4 * (lane >> 4);
+#pragma unroll
+          for (int ni = 0; ni < kSubN; ++ni) {
+            const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
+            float qv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+            *reinterpret_cast<uint32_t *>(qrow + ni * 16) = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+          }
+        }
+      }
+    }
   } else {
     // Quantized epilogue (the activation quantization of the next layer, done
     // by the producer instead of by a separate pass over bf16 Y; page 1,
@@ -908,9 +982,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   t.m_valid = (int)((m_end - m0) < C::kBM ? (m_end - m0) : C::kBM);
   t.n_valid = n_valid;
   TileOut o{nullptr, nullptr, nullptr};
-  if constexpr (kOut == kOutBf16)
+  if constexpr (kOut == kOutBf16) {
     o.y = p.y + m0 * p.N + n0;
-  else {
+  } else if constexpr (V::kSwiGLU) {  // h [M][N/2]: this tile's 128 columns start at n0/2
+    o.yq = p.yq + m0 * (p.N >> 1) + (n0 >> 1);
+    o.ys = p.ys + m0 * (p.N >> 8) + (n0 >> 8);
+  } else {
     o.yq = p.yq + m0 * p.N + n0;
     o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
   }
@@ -932,11 +1009,11 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool kPow2, int kOut = kOutBf16, bool kBRow = false>
+template <bool kPow2, int kOut = kOutBf16, bool kBRow = false, bool kSwiGLU = false>
 static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                         uint16_t *y, uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
                         hipStream_t stream) {
-  using V = Variant<false, kPow2, kOut, false, kBRow>;
+  using V = Variant<false, kPow2, kOut, false, kBRow, kSwiGLU>;
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n};
@@ -990,6 +1067,15 @@ hipError_t launch_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
                                          hipStream_t stream) {
   return pow2 ? dense<true, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream)
               : dense<false, kOutBf16, true>(a_q, a_s, b_q, b_s, y, nullptr, nullptr, M, N, K, stream);
+}
+
+hipError_t launch_blockscaled_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s,
+                                                const uint8_t *b_q, const float *b_s,
+                                                uint8_t *hq, float *hs, int64_t M, int64_t F, int64_t K,
+                                                int mode, hipStream_t stream) {
+  return mode == kModePow2
+             ? dense<false, kModePow2, false, true>(a_q, a_s, b_q, b_s, nullptr, hq, hs, M, 2 * F, K, stream)
+             : dense<false, kModeAmax, false, true>(a_q, a_s, b_q, b_s, nullptr, hq, hs, M, 2 * F, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,

@@ -179,6 +179,38 @@ fp8q_status fp8_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
                                        void *stream);
 
 /*
+ * The fused gate and up projections of a SwiGLU MLP with the activation of
+ * the down projection quantized in the epilogue: the 1x128 quantization of
+ *   h = silu(gate) * up,  silu(g) = g / (1 + e^-g),
+ * where gate and up are the two halves of one block-scaled FP8 GEMM against
+ * the concatenated weight, each rounded to bf16 as fp8_blockscaled_gemm rounds
+ * its output.  The bf16 gate, up and h never go to memory (page 1,
+ * "Leistungsgewinne in der Praxis": quantization-kernel overhead is part of
+ * the gap between the FP8 linear layers' gain and the ideal 2x).
+ *   a_q [M][K], a_s [M][K/128]    as for fp8_blockscaled_gemm
+ *   b_q [2F][K], b_s [2F/128][K/128]  the weight with gate and up rows in
+ *                                 alternating 128-row blocks: rows
+ *                                 256p .. 256p+127 are gate rows 128p .., rows
+ *                                 256p+128 .. 256p+255 the up rows of the same
+ *                                 output features; each block is one 128x128
+ *                                 tile row of the quantized weight
+ *   h_q [M][F] E4M3 bytes (out), h_s [M][F/128] fp32 (out): block (m, fb)
+ *                                 covers h[m][128*fb .. 128*fb+127]
+ *   F  output features, a positive multiple of 128 (0 returns at once)
+ *   mode fp8q_scale_mode of the output blocks (the weight's own scales are
+ *        read as fp8_blockscaled_gemm reads them, either mode)
+ * h is formed in fp32 from the bf16 gate and up (the exponential is the
+ * hardware's base-2 one, a few ulp from exact) and rounded to bf16 (nearest
+ * even) before the 1x128 quantization, whose rule is fp8_quant_act_1x128's.
+ * Errors as for fp8_blockscaled_gemm_quant.
+ */
+fp8q_status fp8_blockscaled_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s,
+                                              const uint8_t *b_q, const float *b_s,
+                                              uint8_t *h_q, float *h_s,
+                                              int64_t M, int64_t F, int64_t K, int mode,
+                                              void *stream);
+
+/*
  * Block-scaled FP8 GEMM with 1x128 blocks on both operands: the weight
  * gradient of a linear layer (training end to end in FP8, page 1, title and
  * "Der technische Durchbruch"), dW = dY^T X, contracted over the tokens:

@@ -30,8 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-              "fp8_blockscaled_gemm_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
-              "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
+              "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
+              "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
               "fp8_kv_cache_append",
               "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
@@ -97,6 +97,22 @@ def test_gemm_quant_argument_errors(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 128, 128, 0, None) == 1      # null scales out
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 64, 128, 128, 0, None) == 3       # misaligned y_q
     assert f(None, None, None, None, None, None, 0, 128, 128, 0, None) == 0       # empty call
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, 0, None) == 2
+
+
+def test_gemm_swiglu_quant_argument_errors(lib):
+    f = lib.fp8_blockscaled_gemm_swiglu_quant
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 128, 2, None) == 1      # unknown mode
+    assert "mode" in _err(lib)
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, 130, 0, None) == 2      # K not a multiple of 128
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 64, 128, 1, None) == 2       # F not a multiple of 128
+    assert "F" in _err(lib)
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, -128, 128, 0, None) == 1
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, (1 << 30) + 128, 128, 0, None) == 1
+    assert f(GOOD, GOOD, None, GOOD, GOOD, GOOD, 64, 128, 128, 0, None) == 1      # null weight
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 64, 128, 128, 0, None) == 3       # misaligned h_s
+    assert f(None, None, None, None, None, None, 64, 0, 128, 0, None) == 0        # F = 0: nothing to do
+    assert f(None, None, None, None, None, None, 0, 128, 128, 0, None) == 0
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, 0, None) == 2
 
 
