@@ -31,5 +31,7 @@ from .oracle import (  # noqa: F401
     bf16_to_f64,
     swiglu_h_f64,
     gemm_swiglu_quant,
+    rmsnorm_f64,
+    rmsnorm_quant_1x128,
     num_threads,
 )

@@ -389,3 +389,31 @@ def gemm_swiglu_quant(aq, as_, bq, bs, mode=MODE_AMAX):
     """(h_q uint8 [M, F], h_s f32 [M, F/128]): h rounded to bf16 and quantized
     in 1x128 blocks, the input of the down projection."""
     return quant_act_1x128(round_bf16(swiglu_h_f64(aq, as_, bq, bs)), mode)
+
+
+# ---------------------------------------------------------------------------
+# RMS normalization with the next layer's quantization fused: the third
+# producer of FP8 activations in a Llama/Qwen3 block (its norms feed the QKV
+# and gate+up projections; page 1, "Leistungsgewinne in der Praxis": the
+# quantization kernels are overhead).  Reading: y = gamma * x / sqrt(mean(x^2)
+# + eps) over each row of K values, computed exactly (fp64) from the bf16 x
+# and gamma and the fp32 eps, rounded once to bf16, then quantized in 1x128
+# blocks by the activation rule.
+# ---------------------------------------------------------------------------
+
+def rmsnorm_f64(x_bits, gamma_bits, eps):
+    """y [M, K] in fp64 before its bf16 rounding; x_bits [M, K] and gamma_bits
+    [K] are bf16 bit patterns, eps a float32 value."""
+    x = bf16_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    g = bf16_to_f64(np.asarray(gamma_bits, dtype=np.uint16))
+    if x.ndim != 2 or g.shape != (x.shape[1],):
+        raise ValueError("x must be [M, K] and gamma [K]")
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    e = float(np.float32(eps))
+    return x / np.sqrt(ms + e) * g[None, :]
+
+
+def rmsnorm_quant_1x128(x_bits, gamma_bits, eps, mode=MODE_AMAX):
+    """(q uint8 [M, K], s f32 [M, K/128]): bf16(rmsnorm(x)) quantized in 1x128
+    blocks, the input of the projection that follows the norm."""
+    return quant_act_1x128(round_bf16(rmsnorm_f64(x_bits, gamma_bits, eps)), mode)
