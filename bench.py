@@ -13,6 +13,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -119,7 +120,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,backward,recal,moe,dispatch,attention,bf16,cpu",
+    ap.add_argument("--sections", default="pow2,fused,norm,backward,recal,moe,dispatch,attention,bf16,cpu",
                     help="extra measurements after the step (comma list of pow2, fused, backward, recal, "
                          "moe, dispatch, attention, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
@@ -288,6 +289,8 @@ def main():
         result["pow2"] = pow2_gemm(fp8q, layers, torch, M, reps)
     if "fused" in sections:
         result["fused_output_quant"] = fused_output_quant(fp8q, layers, torch, M, reps)
+    if "norm" in sections:
+        result["rmsnorm_quant"] = rmsnorm_quant(fp8q, torch, dev, M, reps, copy_gbs)
     if "recal" in sections:
         result["recalibration"] = recalibration(fp8q, synth, torch, dev, copy_gbs)
     if "moe" in sections:
@@ -411,6 +414,49 @@ def fused_swiglu(fp8q, layers, torch, M, reps):
             "separate_us": round(ts * 1e6, 2), "gemm_alone_us": round(tg * 1e6, 2),
             "fused_tflops": round(f / tf / 1e12, 1), "speedup": round(ts / tf, 3),
             "epilogue_overhead": round(tf / tg - 1.0, 4)}
+
+
+def rmsnorm_quant(fp8q, torch, dev, M, reps, copy_gbs):
+    """RMS normalization fused with the 1x128 quantization of its output, on
+    the Llama-3.1-8B hidden state (4096 tokens x 4096), rotating through
+    >= 1.2 GB of distinct inputs: against torch's bf16 rms_norm followed by
+    fp8_quant_act_1x128, and against fp8_quant_act_1x128 alone (the same
+    bytes moved without the norm).  Algorithmic bytes: 2 per input value, 1
+    per code, 4 per scale (gamma, 8 KB, not counted)."""
+    K = 4096
+    nrot = max(1, math.ceil(1.2e9 / (M * K * 3)))
+    xs = [torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(nrot)]
+    g = (1.0 + 0.1 * torch.randn(K, device=dev)).to(torch.bfloat16)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    ctr = [0]
+
+    def fused():
+        fp8q.fp8_rmsnorm_quant_1x128(xs[ctr[0] % nrot], g, 1e-5, "amax", out=(q, s))
+        ctr[0] += 1
+
+    def separate():
+        h = torch.nn.functional.rms_norm(xs[ctr[0] % nrot], (K,), weight=g, eps=1e-5)
+        fp8q.fp8_quant_act_1x128(h, "amax", out=(q, s))
+        ctr[0] += 1
+
+    def quant_only():
+        fp8q.fp8_quant_act_1x128(xs[ctr[0] % nrot], "amax", out=(q, s))
+        ctr[0] += 1
+    fused()
+    separate()
+    tf = time_loop(fused, reps * nrot, torch)
+    ts = time_loop(separate, reps * nrot, torch)
+    tq = time_loop(quant_only, reps * nrot, torch)
+    b = act_quant_bytes(M, K)
+    log(f"rmsnorm+quant {b / tf / 1e9:.1f} GB/s ({tf * 1e6:.1f} us) vs {ts * 1e6:.1f} us separate, "
+        f"{tq * 1e6:.1f} us quantizer alone")
+    del xs
+    return {"M": M, "K": K, "fused_us": round(tf * 1e6, 2), "fused_gbs": round(b / tf / 1e9, 1),
+            "fused_frac_hbm": round(b / tf / 1e9 / HBM_PEAK_GBS, 4),
+            "fused_frac_copy": round(b / tf / 1e9 / copy_gbs, 4) if copy_gbs else None,
+            "separate_us": round(ts * 1e6, 2), "speedup": round(ts / tf, 3),
+            "quant_alone_us": round(tq * 1e6, 2)}
 
 
 def recalibration(fp8q, synth, torch, dev, copy_gbs=None):

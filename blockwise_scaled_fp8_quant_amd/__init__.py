@@ -23,7 +23,8 @@ SCALE_AMAX = 0
 SCALE_POW2 = 1
 _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_POW2: SCALE_POW2}
 
-__all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_quant_weight_128x128",
+__all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128",
+           "fp8_quant_weight_128x128",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant",
            "fp8_grouped_gemm_gather",
@@ -87,6 +88,29 @@ def fp8_quant_act_1x128(x, mode="amax", out=None):
         raise ValueError("output shapes do not match x")
     _lib.check("fp8_quant_act_1x128",
                _lib.load().fp8_quant_act_1x128(px, M, K, pq, ps, _mode(mode), _stream(x)))
+    return q, s
+
+
+def fp8_rmsnorm_quant_1x128(x, gamma, eps=1e-5, mode="amax", out=None):
+    """RMS normalization fused with the 1x128 quantization of its output:
+    x bf16 [M, K], gamma bf16 [K] (K % 128 == 0, K <= 8192) ->
+    (q uint8 [M, K], s fp32 [M, K/128]) of bf16(x / sqrt(mean(x^2) + eps) * gamma)."""
+    px = _dev(x, "x", torch.bfloat16, 2)
+    pg = _dev(gamma, "gamma", torch.bfloat16, 1)
+    M, K = x.shape
+    if tuple(gamma.shape) != (K,):
+        raise ValueError("gamma must have K elements")
+    if out is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    _, pq = _as_bytes(q, "q", 2)
+    ps = _dev(s, "scales", torch.float32, 2)
+    if tuple(q.shape) != (M, K) or tuple(s.shape) != (M, K // 128):
+        raise ValueError("output shapes do not match x")
+    _lib.check("fp8_rmsnorm_quant_1x128",
+               _lib.load().fp8_rmsnorm_quant_1x128(px, pg, M, K, float(eps), pq, ps, _mode(mode), _stream(x)))
     return q, s
 
 

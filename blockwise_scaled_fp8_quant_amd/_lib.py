@@ -12,7 +12,8 @@ LIB_PATH = os.path.join(HERE, "libfp8q.so")
 FP8Q_OK = 0
 STATUS_NAMES = {0: "FP8Q_OK", 1: "FP8Q_EINVAL", 2: "FP8Q_ESHAPE", 3: "FP8Q_EALIGN",
                 4: "FP8Q_EDEVICE", 5: "FP8Q_EHIP"}
-ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
+ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_weight_128x128",
+                "fp8_blockscaled_gemm",
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
                 "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
@@ -42,6 +43,8 @@ def load():
     p, i64, i32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     lib.fp8_quant_act_1x128.argtypes = [p, i64, i64, p, p, ci, p]
     lib.fp8_quant_act_1x128.restype = ci
+    lib.fp8_rmsnorm_quant_1x128.argtypes = [p, p, i64, i64, ctypes.c_float, p, p, ci, p]
+    lib.fp8_rmsnorm_quant_1x128.restype = ci
     lib.fp8_quant_weight_128x128.argtypes = [p, i64, i64, p, p, ci, p]
     lib.fp8_quant_weight_128x128.restype = ci
     for name in ("fp8_quant_act_dual", "fp8_quant_weight_128x128_dual"):

@@ -3,6 +3,7 @@
 // the device before every check has passed.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -72,6 +73,24 @@ fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t
   fp8q_status st = check_device(__func__);
   if (st != FP8Q_OK) return st;
   return launched(fp8q::launch_quant_act_1x128(x, M, K, q, scales, mode, (hipStream_t)stream), __func__);
+}
+
+fp8q_status fp8_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma, int64_t M, int64_t K, float eps,
+                                    uint8_t *q, float *scales, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(M >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(std::isfinite(eps) && eps >= 0.0f, FP8Q_EINVAL, "eps must be finite and >= 0");
+  FP8Q_REQUIRE(K > 0 && K % 128 == 0 && K <= 8192, FP8Q_ESHAPE, "K must be a multiple of 128 in [128, 8192]");
+  FP8Q_REQUIRE(M <= ((int64_t)1 << 31), FP8Q_EINVAL, "M too large");  // one wave per row: grid < 2^31
+  if (M == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(x && gamma && q && scales, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(x) && aligned16(gamma) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,
+               "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_rmsnorm_quant_1x128(x, gamma, M, K, eps, q, scales, mode, (hipStream_t)stream),
+                  __func__);
 }
 
 fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *q,

@@ -58,6 +58,11 @@ hipError_t launch_blockscaled_gemm_swiglu_quant(const uint8_t *a_q, const float 
 hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *s, uint8_t *qt,
                              float *st, int mode, bool tile, hipStream_t stream);
 
+// RMS normalization of x [M][K] by gamma [K] with eps, output quantized in
+// 1x128 blocks: q [M][K], s [M][K/128].  K % 128 == 0, K <= 8192.
+hipError_t launch_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma, int64_t M, int64_t K, float eps,
+                                      uint8_t *q, float *s, int mode, hipStream_t stream);
+
 // Grouped GEMM whose token rows are gathered: routed row r reads token row
 // row_index[r] of a_q [T][K] / a_s [T][K/128] (quantize before dispatch).
 hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_t T,

@@ -427,4 +427,135 @@ hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// RMS normalization fused with the 1x128 quantization of its output: the
+// norms ahead of the QKV and gate+up projections produce those layers' FP8
+// activations in their own pass (page 1, "Leistungsgewinne in der Praxis":
+// separate quantization kernels are overhead).
+//   y = bf16_RNE((x * r) * gamma),  r = 1 / sqrt(sum(x^2) / K + eps)
+// in fp32 (the sum of squares by paired bf16 dot products in a fixed order),
+// then the activation rule on each 128 values of y.
+//
+// One wave per row.  Lane l holds chunk i = columns 512 i + 8 l .. +7, so the
+// 16 lanes of each DPP row hold one 1x128 block (block 4 i + l / 16).  Every
+// load is unconditional (addresses clamped into the tensors, values past the
+// row masked) and all of them are issued before any math, so each wait counts
+// only the loads it needs.  The block |max| is taken over the fp32 values
+// before their bf16 rounding and rounded once: the rounding is monotonic, so
+// this is the |max| of the rounded values.  With one row per wave the chip
+// keeps 16 rows per CU in flight; giving a wave several rows, with the next
+// row's loads overlapping the current row's math, measured slower (fewer
+// waves to hide the per-element VALU work).
+// ---------------------------------------------------------------------------
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxK = 8192;
+
+__device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));  // RNE
+}
+
+// a.lo * a.lo + a.hi * a.hi + c for a word of two bf16 values.
+__device__ __forceinline__ float dot2_sq(uint32_t a, float c) {
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = __builtin_bit_cast(h2, a);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, c, false);
+}
+
+template <int kMode, int kChunks>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma, int64_t M, int K, float eps,
+    uint8_t *__restrict__ q, float *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
+  const uint16_t *xr = x + (row < M ? row : M - 1) * K;
+  uint4 gam[kChunks], w[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    gam[i] = *reinterpret_cast<const uint4 *>(gamma + (col < K ? col : K - 8));
+  }
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    w[i] = load_stream16(xr + (col < K ? col : K - 8));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
+
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const bool in = 512 * i + 8 * lane < K;  // a chunk past the row (clamped load) adds nothing
+    ss = dot2_sq(in ? w[i].x : 0u, ss);
+    ss = dot2_sq(in ? w[i].y : 0u, ss);
+    ss = dot2_sq(in ? w[i].z : 0u, ss);
+    ss = dot2_sq(in ? w[i].w : 0u, ss);
+  }
+  // butterfly: every lane ends with the same sum (each step adds a pair in
+  // either order, and fp32 addition is commutative)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  const float r = 1.0f / __builtin_sqrtf(ss * (1.0f / (float)K) + eps);
+
+  const int nb = K >> 7;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    const uint32_t xw[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+    const uint32_t gw[4] = {gam[i].x, gam[i].y, gam[i].z, gam[i].w};
+    float yf[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      yf[2 * k] = (bf16_lo(xw[k]) * r) * bf16_lo(gw[k]);
+      yf[2 * k + 1] = (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]);
+      m = max3_abs(m, yf[2 * k], yf[2 * k + 1]);
+    }
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = to_bf16x2(yf[2 * k], yf[2 * k + 1]);
+      f[2 * k] = bf16_lo(b);
+      f[2 * k + 1] = bf16_hi(b);
+    }
+    const float amax = bf16_lo(to_bf16x2(group16_max(m), 0.0f));
+    const BlockQ p = block_params<kMode>(amax);
+    const uint2 o = quant8<kMode>(p, f);
+    if (col < K && row < M) {  // (col < K is uniform over each 16-lane block)
+      if ((lane & 15) == 0) scales[row * nb + (col >> 7)] = p.s;
+      *reinterpret_cast<uint2 *>(q + row * K + col) = o;
+    }
+  }
+}
+
+template <int kMode, int kChunks>
+static void launch_norm(const uint16_t *x, const uint16_t *gamma, int64_t M, int64_t K, float eps, uint8_t *q,
+                        float *s, hipStream_t stream) {
+  constexpr int kWaves = kNormThreads / 64;
+  hipLaunchKernelGGL((rmsnorm_quant_kernel<kMode, kChunks>), dim3((unsigned)((M + kWaves - 1) / kWaves)),
+                     dim3(kNormThreads), 0, stream, x, gamma, M, (int)K, eps, q, s);
+}
+
+template <int kMode>
+static void launch_norm_mode(const uint16_t *x, const uint16_t *gamma, int64_t M, int64_t K, float eps, uint8_t *q,
+                             float *s, hipStream_t stream) {
+  const int64_t chunks = (K + 511) / 512;
+  if (chunks <= 1) launch_norm<kMode, 1>(x, gamma, M, K, eps, q, s, stream);
+  else if (chunks <= 2) launch_norm<kMode, 2>(x, gamma, M, K, eps, q, s, stream);
+  else if (chunks <= 4) launch_norm<kMode, 4>(x, gamma, M, K, eps, q, s, stream);
+  else if (chunks <= 8) launch_norm<kMode, 8>(x, gamma, M, K, eps, q, s, stream);
+  else launch_norm<kMode, 16>(x, gamma, M, K, eps, q, s, stream);
+}
+
+hipError_t launch_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma, int64_t M, int64_t K, float eps,
+                                      uint8_t *q, float *s, int mode, hipStream_t stream) {
+  if (M == 0 || K == 0) return hipSuccess;
+  if (K % 128 != 0 || K > kNormMaxK) return hipErrorInvalidValue;
+  if (mode == kModeAmax) launch_norm_mode<kModeAmax>(x, gamma, M, K, eps, q, s, stream);
+  else launch_norm_mode<kModePow2>(x, gamma, M, K, eps, q, s, stream);
+  return hipGetLastError();
+}
+
 }  // namespace fp8q

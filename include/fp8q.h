@@ -83,6 +83,32 @@ fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
                                 void *stream);
 
 /*
+ * RMS normalization with its output quantized in 1x128 blocks, in one pass:
+ * the norms ahead of a block's QKV and gate+up projections produce those
+ * layers' FP8 inputs directly (page 1, "Leistungsgewinne in der Praxis":
+ * separate quantization kernels are part of the gap to 2x).
+ *   x       [M][K] bf16 bits (in), K a multiple of 128, 128 <= K <= 8192
+ *   gamma   [K] bf16 bits (in): the norm's weight
+ *   eps     finite, >= 0
+ *   q       [M][K] E4M3 bytes (out), scales [M][K/128] fp32 (out), laid out
+ *           as by fp8_quant_act_1x128
+ *   mode    fp8q_scale_mode
+ * y = bf16_RNE((x * r) * gamma) with r = 1 / sqrt(sum(x^2) / K + eps), each
+ * step in fp32 (the sum of squares in a fixed but unspecified order), and y
+ * is then quantized exactly as fp8_quant_act_1x128 quantizes a bf16 input.
+ * Against y computed exactly, the fp32 steps cost a few fp32 ulp, which can
+ * move the bf16 rounding (and then a code) where y sits on a rounding
+ * midpoint.  Precondition, as for the quantizer: finite x and gamma; with
+ * eps = 0 also no row whose mean square is 0 in fp32 (an all-zero row, or
+ * values below about 1e-19, whose squares underflow); the outputs of such a
+ * row are unspecified.
+ */
+fp8q_status fp8_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma,
+                                    int64_t M, int64_t K, float eps,
+                                    uint8_t *q, float *scales, int mode,
+                                    void *stream);
+
+/*
  * Weight recalibration and requantization, 128x128 blocks (page 1, "Der
  * technische Durchbruch" and "Leistungsgewinne in der Praxis"; power-of-two
  * mode: "Warum dies fuer die KI-Oekonomie wichtig ist").

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
+    for n in ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
               "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
@@ -98,6 +98,23 @@ def test_gemm_quant_argument_errors(lib):
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 64, 128, 128, 0, None) == 3       # misaligned y_q
     assert f(None, None, None, None, None, None, 0, 128, 128, 0, None) == 0       # empty call
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 128, (1 << 22) + 128, 0, None) == 2
+
+
+def test_rmsnorm_quant_argument_errors(lib):
+    import ctypes
+    f = lib.fp8_rmsnorm_quant_1x128
+    e = ctypes.c_float(1e-5)
+    assert f(GOOD, GOOD, 4, 256, e, GOOD, GOOD, 3, None) == 1                     # unknown mode
+    assert f(GOOD, GOOD, 4, 200, e, GOOD, GOOD, 0, None) == 2                     # K not a multiple of 128
+    assert f(GOOD, GOOD, 4, 8192 + 128, e, GOOD, GOOD, 0, None) == 2              # K above 8192
+    assert "8192" in _err(lib)
+    assert f(GOOD, GOOD, 4, 256, ctypes.c_float(-1.0), GOOD, GOOD, 0, None) == 1  # negative eps
+    assert f(GOOD, GOOD, 4, 256, ctypes.c_float(float("nan")), GOOD, GOOD, 0, None) == 1
+    assert f(GOOD, GOOD, 4, 256, ctypes.c_float(float("inf")), GOOD, GOOD, 0, None) == 1
+    assert f(GOOD, None, 4, 256, e, GOOD, GOOD, 0, None) == 1                     # null gamma
+    assert f(GOOD, ODD, 4, 256, e, GOOD, GOOD, 0, None) == 3                      # misaligned gamma
+    assert f(GOOD, GOOD, -1, 256, e, GOOD, GOOD, 0, None) == 1
+    assert f(None, None, 0, 256, e, None, None, 0, None) == 0                     # empty call
 
 
 def test_gemm_swiglu_quant_argument_errors(lib):
