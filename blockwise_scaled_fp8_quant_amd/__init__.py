@@ -24,7 +24,7 @@ SCALE_POW2 = 1
 _MODES = {"amax": SCALE_AMAX, "pow2": SCALE_POW2, SCALE_AMAX: SCALE_AMAX, SCALE_POW2: SCALE_POW2}
 
 __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128",
-           "fp8_quant_weight_128x128",
+           "fp8_quant_weight_128x128", "WeightBatch", "fp8_quant_weight_128x128_batched",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant",
            "fp8_grouped_gemm_gather",
@@ -130,6 +130,64 @@ def fp8_quant_weight_128x128(w, mode="amax", out=None):
     _lib.check("fp8_quant_weight_128x128",
                _lib.load().fp8_quant_weight_128x128(pw, N, K, pq, ps, _mode(mode), _stream(w)))
     return q, s
+
+
+class WeightBatch:
+    """A fixed set of weight matrices that are requantized together, e.g. every
+    linear weight of a model after each policy update.
+
+    weights: bf16 [N_i, K_i] tensors on one device (N_i, K_i % 128 == 0).
+    outs:    optional (q uint8 [N_i, K_i], s fp32 [N_i/128, K_i/128]) per weight.
+    The job table of the C ABI (fp8q_weight_job: w, q, scales, N, K,
+    tile_begin; 48 bytes each) is built once, here, in device memory; the
+    tensors stay referenced so that the addresses in it remain valid.
+    """
+
+    def __init__(self, weights, outs=None):
+        weights = list(weights)
+        if not weights:
+            raise ValueError("WeightBatch needs at least one weight")
+        device = weights[0].device
+        if outs is None:
+            outs = [(torch.empty(tuple(w.shape), dtype=torch.uint8, device=device),
+                     torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32, device=device))
+                    for w in weights]
+        outs = list(outs)
+        if len(outs) != len(weights):
+            raise ValueError("one (q, s) pair per weight")
+        rows, tiles = [], 0
+        for i, (w, (q, s)) in enumerate(zip(weights, outs)):
+            pw = _dev(w, f"weights[{i}]", torch.bfloat16, 2)
+            _, pq = _as_bytes(q, f"q[{i}]", 2)
+            ps = _dev(s, f"scales[{i}]", torch.float32, 2)
+            if w.device != device or q.device != device or s.device != device:
+                raise ValueError("all tensors of a WeightBatch must be on one device")
+            N, K = w.shape
+            if N % 128 or K % 128 or K == 0:
+                raise ValueError(f"weights[{i}]: N and K must be multiples of 128 and K > 0 (got {N}x{K})")
+            if tuple(q.shape) != (N, K) or tuple(s.shape) != (N // 128, K // 128):
+                raise ValueError(f"outs[{i}]: shapes do not match weights[{i}]")
+            rows.append([pw.value, pq.value, ps.value, N, K, tiles])
+            tiles += (N // 128) * (K // 128)
+        self.weights, self.outs = weights, outs
+        self.total_tiles = tiles
+        self.jobs = torch.tensor(rows, dtype=torch.int64).to(device)
+        torch.cuda.synchronize(device)
+
+    def __len__(self):
+        return len(self.weights)
+
+
+def fp8_quant_weight_128x128_batched(batch, mode="amax"):
+    """Quantize every weight of a WeightBatch in one launch, each exactly as
+    fp8_quant_weight_128x128 would; returns the batch's list of (q, s)."""
+    if not isinstance(batch, WeightBatch):
+        raise TypeError("batch must be a WeightBatch")
+    _lib.check("fp8_quant_weight_128x128_batched",
+               _lib.load().fp8_quant_weight_128x128_batched(
+                   ctypes.c_void_p(int(batch.jobs.data_ptr())), len(batch), batch.total_tiles, _mode(mode),
+                   _stream(batch.jobs)))
+    return batch.outs
 
 
 def _gemm(fn, a_q, a_s, b_q, b_s, out):

@@ -13,6 +13,7 @@ FP8Q_OK = 0
 STATUS_NAMES = {0: "FP8Q_OK", 1: "FP8Q_EINVAL", 2: "FP8Q_ESHAPE", 3: "FP8Q_EALIGN",
                 4: "FP8Q_EDEVICE", 5: "FP8Q_EHIP"}
 ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_weight_128x128",
+                "fp8_quant_weight_128x128_batched",
                 "fp8_blockscaled_gemm",
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
                 "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
@@ -47,6 +48,8 @@ def load():
     lib.fp8_rmsnorm_quant_1x128.restype = ci
     lib.fp8_quant_weight_128x128.argtypes = [p, i64, i64, p, p, ci, p]
     lib.fp8_quant_weight_128x128.restype = ci
+    lib.fp8_quant_weight_128x128_batched.argtypes = [p, i32, i64, ci, p]
+    lib.fp8_quant_weight_128x128_batched.restype = ci
     for name in ("fp8_quant_act_dual", "fp8_quant_weight_128x128_dual"):
         getattr(lib, name).argtypes = [p, i64, i64, p, p, p, p, ci, p]
         getattr(lib, name).restype = ci

@@ -110,6 +110,21 @@ fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, ui
                   __func__);
 }
 
+fp8q_status fp8_quant_weight_128x128_batched(const fp8q_weight_job *jobs, int32_t count, int64_t total_tiles,
+                                             int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(count >= 0 && total_tiles >= 0, FP8Q_EINVAL, "negative count or tile total");
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(total_tiles < ((int64_t)1 << 31), FP8Q_ESHAPE, "more than 2^31 - 1 tiles in one batch");
+  if (count == 0 || total_tiles == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(jobs != nullptr, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE((reinterpret_cast<uintptr_t>(jobs) & 7u) == 0, FP8Q_EALIGN, "job table must be 8-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_quant_weight_batched(jobs, count, total_tiles, mode, (hipStream_t)stream),
+                  __func__);
+}
+
 fp8q_status fp8_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, float *scales,
                                uint8_t *q_t, float *scales_t, int mode, void *stream) {
   g_last_error.clear();

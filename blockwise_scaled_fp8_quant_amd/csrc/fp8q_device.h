@@ -25,6 +25,21 @@ __device__ __forceinline__ uint4 load_stream16(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming stores, for codes that are written once and read only much later
+// (quantized weights): the non-temporal hint lets the write stream pass the
+// caches (measured on gfx950: ~6% more HBM bandwidth for the weight quantizer
+// than plain stores).  Activation codes, read by the very next GEMM, use
+// plain stores and may stay in the caches.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream8(void *p, uint2 v) {
+  const u32x2_t x = {v.x, v.y};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t *>(p));
+}
+__device__ __forceinline__ void store_stream16(void *p, uint4 v) {
+  const u32x4_t x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(p));
+}
+
 // bf16 halves of a 32-bit word -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

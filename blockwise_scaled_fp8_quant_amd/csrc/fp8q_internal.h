@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct fp8q_weight_job;  // include/fp8q.h
+
 namespace fp8q {
 
 hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
@@ -14,6 +16,11 @@ hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
 hipError_t launch_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
                                        uint8_t *q, float *s, int mode,
                                        hipStream_t stream);
+
+// Many weight matrices in one launch: jobs [count] in device memory,
+// total_tiles < 2^31 tiles in all.
+hipError_t launch_quant_weight_batched(const fp8q_weight_job *jobs, int32_t count, int64_t total_tiles,
+                                       int mode, hipStream_t stream);
 
 // pow2: every scale is a power of two and the matrix core applies it (E8M0
 // scale operands); otherwise the per-K-block scale fold runs on the VALU.

@@ -5,6 +5,7 @@
 // element, plus one fp32 scale per block.  Loads are 16 bytes per lane and
 // cover whole 128-byte lines; the block |max| is reduced in registers and
 // through DPP lane exchanges, never through memory.
+#include "../../include/fp8q.h"
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 
@@ -85,13 +86,11 @@ hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
 // ---------------------------------------------------------------------------
 constexpr int kWThreads = 256;
 
+// Tile (nb, kb) of w [N][K]; part holds kWThreads/16 floats of LDS.
 template <int kMode>
-__global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
-    const uint16_t *__restrict__ w, uint8_t *__restrict__ q,
-    float *__restrict__ scales, int64_t K, int64_t KB) {
-  __shared__ float part[kWThreads / 16];
-  const int64_t tile = blockIdx.x;
-  const int64_t nb = tile / KB, kb = tile - nb * KB;
+__device__ __forceinline__ void quant_weight_tile(const uint16_t *__restrict__ w, uint8_t *__restrict__ q,
+                                                  float *__restrict__ scales, int64_t K, int64_t nb, int64_t kb,
+                                                  int64_t tile, float *part) {
   const int c = threadIdx.x & 15;
   const int r0 = threadIdx.x >> 4;
   const uint16_t *base = w + (nb * 128 + r0) * K + kb * 128 + c * 8;
@@ -116,7 +115,68 @@ __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
   uint8_t *obase = q + (nb * 128 + r0) * K + kb * 128 + c * 8;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint2 *>(obase + (int64_t)(16 * i) * K) = quant_chunk<kMode>(p, v[i]);
+    store_stream8(obase + (int64_t)(16 * i) * K, quant_chunk<kMode>(p, v[i]));  // read by later GEMMs
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
+    const uint16_t *__restrict__ w, uint8_t *__restrict__ q,
+    float *__restrict__ scales, int64_t K, int64_t KB) {
+  __shared__ float part[kWThreads / 16];
+  const int64_t tile = blockIdx.x;
+  const int64_t nb = tile / KB, kb = tile - nb * KB;
+  quant_weight_tile<kMode>(w, q, scales, K, nb, kb, tile, part);
+}
+
+// ---------------------------------------------------------------------------
+// A whole set of weight matrices in one launch (the recalibration after every
+// policy update of page 1, "Leistungsgewinne in der Praxis", covers all linear
+// weights of the model at once).  Workgroup t quantizes tile t of the
+// concatenated tile sequence: its job is the last one whose tile_begin <= t,
+// found with one coalesced load of 64 jobs' tile_begin per round and a
+// ballot (no dependent search steps before the tile's own loads go out).  A
+// separate launch per matrix pays the start-up and drain of a launch each
+// time; here they are paid once.  The job table is caller data in device
+// memory: a tile whose job is inconsistent (shape not a multiple of 128, tile
+// outside the job's range) is skipped, so no access leaves a job's tensors.
+// ---------------------------------------------------------------------------
+template <int kMode>
+__global__ __launch_bounds__(kWThreads) void quant_weight_batched_kernel(const fp8q_weight_job *__restrict__ jobs,
+                                                                         int32_t count) {
+  __shared__ float part[kWThreads / 16];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  int32_t cnt = 0;
+  for (int32_t base = 0; base < count; base += 64) {
+    const int32_t j = base + lane;
+    const int64_t b = j < count ? jobs[j].tile_begin : 0;
+    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j < count && b <= t));
+  }
+  int32_t j = cnt - 1;
+  j = j < 0 ? 0 : j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const uint16_t *w = jobs[j].w;
+  uint8_t *q = jobs[j].q;
+  float *scales = jobs[j].scales;
+  const int64_t N = jobs[j].N, K = jobs[j].K, begin = jobs[j].tile_begin;
+  if (N < 0 || K <= 0 || (N & 127) != 0 || (K & 127) != 0) return;
+  const int64_t KB = K >> 7;
+  const int64_t tile = t - begin;
+  if (tile < 0 || tile >= (N >> 7) * KB) return;
+  const int64_t nb = tile / KB, kb = tile - nb * KB;
+  quant_weight_tile<kMode>(w, q, scales, K, nb, kb, tile, part);
+}
+
+hipError_t launch_quant_weight_batched(const fp8q_weight_job *jobs, int32_t count, int64_t total_tiles, int mode,
+                                       hipStream_t stream) {
+  if (count == 0 || total_tiles == 0) return hipSuccess;
+  if (mode == kModeAmax)
+    hipLaunchKernelGGL(quant_weight_batched_kernel<kModeAmax>, dim3((unsigned)total_tiles), dim3(kWThreads), 0,
+                       stream, jobs, count);
+  else
+    hipLaunchKernelGGL(quant_weight_batched_kernel<kModePow2>, dim3((unsigned)total_tiles), dim3(kWThreads), 0,
+                       stream, jobs, count);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
@@ -396,7 +456,12 @@ __global__ __launch_bounds__(kDThreads) void quant_dual_kernel(DualArgs a) {
     const int id = u * kDThreads + t;  // 16-byte chunk of the 128x128 transposed tile
     const int row = id >> 3, part = id & 7;
     const uint4 w = *reinterpret_cast<const uint4 *>(tq + row * kTPitch + part * 16);
-    *reinterpret_cast<uint4 *>(a.qt + (k0 + row) * Mp + m0 + part * 16) = w;
+    // weight codes stream out (read much later, by the backward GEMMs); the
+    // transposed activation codes stay cacheable for the GEMM that follows
+    if constexpr (kTile)
+      store_stream16(a.qt + (k0 + row) * Mp + m0 + part * 16, w);
+    else
+      *reinterpret_cast<uint4 *>(a.qt + (k0 + row) * Mp + m0 + part * 16) = w;
   }
 }
 

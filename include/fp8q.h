@@ -55,7 +55,7 @@ typedef enum fp8q_status {
     FP8Q_OK = 0,
     FP8Q_EINVAL = 1,  /* null pointer, negative size, unknown mode, G < 1 */
     FP8Q_ESHAPE = 2,  /* K not a positive multiple of 128 (or, for a GEMM, above 4194304), or N not a multiple of 128 */
-    FP8Q_EALIGN = 3,  /* a pointer not 16-byte aligned */
+    FP8Q_EALIGN = 3,  /* a pointer not 16-byte aligned (a batched job table: not 8-byte aligned) */
     FP8Q_EDEVICE = 4, /* no HIP device, or the current device is not gfx950 */
     FP8Q_EHIP = 5     /* the HIP runtime reported an error while enqueueing */
 } fp8q_status;
@@ -122,6 +122,45 @@ fp8q_status fp8_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma,
 fp8q_status fp8_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
                                      uint8_t *q, float *scales, int mode,
                                      void *stream);
+
+/*
+ * One matrix of a batched weight recalibration (fp8_quant_weight_128x128_batched).
+ *   w, q, scales  as the arguments of fp8_quant_weight_128x128 (device memory,
+ *                 16-byte aligned)
+ *   N, K          the matrix shape: N >= 0 and K > 0, both multiples of 128
+ *   tile_begin    the sum of (N/128)*(K/128) over the jobs before this one
+ */
+typedef struct fp8q_weight_job {
+    const uint16_t *w;
+    uint8_t *q;
+    float *scales;
+    int64_t N;
+    int64_t K;
+    int64_t tile_begin;
+} fp8q_weight_job;
+
+/*
+ * Recalibration of a whole set of weights in one launch (page 1,
+ * "Leistungsgewinne in der Praxis": every weight's scales are recomputed after
+ * each policy update).  Each job is quantized exactly as
+ * fp8_quant_weight_128x128 quantizes it, with the same bytes and scales; one
+ * launch for all of them pays a launch's start-up and drain once instead of
+ * once per matrix.
+ *   jobs         [count] fp8q_weight_job in DEVICE memory, read by the kernel
+ *                (build it once per set of weights and keep it; the library
+ *                holds no pointer to it after the call is enqueued)
+ *   count        number of jobs, >= 0
+ *   total_tiles  sum of (N/128)*(K/128) over the jobs, < 2^31
+ *   mode         fp8q_scale_mode, for every job
+ * The table is in device memory, so the host checks only count, total_tiles,
+ * mode and the table's alignment (8 bytes).  On the device a tile whose job
+ * has a shape that is not a positive multiple of 128, or which falls outside
+ * its job's range of tiles (tile_begin not the running sum), is skipped: its
+ * outputs are left as they were, and no access leaves a job's tensors.  Jobs
+ * must not write to one another's inputs.
+ */
+fp8q_status fp8_quant_weight_128x128_batched(const fp8q_weight_job *jobs, int32_t count,
+                                             int64_t total_tiles, int mode, void *stream);
 
 /*
  * Both quantized layouts of an activation (or activation gradient) in one

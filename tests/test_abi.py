@@ -28,7 +28,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_weight_128x128", "fp8_blockscaled_gemm",
+    for n in ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_weight_128x128",
+              "fp8_quant_weight_128x128_batched", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
               "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
@@ -72,6 +73,19 @@ def test_quantizer_argument_errors(lib, fn):
     assert f(GOOD, 0, 128, None, None, 0, None) == 0            # empty: no-op
     if fn == "fp8_quant_weight_128x128":
         assert f(GOOD, 100, 128, GOOD, GOOD, 0, None) == 2      # N % 128
+
+
+def test_batched_weight_quant_argument_errors(lib):
+    f = lib.fp8_quant_weight_128x128_batched
+    assert f(GOOD, -1, 4, 0, None) == 1                # negative count
+    assert f(GOOD, 2, -4, 0, None) == 1                # negative tile total
+    assert f(GOOD, 2, 4, 5, None) == 1                 # unknown mode
+    assert "mode" in _err(lib)
+    assert f(GOOD, 2, 1 << 31, 0, None) == 2           # more tiles than one grid holds
+    assert f(None, 2, 4, 0, None) == 1                 # null table
+    assert f(P(0x10004), 2, 4, 1, None) == 3           # table not 8-byte aligned
+    assert f(None, 0, 0, 0, None) == 0                 # empty batch: no-op
+    assert f(None, 3, 0, 1, None) == 0                 # no tiles: no-op
 
 
 @pytest.mark.parametrize("fn", ["fp8_blockscaled_gemm", "fp8_blockscaled_gemm_pow2"])
