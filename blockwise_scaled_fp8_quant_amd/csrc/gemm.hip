@@ -381,28 +381,45 @@ __device__ __forceinline__ uint32_t e8m0_of(float s, uint32_t &bad, uint32_t bit
   return e & 0xFFu;
 }
 
+// The raw scale words of a K block as read from LDS: the lane's four token
+// rows' scales and the weight-side scale(s).
+struct HeadRaw {
+  float4 sa4;
+  float sb;
+  float4 lo, hi;  // per-row power-of-two weight-side scales (kPow2 && kBRow)
+};
+
+// Everything of a K block's fragments except the token sub-tiles, in two
+// steps: the LDS reads (first weight sub-tile, scale words), then the scale
+// arithmetic (combined per-lane scales, or E8M0 bytes), which can wait until
+// the reads have landed without holding up other work.
 template <class C, class V>
-__device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
-                                           BlockFrags &f) {
-  constexpr bool kPow2 = V::kPow2;
-  const float4 sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
-  const float sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
+__device__ __forceinline__ void read_head(const uint8_t *buf, int wn, int wm, int lane, BlockFrags &f, HeadRaw &h) {
 #pragma unroll
   for (int a = 0; a < kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
-  if constexpr (kPow2) {
+  h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
+  if constexpr (V::kPow2 && V::kBRow) {
+    const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
+    h.lo = rp[0];
+    h.hi = rp[1];
+  } else {
+    h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
+  }
+}
+
+template <class V>
+__device__ __forceinline__ void finish_head(const HeadRaw &h, BlockFrags &f) {
+  const float4 sa4 = h.sa4;
+  if constexpr (V::kPow2) {
     f.ea = e8m0_of(sa4.x, f.bad, 1u) | (e8m0_of(sa4.y, f.bad, 2u) << 8) | (e8m0_of(sa4.z, f.bad, 4u) << 16) |
            (e8m0_of(sa4.w, f.bad, 8u) << 24);
     if constexpr (V::kBRow) {
-      const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
-      const float4 lo = rp[0], hi = rp[1];
-      f.ebr[0] = e8m0_of(lo.x, f.bad, 1u << 16) | (e8m0_of(lo.y, f.bad, 1u << 17) << 8) |
-                 (e8m0_of(lo.z, f.bad, 1u << 18) << 16) | (e8m0_of(lo.w, f.bad, 1u << 19) << 24);
-      f.ebr[1] = e8m0_of(hi.x, f.bad, 1u << 20) | (e8m0_of(hi.y, f.bad, 1u << 21) << 8) |
-                 (e8m0_of(hi.z, f.bad, 1u << 22) << 16) | (e8m0_of(hi.w, f.bad, 1u << 23) << 24);
+      f.ebr[0] = e8m0_of(h.lo.x, f.bad, 1u << 16) | (e8m0_of(h.lo.y, f.bad, 1u << 17) << 8) |
+                 (e8m0_of(h.lo.z, f.bad, 1u << 18) << 16) | (e8m0_of(h.lo.w, f.bad, 1u << 19) << 24);
+      f.ebr[1] = e8m0_of(h.hi.x, f.bad, 1u << 20) | (e8m0_of(h.hi.y, f.bad, 1u << 21) << 8) |
+                 (e8m0_of(h.hi.z, f.bad, 1u << 22) << 16) | (e8m0_of(h.hi.w, f.bad, 1u << 23) << 24);
     } else {
-      f.eb = e8m0_of(sb, f.bad, 16u);
+      f.eb = e8m0_of(h.sb, f.bad, 16u);
     }
   } else if constexpr (V::kBRow) {
     // the weight-side scale differs between a lane's four outputs: the folds
@@ -412,11 +429,21 @@ __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn,
     f.scl[2] = sa4.z;
     f.scl[3] = sa4.w;
   } else {
-    f.scl[0] = sa4.x * sb;
-    f.scl[1] = sa4.y * sb;
-    f.scl[2] = sa4.z * sb;
-    f.scl[3] = sa4.w * sb;
+    f.scl[0] = sa4.x * h.sb;
+    f.scl[1] = sa4.y * h.sb;
+    f.scl[2] = sa4.z * h.sb;
+    f.scl[3] = sa4.w * h.sb;
   }
+}
+
+template <class C, class V>
+__device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
+                                           BlockFrags &f) {
+  HeadRaw h;
+  read_head<C, V>(buf, wn, wm, lane, f, h);
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
+  finish_head<V>(h, f);
 }
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
@@ -495,10 +522,15 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 // With per-row weight-side scales (kBRow) the four scales of sub-tile row ni
 // are read with its weight fragment (a ring of two rows, as a fold trails its
 // MFMA by two) and each fold multiplies them in.
-template <class C, class V>
+//
+// Only MFMAs j < kJEnd are issued here.  With kJEnd = 28 the last row's weight
+// fragment comes back in wlast and its four MFMAs are left to block_boundary,
+// which issues them after the barrier, between the LDS reads of the next
+// block's token fragments.
+template <class C, class V, int kJEnd = kMfmaPerBlock>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], float4 (&sbq)[2],
-                                          const StageDma &dma) {
+                                          const StageDma &dma, v8i &wlast) {
   constexpr bool kPow2 = V::kPow2;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int R = kWAhead + 1;
@@ -506,7 +538,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
 #pragma unroll
   for (int a = 0; a < kWAhead; ++a) wf[a] = f.wf[a];
 #pragma unroll
-  for (int j = 0; j < kMfmaPerBlock; ++j) {
+  for (int j = 0; j < kJEnd; ++j) {
     const int ni = j / kSubM, mi = j % kSubM;
     if (mi == 0) {
       // the reads of sub-tile ni+kWAhead go out before any MFMA of row ni
@@ -546,6 +578,12 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       }
     }
   }
+  if constexpr (V::kBRow && !kPow2 && kJEnd < kMfmaPerBlock) {
+    // the row scales of the deferred last row (its slot's previous row has
+    // had all its folds by now)
+    constexpr int ni = kJEnd / kSubM;
+    sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ni = 0; ni < kSubN; ++ni)
@@ -553,7 +591,43 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
     for (int mi = 0; mi < kSubM; ++mi) pin(acc[ni][mi]);
 #pragma unroll
   for (int r = 0; r < kRing; ++r) pin(p[r]);
+  wlast = wf[(kSubN - 1) % R];
 }
+
+// The MFMA of sub-tile (ni, mi) = j with the block's scales: straight into
+// acc (power-of-two scales), or into the partial-product ring.
+template <class V>
+__device__ __forceinline__ void mma_one(int ni, int mi, int j, const v8i &w, const BlockFrags &f,
+                                        v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing]) {
+  if constexpr (V::kPow2) {
+    if constexpr (V::kBRow) {
+      const uint32_t eb = f.ebr[ni >> 2];
+      switch (ni & 3) {
+        case 0: acc[ni][mi] = mfma_pow2_rows<0>(w, f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+        case 1: acc[ni][mi] = mfma_pow2_rows<1>(w, f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+        case 2: acc[ni][mi] = mfma_pow2_rows<2>(w, f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+        default: acc[ni][mi] = mfma_pow2_rows<3>(w, f.xf[mi], acc[ni][mi], eb, f.ea, mi); break;
+      }
+    } else {
+      acc[ni][mi] = mfma_pow2(w, f.xf[mi], acc[ni][mi], f.eb, f.ea, mi);
+    }
+  } else {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, f.xf[mi], zero, 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// The scale fold of partial product jj.
+template <class V>
+__device__ __forceinline__ void fold_one(int jj, const float (&scl)[kSubM], v4f (&acc)[kSubN][kSubM],
+                                         const v4f (&p)[kRing], const float4 (&sbq)[2]) {
+  if constexpr (V::kBRow)
+    fold_rows(acc[jj / kSubM][jj % kSubM], p[jj % kRing], scl[jj % kSubM], sbq[(jj / kSubM) & 1]);
+  else
+    fold1(acc[jj / kSubM][jj % kSubM], p[jj % kRing], scl[jj % kSubM]);
+}
+
+constexpr int kSchedDsRead = 0x100;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -607,6 +681,48 @@ __device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
   barrier_nofence();
 }
 
+// The end of K block k and the start of block k+1, software-pipelined across
+// the barrier: the four MFMAs of block k's last weight row (operands already
+// in registers) are issued after the barrier, each followed by the LDS reads
+// of one of block k+1's token sub-tiles, so the matrix core has work while
+// those reads are in flight instead of idling until they land.  Every LDS
+// read of block k has landed before this wave arrives at the barrier (after
+// which the DMA of block k+2 may overwrite block k's buffer).
+template <class C, class V>
+__device__ __forceinline__ void block_boundary(const uint8_t *nbuf, int knext, int KB, int wave, int wn, int wm,
+                                               int lane, BlockFrags &f, const v8i &wlast,
+                                               v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const float4 (&sbq)[2]) {
+  constexpr bool kPow2 = V::kPow2;
+  constexpr int ni = kSubN - 1;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wait_block<C, V>(knext, KB, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  BlockFrags g;
+  g.bad = f.bad;
+  HeadRaw h;
+  read_head<C, V>(nbuf, wn, wm, lane, g, h);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) {
+    const int j = kMfmaPerBlock - kSubM + mi;
+    mma_one<V>(ni, mi, j, wlast, f, acc, p);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (!kPow2) {
+      fold_one<V>(j - 2, f.scl, acc, p, sbq);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, V::kBRow ? 8 : 4, 0);
+    }
+    g.xf[mi] = frag(nbuf + C::kOffA, wm * 64 + mi * 16, lane);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+  if constexpr (!kPow2) {
+    fold_one<V>(kMfmaPerBlock - 2, f.scl, acc, p, sbq);
+    fold_one<V>(kMfmaPerBlock - 1, f.scl, acc, p, sbq);
+  }
+  finish_head<V>(h, g);
+  __builtin_amdgcn_sched_barrier(0);
+  f = g;
+}
+
 struct TileOut {
   uint16_t *y;   // bf16: tile origin of Y [M][N]
   uint8_t *yq;   // E4M3: tile origin of Yq [M][N]
@@ -650,31 +766,28 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
   int cur = 0;  // stage buffer of block k
   StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
                C::kStages - 1 < KB};
-  for (int k = 0; k < KB; ++k) {
-    mma_steps<C, V>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma);
-    const float s30 = f.scl[(kMfmaPerBlock - 2) % kSubM];
-    const float s31 = f.scl[(kMfmaPerBlock - 1) % kSubM];
-    if (k + 1 < KB) {
-      // Block k's buffer is free once every wave is past this barrier; it
-      // receives block k + kStages.
-      wait_block<C, V>(k + 1, KB, wave);
-      // block k + kStages goes into block k's buffer during the next block
-      dma.k = k + C::kStages;
-      dma.buf = lds + cur * C::kStageBytes;
-      dma.on = k + C::kStages < KB;
-      cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-      load_block<C, V>(lds + cur * C::kStageBytes, wave, wn, wm, lane, f);
-    }
-    if constexpr (!kPow2) {
-      constexpr int j30 = kMfmaPerBlock - 2, j31 = kMfmaPerBlock - 1;
-      if constexpr (V::kBRow) {
-        fold_rows(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30, sbq[(j30 / kSubM) & 1]);
-        fold_rows(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31, sbq[(j31 / kSubM) & 1]);
-      } else {
-        fold1(acc[j30 / kSubM][j30 % kSubM], p[j30 % kRing], s30);
-        fold1(acc[j31 / kSubM][j31 % kSubM], p[j31 % kRing], s31);
-      }
-    }
+  v8i wlast;
+  for (int k = 0; k + 1 < KB; ++k) {
+    mma_steps<C, V, kMfmaPerBlock - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+    // Block k's buffer is free once every wave is past the barrier in
+    // block_boundary; block k + kStages goes into it during the next block.
+    dma.k = k + C::kStages;
+    dma.buf = lds + cur * C::kStageBytes;
+    dma.on = k + C::kStages < KB;
+    cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
+    block_boundary<C, V>(lds + cur * C::kStageBytes, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
+  }
+  // the last block: its last row's MFMAs and the trailing folds, no barrier
+  mma_steps<C, V, kMfmaPerBlock - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) {
+    const int j = kMfmaPerBlock - kSubM + mi;
+    mma_one<V>(kSubN - 1, mi, j, wlast, f, acc, p);
+    if constexpr (!kPow2) fold_one<V>(j - 2, f.scl, acc, p, sbq);
+  }
+  if constexpr (!kPow2) {
+    fold_one<V>(kMfmaPerBlock - 2, f.scl, acc, p, sbq);
+    fold_one<V>(kMfmaPerBlock - 1, f.scl, acc, p, sbq);
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   // A scale outside the power-of-two contract turns the outputs that depend
