@@ -29,7 +29,7 @@
 //  - Rows are 128 B in LDS; 16-byte chunks are XOR-swizzled by row so that the
 //    fragment reads (two ds_read_b128 per lane) hit distinct banks.
 //  - Workgroup ids are remapped so that each XCD (own L2) gets a contiguous
-//    range of tiles, enumerated in groups of 4 weight panels so that the tiles
+//    range of tiles, enumerated in groups of 8 weight panels so that the tiles
 //    running at the same time share operand panels.
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
@@ -46,7 +46,7 @@ constexpr int kBK = 128;  // one scale block of K
 constexpr int kSubN = 8;  // 16-row MFMA sub-tiles per wave along n (128 rows)
 constexpr int kSubM = 4;  // 16-col MFMA sub-tiles per wave along m (64 rows)
 constexpr int kNumXcd = 8;
-constexpr int kGroupN = 4;  // weight panels per rasterization group
+constexpr int kGroupN = 8;  // weight panels per rasterization group
 
 // Output of a tile: bf16 Y, or Y quantized to E4M3 in 1x128 blocks along N
 // with the activation quantizer's rule (kOut = its scale mode).
@@ -75,13 +75,20 @@ struct Variant {
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
 
-template <int kBM_, int kWaves_, int kStages_, int kLoaders_>
+template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_>
 struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
   static constexpr int kStages = kStages_;
+  // The n step of a K block at which the waves issue the DMA of a later
+  // block.  With two stages, issuing it mid-block (step 4) keeps its LDS
+  // writes away from the fragment reads that start each block: +8% (amax)
+  // and +12% (power-of-two) on the dense Llama shapes against step 0; step 5
+  // and later leave the DMA unfinished at the block's end.
   // The last kLoaders waves issue the stage DMA.
   static constexpr int kLoaders = kLoaders_;
+  static constexpr int kDmaStep = kDmaStep_;
+  static_assert(kDmaStep < kSubN - 1, "the DMA goes out in one of the n steps before the deferred last row");
   static constexpr int kFirstLoader = kWaves - kLoaders;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kWavesM = kWaves / 2;  // waves along m; 2 along n
@@ -103,8 +110,8 @@ struct TileCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-using CfgLarge = TileCfg<256, 8, 2, 8>;
-using CfgSmall = TileCfg<128, 4, 3, 4>;
+using CfgLarge = TileCfg<256, 8, 2, 8, 4>;
+using CfgSmall = TileCfg<128, 4, 3, 4, 0>;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -532,6 +539,9 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], float4 (&sbq)[2],
                                           const StageDma &dma, v8i &wlast) {
   constexpr bool kPow2 = V::kPow2;
+  // per-row weight scales with VALU folds hold the most registers; issuing
+  // their DMA mid-block made the compiler spill inside the loop
+  constexpr int kDmaStep = (V::kBRow && !kPow2) ? 0 : C::kDmaStep;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int R = kWAhead + 1;
   v8i wf[R];
@@ -546,7 +556,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       if (ni + kWAhead < kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * 128 + (ni + kWAhead) * 16, lane);
       if constexpr (V::kBRow)
         sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
-      if (ni == 0 && dma.on && dma.wave >= C::kFirstLoader)
+      if (ni == kDmaStep && dma.on && dma.wave >= C::kFirstLoader)
         issue_stage<C, V>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
       __builtin_amdgcn_sched_barrier(0);
     }
