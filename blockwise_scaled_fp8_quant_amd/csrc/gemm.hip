@@ -80,11 +80,13 @@ struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
   static constexpr int kStages = kStages_;
-  // The n step of a K block at which the waves issue the DMA of a later
-  // block.  With two stages, issuing it mid-block (step 4) keeps its LDS
-  // writes away from the fragment reads that start each block: +8% (amax)
-  // and +12% (power-of-two) on the dense Llama shapes against step 0; step 5
-  // and later leave the DMA unfinished at the block's end.
+  // The n step of a K block at which the waves issue the DMA of the next
+  // block.  Issuing it mid-block keeps its LDS writes away from the fragment
+  // reads that start each block.  256-row tiles (8 waves): step 4, +8% (amax)
+  // and +12% (power-of-two) on the dense Llama shapes against step 0; at step
+  // 5 and later the DMA is not finished when the block ends.  128-row tiles
+  // (4 waves, one per SIMD, so each K block takes longer per wave): step 5
+  // with two stages, +22% against three stages and step 0.
   // The last kLoaders waves issue the stage DMA.
   static constexpr int kLoaders = kLoaders_;
   static constexpr int kDmaStep = kDmaStep_;
@@ -111,7 +113,7 @@ struct TileCfg {
 };
 
 using CfgLarge = TileCfg<256, 8, 2, 8, 4>;
-using CfgSmall = TileCfg<128, 4, 3, 4, 0>;
+using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
