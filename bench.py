@@ -120,9 +120,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens per layer in the oracle's CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,norm,backward,recal,moe,dispatch,attention,bf16,cpu",
-                    help="extra measurements after the step (comma list of pow2, fused, backward, recal, "
-                         "moe, dispatch, attention, bf16, cpu)")
+    ap.add_argument("--sections", default="pow2,fused,norm,backward,recal,moe,dispatch,attention,smallm,bf16,cpu",
+                    help="extra measurements after the step (comma list of pow2, fused, norm, backward, recal, "
+                         "moe, dispatch, attention, smallm, bf16, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -301,6 +301,8 @@ def main():
         result["attention_decode"] = attention(fp8q, synth, torch, dev, reps)
     if "dispatch" in sections:
         result["moe_dispatch"] = dispatch(fp8q, synth, torch, dev, reps)
+    if "smallm" in sections:
+        result["small_m"] = small_m(fp8q, layers, torch, dev, reps)
     if "bf16" in sections:
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
     if "cpu" in sections:
@@ -308,6 +310,28 @@ def main():
             del l["w"]
         result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def small_m(fp8q, layers, torch, dev, reps, M=2048):
+    """The four layers at 2048 tokens: O and down then have too few 256x256
+    tiles to fill the GPU and run on 128-row tiles."""
+    out = {}
+    for l in layers:
+        x = torch.randn((M, l["K"]), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        aq, as_ = fp8q.fp8_quant_act_1x128(x)
+        y = torch.empty((M, l["N"]), dtype=torch.bfloat16, device=dev)
+
+        def g(aq=aq, as_=as_, l=l, y=y):
+            fp8q.fp8_blockscaled_gemm(aq, as_, l["bq"], l["bs"], out=y)
+        g()
+        t = time_loop(g, reps, torch)
+        tiles256 = -(-M // 256) * -(-l["N"] // 256)
+        tiles128 = -(-M // 128) * -(-l["N"] // 256)
+        rows = 256 if -(-tiles256 // 256) * 10 <= -(-tiles128 // 256) * 7 else 128  # the library's choice
+        out[l["name"]] = {"gemm_us": round(t * 1e6, 2), "tflops": round(2.0 * M * l["N"] * l["K"] / t / 1e12, 1),
+                          "tile_rows": rows}
+        log(f"M={M} {l['name']}: {out[l['name']]}")
+    return {"tokens": M, "per_layer": out}
 
 
 def pow2_gemm(fp8q, layers, torch, M, reps):

@@ -1142,9 +1142,15 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n};
-  // Large tiles when they still give at least one tile per CU.
+  // The tile shape with the shorter estimated time: rounds of tiles over the
+  // 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a 256-row
+  // one (measured on the Llama shapes).  At 4096 tokens QKV's 384 large tiles
+  // (two rounds) beat its 768 small ones (three); at 2048 tokens its 192
+  // large tiles (one round) beat 384 small ones (+37%), while O and down at
+  // 2048 tokens (128 large tiles, half the CUs idle) take small tiles.
   const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
-  if (large_tiles >= 256) {
+  const int64_t small_tiles = (M + CfgSmall::kBM - 1) / CfgSmall::kBM * tiles_n;
+  if ((large_tiles + 255) / 256 * 10 <= (small_tiles + 255) / 256 * 7) {
     p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
     return launch<CfgLarge, V>(p, stream);
   }
