@@ -1017,6 +1017,7 @@ struct GemmParams {
   int64_t slots_m;
   int32_t G;
   int32_t tiles_n;
+  int64_t ldy;  // row stride of y (bf16 output): N, or the full width for a column slice
 };
 
 __device__ __forceinline__ int64_t clamp_off(const int32_t *off, int32_t g, int64_t M) {
@@ -1108,7 +1109,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   t.n_valid = n_valid;
   TileOut o{nullptr, nullptr, nullptr};
   if constexpr (kOut == kOutBf16) {
-    o.y = p.y + m0 * p.N + n0;
+    o.y = p.y + m0 * p.ldy + n0;
   } else if constexpr (V::kSwiGLU) {  // h [M][N/2]: this tile's 128 columns start at n0/2
     o.yq = p.yq + m0 * (p.N >> 1) + (n0 >> 1);
     o.ys = p.ys + m0 * (p.N >> 8) + (n0 >> 8);
@@ -1116,7 +1117,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     o.yq = p.yq + m0 * p.N + n0;
     o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
   }
-  gemm_tile<C, V>(t, o, p.N, lds);
+  gemm_tile<C, V>(t, o, kOut == kOutBf16 ? p.ldy : p.N, lds);
 }
 
 template <class C, class V>
@@ -1141,20 +1142,47 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   using V = Variant<false, kPow2, kOut, false, kBRow, kSwiGLU>;
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n};
-  // The tile shape with the shorter estimated time: rounds of tiles over the
-  // 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a 256-row
-  // one (measured on the Llama shapes).  At 4096 tokens QKV's 384 large tiles
-  // (two rounds) beat its 768 small ones (three); at 2048 tokens its 192
-  // large tiles (one round) beat 384 small ones (+37%), while O and down at
-  // 2048 tokens (128 large tiles, half the CUs idle) take small tiles.
-  const int64_t large_tiles = (M + CfgLarge::kBM - 1) / CfgLarge::kBM * tiles_n;
-  const int64_t small_tiles = (M + CfgSmall::kBM - 1) / CfgSmall::kBM * tiles_n;
-  if ((large_tiles + 255) / 256 * 10 <= (small_tiles + 255) / 256 * 7) {
-    p.slots_m = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
+  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N};
+  // The tile shapes with the shortest estimated time: rounds of tiles over
+  // the 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a
+  // 256-row one (measured on the Llama shapes).  A bf16 output may also be
+  // split by weight panels: the first n1 panels on 256-row tiles, the rest on
+  // 128-row tiles, as two launches into column slices of Y.  At 4096 tokens
+  // QKV's 24 panels make 384 large tiles (two rounds, the second half
+  // empty); 16 panels on large tiles (one round) and 8 on small ones (one
+  // round) cost 1.7 instead of 2.  At 2048 tokens QKV's 192 large tiles (one
+  // round) beat 384 small ones (+37%), while O and down (128 large tiles,
+  // half the CUs idle) take small tiles.
+  const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
+  const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  auto cost = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
+    return (mt_large * n1 + 255) / 256 * 10 + (mt_small * (tiles_n - n1) + 255) / 256 * 7;
+  };
+  int64_t n1 = cost(tiles_n) <= cost(0) ? tiles_n : 0;
+  if constexpr (kOut == kOutBf16) {
+    for (int64_t c = 1; c < tiles_n; ++c)
+      if (cost(c) < cost(n1)) n1 = c;
+  }
+  if (n1 == tiles_n) {
+    p.slots_m = mt_large;
     return launch<CfgLarge, V>(p, stream);
   }
-  p.slots_m = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  if (n1 > 0) {
+    // panels [0, n1) on 256-row tiles, then the rest on 128-row tiles
+    const int64_t n_off = n1 * kBN;
+    GemmParams q = p;
+    q.N = n_off;
+    q.tiles_n = (int32_t)n1;
+    q.slots_m = mt_large;
+    hipError_t e = launch<CfgLarge, V>(q, stream);
+    if (e != hipSuccess) return e;
+    p.b_q = b_q + n_off * K;
+    p.b_s = b_s + (kBRow ? n_off : n_off / 128) * (K / kBK);
+    p.y = y + n_off;
+    p.N = N - n_off;
+    p.tiles_n = (int32_t)(tiles_n - n1);
+  }
+  p.slots_m = mt_small;
   return launch<CfgSmall, V>(p, stream);
 }
 
@@ -1165,7 +1193,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
   using V = Variant<true, kPow2, kOutBf16, kGather>;
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n, N};
   // 256-row tiles once the average group fills one; their ragged last tile
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {

@@ -158,3 +158,39 @@ def test_wide_shapes_ragged(M, N, K):
     ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 20000)])
     ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms, ns)
     gemm_tolerance_check(y[ms, ns], ref, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("variant", ["amax", "pow2", "per_row_scales"])
+def test_split_by_weight_panels(variant):
+    """Shapes whose 256x256 tiles would leave a partly empty last round are
+    split by weight panels: the first panels on 256-row tiles, the rest on
+    128-row tiles, as two launches into column slices of Y (4000 x 6016:
+    16 panels + 7.5 panels, ragged tokens and a half last panel).  Whole rows
+    and scattered elements against the oracle, for the amax and power-of-two
+    GEMMs and for the GEMM with one scale per row on both operands."""
+    require_gpu()
+    fp8q = lib()
+    M, N, K = 4000, 6016, 256
+    mode = 1 if variant == "pow2" else 0
+    if variant == "per_row_scales":
+        x = synth.normal_bf16((M, K), 1.0, synth.seed_of(10, 77, 0), outlier_frac=0.01)
+        w = synth.normal_bf16((N, K), 0.02, synth.seed_of(10, 77, 1))
+        aq, as_ = oracle.quant_act_1x128(synth.bf16_bits(x))
+        bq, bs = oracle.quant_act_1x128(synth.bf16_bits(w))
+    else:
+        aq, as_, bq, bs = _quantized(M, N, K, seed=77, outliers=0.01, mode=mode)
+    fn = {"amax": fp8q.fp8_blockscaled_gemm, "pow2": fp8q.fp8_blockscaled_gemm_pow2,
+          "per_row_scales": fp8q.fp8_blockscaled_gemm_wgrad}[variant]
+    say("gemm split by panels", variant, M, N, K)
+    y = fn(_dev_u8(aq), _dev_f32(as_), _dev_u8(bq), _dev_f32(bs))
+    torch.cuda.synchronize()
+    y = host_bf16_as_f64(y)
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 3999], rng.integers(0, M, 5)]))
+    ms = np.concatenate([np.repeat(rows, N), rng.integers(0, M, 20000)])
+    ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 20000)])
+    if variant == "per_row_scales":
+        ref = oracle.gemm_wgrad_sampled_f64(aq, as_, bq, bs, ms, ns)
+    else:
+        ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms, ns)
+    gemm_tolerance_check(y[ms, ns], ref, f"split {variant}")
