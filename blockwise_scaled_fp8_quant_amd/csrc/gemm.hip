@@ -75,7 +75,7 @@ struct Variant {
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
 
-template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_>
+template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_, int kWAhead_ = 1>
 struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
@@ -90,6 +90,8 @@ struct TileCfg {
   // The last kLoaders waves issue the stage DMA.
   static constexpr int kLoaders = kLoaders_;
   static constexpr int kDmaStep = kDmaStep_;
+  // Weight sub-tiles whose LDS reads go out ahead of their MFMAs.
+  static constexpr int kWAhead = kWAhead_;
   static_assert(kDmaStep < kSubN - 1, "the DMA goes out in one of the n steps before the deferred last row");
   static constexpr int kFirstLoader = kWaves - kLoaders;
   static constexpr int kThreads = 64 * kWaves;
@@ -364,11 +366,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Fragments of one K block that a wave keeps in registers: the four token
 // sub-tiles (B operands), the first weight sub-tile (A operand) and the four
 // combined scales a_s[row] * b_s of this lane's token rows.
-constexpr int kWAhead = 1;  // weight sub-tiles read ahead of their MFMAs
+constexpr int kMaxWAhead = 3;  // weight sub-tiles read ahead of their MFMAs, at most
 
 struct BlockFrags {
   v8i xf[kSubM];
-  v8i wf[kWAhead];  // the block's first weight sub-tiles
+  v8i wf[kMaxWAhead];  // the block's first weight sub-tiles (TileCfg::kWAhead of them)
   float scl[kSubM];
   // power-of-two scales: E8M0 exponent bytes (token rows mi = 0..3 in byte mi;
   // the weight block's), and which of them (bit mi; bit 4: the weight
@@ -405,7 +407,7 @@ struct HeadRaw {
 template <class C, class V>
 __device__ __forceinline__ void read_head(const uint8_t *buf, int wn, int wm, int lane, BlockFrags &f, HeadRaw &h) {
 #pragma unroll
-  for (int a = 0; a < kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
+  for (int a = 0; a < C::kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
   h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   if constexpr (V::kPow2 && V::kBRow) {
     const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
@@ -545,6 +547,8 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
   // their DMA mid-block made the compiler spill inside the loop
   constexpr int kDmaStep = (V::kBRow && !kPow2) ? 0 : C::kDmaStep;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kWAhead = C::kWAhead;
+  static_assert(kWAhead >= 1 && kWAhead <= kMaxWAhead, "weight read-ahead");
   constexpr int R = kWAhead + 1;
   v8i wf[R];
 #pragma unroll
