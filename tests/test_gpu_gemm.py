@@ -194,3 +194,21 @@ def test_split_by_weight_panels(variant):
     else:
         ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms, ns)
     gemm_tolerance_check(y[ms, ns], ref, f"split {variant}")
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 6144, 256), (2048, 4096, 384), (2000, 4096, 128)])
+def test_tile_choice_at_2048_tokens(M, N, K):
+    """At 2048 tokens the tile shape follows the estimated rounds: QKV-wide
+    outputs (192 tiles of 256 x 256, one round) on 256-row tiles, O-wide ones
+    (128 such tiles) on 128-row tiles.  Whole rows and scattered elements
+    against the oracle."""
+    require_gpu()
+    aq, as_, bq, bs = _quantized(M, N, K, seed=M + 3 * N + K, outliers=0.01)
+    say("gemm tile choice", M, N, K)
+    y = _run_gemm(aq, as_, bq, bs)
+    rng = np.random.default_rng(M + N + K)
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, M - 1], rng.integers(0, M, 5)]))
+    ms = np.concatenate([np.repeat(rows, N), rng.integers(0, M, 20000)])
+    ns = np.concatenate([np.tile(np.arange(N), rows.size), rng.integers(0, N, 20000)])
+    ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms, ns)
+    gemm_tolerance_check(y[ms, ns], ref, f"{M}x{N}x{K}")
