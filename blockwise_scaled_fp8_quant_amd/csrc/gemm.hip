@@ -43,7 +43,7 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kBN = 256;  // weight rows per tile
 constexpr int kBK = 128;  // one scale block of K
-constexpr int kSubN = 8;  // 16-row MFMA sub-tiles per wave along n (128 rows)
+constexpr int kSubN = 8;  // 16-row MFMA sub-tiles per wave along n, at most (128 rows)
 constexpr int kSubM = 4;  // 16-col MFMA sub-tiles per wave along m (64 rows)
 constexpr int kNumXcd = 8;
 constexpr int kGroupN = 8;  // weight panels per rasterization group
@@ -75,7 +75,7 @@ struct Variant {
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
 
-template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_, int kWAhead_ = 1>
+template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_, int kWAhead_ = 1, int kWavesN_ = 2>
 struct TileCfg {
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
@@ -92,10 +92,16 @@ struct TileCfg {
   static constexpr int kDmaStep = kDmaStep_;
   // Weight sub-tiles whose LDS reads go out ahead of their MFMAs.
   static constexpr int kWAhead = kWAhead_;
+  // Waves along n: 2 (128 weight rows each) or 4 (64 each); the rest along m.
+  static constexpr int kWavesN = kWavesN_;
+  static constexpr int kWaveN = kBN / kWavesN;  // weight rows per wave
+  static constexpr int kSubN = kWaveN / 16;     // MFMA sub-tiles per wave along n
+  static constexpr int kMfma = kSubN * kSubM;   // MFMAs per wave and K block
+  static_assert(kWavesN == 2 || kWavesN == 4, "waves along n");
   static_assert(kDmaStep < kSubN - 1, "the DMA goes out in one of the n steps before the deferred last row");
   static constexpr int kFirstLoader = kWaves - kLoaders;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kWavesM = kWaves / 2;  // waves along m; 2 along n
+  static constexpr int kWavesM = kWaves / kWavesN;  // waves along m
   static_assert(kBM == 64 * kWavesM, "each wave owns 64 token rows");
   static constexpr int kBytesB = kBN * kBK;        // weight tile
   static constexpr int kBytesA = kBM * kBK;        // token tile
@@ -116,6 +122,12 @@ struct TileCfg {
 
 using CfgLarge = TileCfg<256, 8, 2, 8, 4>;
 using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
+// 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD) for
+// bf16 outputs without per-row weight scales, whose epilogues do not need a
+// wave to hold 128 weight rows.
+using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
+template <class V>
+using SmallCfg = typename std::conditional<V::kOut == kOutBf16 && !V::kBRow && !V::kSwiGLU, CfgSmall8, CfgSmall>::type;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -407,14 +419,15 @@ struct HeadRaw {
 template <class C, class V>
 __device__ __forceinline__ void read_head(const uint8_t *buf, int wn, int wm, int lane, BlockFrags &f, HeadRaw &h) {
 #pragma unroll
-  for (int a = 0; a < C::kWAhead; ++a) f.wf[a] = frag(buf, wn * 128 + a * 16, lane);
+  for (int a = 0; a < C::kWAhead; ++a) f.wf[a] = frag(buf, wn * C::kWaveN + a * 16, lane);
   h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   if constexpr (V::kPow2 && V::kBRow) {
+    static_assert(C::kWaveN == 128, "per-row power-of-two weight scales: 128 weight rows per wave");
     const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
     h.lo = rp[0];
     h.hi = rp[1];
   } else {
-    h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
+    h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + ((wn * C::kWaveN) >> 7) * 4);  // the wave's 128-row block
   }
 }
 
@@ -468,7 +481,6 @@ constexpr int kSchedMfma = 0x008;
 // to the caller, which issues them after requesting the next block's
 // fragments so that the LDS latency at the block boundary overlaps FMAs.
 constexpr int kRing = 3;
-constexpr int kMfmaPerBlock = kSubN * kSubM;
 
 // acc + A*B with the E8M0 scale eb on every row of A (one weight block) and,
 // on column j of B, byte `sel` of the lane's ea (its token row's exponent).
@@ -538,7 +550,7 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 // fragment comes back in wlast and its four MFMAs are left to block_boundary,
 // which issues them after the barrier, between the LDS reads of the next
 // block's token fragments.
-template <class C, class V, int kJEnd = kMfmaPerBlock>
+template <class C, class V, int kJEnd>
 __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
                                           v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], float4 (&sbq)[2],
                                           const StageDma &dma, v8i &wlast) {
@@ -549,6 +561,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int kWAhead = C::kWAhead;
   static_assert(kWAhead >= 1 && kWAhead <= kMaxWAhead, "weight read-ahead");
+  static_assert(!V::kBRow || C::kWaveN == 128, "per-row weight scales: 128 weight rows per wave");
   constexpr int R = kWAhead + 1;
   v8i wf[R];
 #pragma unroll
@@ -559,7 +572,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
     if (mi == 0) {
       // the reads of sub-tile ni+kWAhead go out before any MFMA of row ni
       __builtin_amdgcn_sched_barrier(0);
-      if (ni + kWAhead < kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * 128 + (ni + kWAhead) * 16, lane);
+      if (ni + kWAhead < C::kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * C::kWaveN + (ni + kWAhead) * 16, lane);
       if constexpr (V::kBRow)
         sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
       if (ni == kDmaStep && dma.on && dma.wave >= C::kFirstLoader)
@@ -594,7 +607,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       }
     }
   }
-  if constexpr (V::kBRow && !kPow2 && kJEnd < kMfmaPerBlock) {
+  if constexpr (V::kBRow && !kPow2 && kJEnd < C::kMfma) {
     // the row scales of the deferred last row (its slot's previous row has
     // had all its folds by now)
     constexpr int ni = kJEnd / kSubM;
@@ -602,12 +615,12 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int ni = 0; ni < kSubN; ++ni)
+  for (int ni = 0; ni < C::kSubN; ++ni)
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) pin(acc[ni][mi]);
 #pragma unroll
   for (int r = 0; r < kRing; ++r) pin(p[r]);
-  wlast = wf[(kSubN - 1) % R];
+  wlast = wf[(C::kSubN - 1) % R];
 }
 
 // The MFMA of sub-tile (ni, mi) = j with the block's scales: straight into
@@ -709,7 +722,7 @@ __device__ __forceinline__ void block_boundary(const uint8_t *nbuf, int knext, i
                                                int lane, BlockFrags &f, const v8i &wlast,
                                                v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const float4 (&sbq)[2]) {
   constexpr bool kPow2 = V::kPow2;
-  constexpr int ni = kSubN - 1;
+  constexpr int ni = C::kSubN - 1;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   wait_block<C, V>(knext, KB, wave);
   __builtin_amdgcn_sched_barrier(0);
@@ -720,7 +733,7 @@ __device__ __forceinline__ void block_boundary(const uint8_t *nbuf, int knext, i
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) {
-    const int j = kMfmaPerBlock - kSubM + mi;
+    const int j = C::kMfma - kSubM + mi;
     mma_one<V>(ni, mi, j, wlast, f, acc, p);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (!kPow2) {
@@ -731,8 +744,8 @@ __device__ __forceinline__ void block_boundary(const uint8_t *nbuf, int knext, i
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
   }
   if constexpr (!kPow2) {
-    fold_one<V>(kMfmaPerBlock - 2, f.scl, acc, p, sbq);
-    fold_one<V>(kMfmaPerBlock - 1, f.scl, acc, p, sbq);
+    fold_one<V>(C::kMfma - 2, f.scl, acc, p, sbq);
+    fold_one<V>(C::kMfma - 1, f.scl, acc, p, sbq);
   }
   finish_head<V>(h, g);
   __builtin_amdgcn_sched_barrier(0);
@@ -754,12 +767,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
   constexpr bool kGather = V::kGather;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & (C::kWavesN - 1), wm = wave / C::kWavesN;
   const int KB = t.KB;
 
-  v4f acc[kSubN][kSubM];
+  v4f acc[kSubN][kSubM];  // rows ni >= C::kSubN unused
 #pragma unroll
-  for (int ni = 0; ni < kSubN; ++ni)
+  for (int ni = 0; ni < C::kSubN; ++ni)
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -784,7 +797,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
                C::kStages - 1 < KB};
   v8i wlast;
   for (int k = 0; k + 1 < KB; ++k) {
-    mma_steps<C, V, kMfmaPerBlock - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+    mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
     // Block k's buffer is free once every wave is past the barrier in
     // block_boundary; block k + kStages goes into it during the next block.
     dma.k = k + C::kStages;
@@ -794,16 +807,16 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
     block_boundary<C, V>(lds + cur * C::kStageBytes, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
   }
   // the last block: its last row's MFMAs and the trailing folds, no barrier
-  mma_steps<C, V, kMfmaPerBlock - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+  mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) {
-    const int j = kMfmaPerBlock - kSubM + mi;
-    mma_one<V>(kSubN - 1, mi, j, wlast, f, acc, p);
+    const int j = C::kMfma - kSubM + mi;
+    mma_one<V>(C::kSubN - 1, mi, j, wlast, f, acc, p);
     if constexpr (!kPow2) fold_one<V>(j - 2, f.scl, acc, p, sbq);
   }
   if constexpr (!kPow2) {
-    fold_one<V>(kMfmaPerBlock - 2, f.scl, acc, p, sbq);
-    fold_one<V>(kMfmaPerBlock - 1, f.scl, acc, p, sbq);
+    fold_one<V>(C::kMfma - 2, f.scl, acc, p, sbq);
+    fold_one<V>(C::kMfma - 1, f.scl, acc, p, sbq);
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   // A scale outside the power-of-two contract turns the outputs that depend
@@ -828,14 +841,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
     for (int mi = 0; mi < kSubM; ++mi)
       if (f.bad & (1u << mi))
 #pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
+        for (int ni = 0; ni < C::kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
   } else if (kPow2 && f.bad) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi)
       if (f.bad & ((1u << mi) | 16u))
 #pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
+        for (int ni = 0; ni < C::kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
   }
   if constexpr (kGather) {
     // A routed row whose token index is outside [0, T) read zeros; its output
@@ -847,7 +860,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
       const int64_t s = r < t.m_valid ? (int64_t)t.gidx[r] : 0;
       if (!(s >= 0 && s < t.T))
 #pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ni = 0; ni < C::kSubN; ++ni) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
 
@@ -860,8 +873,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
       if (r < t.m_valid) {
         uint16_t *yrow = y + (int64_t)r * N;
 #pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) {
-          const int nn = wn * 128 + ni * 16 + 4 * (lane >> 4);
+        for (int ni = 0; ni < C::kSubN; ++ni) {
+          const int nn = wn * C::kWaveN + ni * 16 + 4 * (lane >> 4);
           if (nn < t.n_valid) {
             uint2 w;
             w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
@@ -872,6 +885,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
       }
     }
   } else if constexpr (V::kSwiGLU) {
+    static_assert(C::kWaveN == 128, "SwiGLU epilogue: a wave holds 128 gate or up rows");
     // SwiGLU epilogue of a fused gate+up projection: the tile's weight rows
     // are 128 gate rows (waves wn = 0) and the 128 up rows of the same output
     // columns (waves wn = 1).  gate and up are rounded to bf16 as the bf16
@@ -949,6 +963,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
     // one 1x128 block of each of its rows, held by the lanes l, l^16, l^32,
     // l^48.  Block |max|, scale and element rule are those of the activation
     // quantizer, so the result equals quantizing the bf16 output bit for bit.
+    static_assert(C::kWaveN == 128, "quantized epilogue: a wave's 128 columns are one 1x128 block");
     if (wn * 128 < t.n_valid) {
       const int64_t nbo = N >> 7;  // scale blocks per output row
 #pragma unroll
@@ -1187,7 +1202,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
     p.tiles_n = (int32_t)(tiles_n - n1);
   }
   p.slots_m = mt_small;
-  return launch<CfgSmall, V>(p, stream);
+  return launch<SmallCfg<V>, V>(p, stream);
 }
 
 template <bool kPow2, bool kGather = false>
@@ -1205,7 +1220,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
     return launch<CfgLarge, V>(p, stream);
   }
   p.slots_m = M_total / CfgSmall::kBM + G;
-  return launch<CfgSmall, V>(p, stream);
+  return launch<SmallCfg<V>, V>(p, stream);
 }
 
 hipError_t launch_blockscaled_gemm(const uint8_t *a_q, const float *a_s,
