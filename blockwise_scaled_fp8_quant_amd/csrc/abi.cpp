@@ -121,6 +121,14 @@ fp8q_status fp8_quant_weight_128x128_batched(const fp8q_weight_job *jobs, int32_
   FP8Q_REQUIRE((reinterpret_cast<uintptr_t>(jobs) & 7u) == 0, FP8Q_EALIGN, "job table must be 8-byte aligned");
   fp8q_status st = check_device(__func__);
   if (st != FP8Q_OK) return st;
+  {
+    // the kernel reads the table: it must be memory the device can read
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, jobs);
+    (void)hipGetLastError();  // an unknown pointer leaves an error that would surface at the launch
+    FP8Q_REQUIRE(e == hipSuccess && (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged),
+                 FP8Q_EINVAL, "job table must be in device memory");
+  }
   return launched(fp8q::launch_quant_weight_batched(jobs, count, total_tiles, mode, (hipStream_t)stream),
                   __func__);
 }

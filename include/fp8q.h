@@ -152,8 +152,9 @@ typedef struct fp8q_weight_job {
  *   count        number of jobs, >= 0
  *   total_tiles  sum of (N/128)*(K/128) over the jobs, < 2^31
  *   mode         fp8q_scale_mode, for every job
- * The table is in device memory, so the host checks only count, total_tiles,
- * mode and the table's alignment (8 bytes).  On the device a tile whose job
+ * The host checks count, total_tiles, mode, the table's alignment (8 bytes)
+ * and that the table is device (or managed) memory (else FP8Q_EINVAL); it
+ * cannot read the table's contents.  On the device a tile whose job
  * has a shape that is not a positive multiple of 128, or which falls outside
  * its job's range of tiles (tile_begin not the running sum), is skipped: its
  * outputs are left as they were, and no access leaves a job's tensors.  Jobs

@@ -157,3 +157,22 @@ def test_inconsistent_jobs_are_skipped():
     _exact(mats[0], outs[0], "bad shape: job 0")
     assert _untouched(outs[1])
     _exact(mats[2], outs[2], "bad shape: job 2")
+
+
+def test_host_job_table_is_rejected():
+    """A job table in host memory is refused on the host (FP8Q_EINVAL), before
+    any launch: the kernel would have to read it from the device."""
+    require_gpu()
+    fp8q = lib()
+    from blockwise_scaled_fp8_quant_amd import _lib
+    import ctypes
+    w = dev_bf16(synth.bf16_bits(synth.normal_bf16((128, 128), 0.02, synth.seed_of(21, 4, 0))))
+    batch = fp8q.WeightBatch([w])
+    host_table = batch.jobs.cpu()
+    st = _lib.load().fp8_quant_weight_128x128_batched(ctypes.c_void_p(int(host_table.data_ptr())), 1, 1, 0, None)
+    assert st == 1 and "device memory" in _lib.load().fp8q_last_error().decode()
+    # the library still works afterwards (no error left behind)
+    outs = fp8q.fp8_quant_weight_128x128_batched(batch, 0)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_weight_128x128(synth.bf16_bits(w.cpu()), 0)
+    assert_bytes_equal(host_u8(outs[0][0]), oq, "after a rejected call")
