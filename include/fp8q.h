@@ -147,8 +147,9 @@ typedef struct fp8q_weight_job {
  * launch for all of them pays a launch's start-up and drain once instead of
  * once per matrix.
  *   jobs         [count] fp8q_weight_job in DEVICE memory, read by the kernel
- *                (build it once per set of weights and keep it; the library
- *                holds no pointer to it after the call is enqueued)
+ *                when it runs: it must stay valid and unchanged until the
+ *                call's work on the stream has completed (build it once per
+ *                set of weights and keep it)
  *   count        number of jobs, >= 0
  *   total_tiles  sum of (N/128)*(K/128) over the jobs, < 2^31
  *   mode         fp8q_scale_mode, for every job
