@@ -159,7 +159,10 @@ typedef struct fp8q_weight_job {
  * has a shape that is not a positive multiple of 128, or which falls outside
  * its job's range of tiles (tile_begin not the running sum), is skipped: its
  * outputs are left as they were, and no access leaves a job's tensors.  Jobs
- * must not write to one another's inputs.
+ * must not write to one another's inputs.  Every workgroup finds its job by
+ * reading the table's tile_begin fields in rounds of 64 jobs, so the lookup
+ * cost grows with count: meant for weight sets of up to a few thousand
+ * matrices (a whole model's linear layers is a few hundred).
  */
 fp8q_status fp8_quant_weight_128x128_batched(const fp8q_weight_job *jobs, int32_t count,
                                              int64_t total_tiles, int mode, void *stream);
