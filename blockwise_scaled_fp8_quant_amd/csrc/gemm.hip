@@ -865,24 +865,40 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
   }
 
   if constexpr (kOut == kOutBf16) {
-    // Epilogue: bf16 (RNE) quads, 8 bytes per lane per sub-tile.
-    uint16_t *__restrict__ y = o.y;
+    // Epilogue through LDS: each wave writes its [64 m][kWaveN n] bf16 (RNE)
+    // block into its own region of the stage buffers (free once every wave is
+    // past the barrier; 16-byte chunks XOR-swizzled by row, so the 16 rows a
+    // write instruction touches fall in distinct banks), then stores whole
+    // rows with 16-byte stores: half the store instructions of 8-byte quads,
+    // and each group of 8 lanes writes one full 128-byte line.  Measured
+    // against the quads: dense Llama shapes +2-4%, MoE grouped GEMMs 6-17%
+    // less time.
+    constexpr int kRowB = C::kWaveN * 2;
+    constexpr int kChunks = kRowB / 16;
+    __syncthreads();
+    uint8_t *wl = lds + wave * (64 * kRowB);
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi) {
-      const int r = wm * 64 + mi * 16 + (lane & 15);
-      if (r < t.m_valid) {
-        uint16_t *yrow = y + (int64_t)r * N;
+      const int r = mi * 16 + (lane & 15);
 #pragma unroll
-        for (int ni = 0; ni < C::kSubN; ++ni) {
-          const int nn = wn * C::kWaveN + ni * 16 + 4 * (lane >> 4);
-          if (nn < t.n_valid) {
-            uint2 w;
-            w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
-            w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
-            *reinterpret_cast<uint2 *>(yrow + nn) = w;
-          }
-        }
+      for (int ni = 0; ni < C::kSubN; ++ni) {
+        const int c = ni * 2 + ((lane >> 4) >> 1);
+        const int pc = c ^ (r & (kChunks - 1));
+        uint2 w;
+        w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+        w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+        *reinterpret_cast<uint2 *>(wl + r * kRowB + pc * 16 + ((lane >> 4) & 1) * 8) = w;
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint16_t *__restrict__ y = o.y;
+#pragma unroll
+    for (int it = 0; it < kChunks; ++it) {
+      const int flat = it * 64 + lane;
+      const int r = flat / kChunks, c = flat % kChunks;
+      const uint4 v = *reinterpret_cast<const uint4 *>(wl + r * kRowB + (c ^ (r & (kChunks - 1))) * 16);
+      const int rr = wm * 64 + r, nn = wn * C::kWaveN + c * 8;
+      if (rr < t.m_valid && nn < t.n_valid) *reinterpret_cast<uint4 *>(y + (int64_t)rr * N + nn) = v;
     }
   } else if constexpr (V::kSwiGLU) {
     static_assert(C::kWaveN == 128, "SwiGLU epilogue: a wave holds 128 gate or up rows");
