@@ -28,7 +28,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 
 // Per-device check that the current device is a gfx950 (cached).
-constexpr int kMaxDevices = 64;
+using fp8q::kMaxDevices;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_ok[kMaxDevices];
 
@@ -66,6 +66,8 @@ fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t
   FP8Q_REQUIRE(M >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
   FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
   FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
+  // four lanes per block: M*K/128 blocks give 4*M*K/128 work-items, below 2^32
+  FP8Q_REQUIRE(M <= (((int64_t)1 << 30) - 1) / (K / 128), FP8Q_ESHAPE, "M*K/128 must be below 2^30");
   if (M == 0) return FP8Q_OK;
   FP8Q_REQUIRE(x && q && scales, FP8Q_EINVAL, "null pointer");
   FP8Q_REQUIRE(aligned16(x) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,
@@ -82,7 +84,9 @@ fp8q_status fp8_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma, in
   FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
   FP8Q_REQUIRE(std::isfinite(eps) && eps >= 0.0f, FP8Q_EINVAL, "eps must be finite and >= 0");
   FP8Q_REQUIRE(K > 0 && K % 128 == 0 && K <= 8192, FP8Q_ESHAPE, "K must be a multiple of 128 in [128, 8192]");
-  FP8Q_REQUIRE(M <= ((int64_t)1 << 31), FP8Q_EINVAL, "M too large");  // one wave per row: grid < 2^31
+  // one wave of 64 lanes per row: the launch's 64*M work-items must stay
+  // below 2^32, the limit of a dispatch's grid size
+  FP8Q_REQUIRE(M < ((int64_t)1 << 26), FP8Q_ESHAPE, "M must be below 2^26");
   if (M == 0) return FP8Q_OK;
   FP8Q_REQUIRE(x && gamma && q && scales, FP8Q_EINVAL, "null pointer");
   FP8Q_REQUIRE(aligned16(x) && aligned16(gamma) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,
@@ -396,6 +400,8 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uin
   FP8Q_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, FP8Q_ESHAPE, "Hq must be a positive multiple of Hkv");
   const int32_t grp = Hq / Hkv;
   FP8Q_REQUIRE(grp == 1 || grp == 2 || grp == 4 || grp == 8, FP8Q_ESHAPE, "Hq / Hkv must be 1, 2, 4 or 8");
+  // 256 lanes per (sequence, key/value head) workgroup: below 2^32 work-items
+  FP8Q_REQUIRE((int64_t)B * Hkv < ((int64_t)1 << 24), FP8Q_ESHAPE, "B * Hkv must be below 2^24");
   if (B == 0) return FP8Q_OK;
   FP8Q_REQUIRE(q_q && q_s && k_cache && k_scale && v_cache && v_scale && seq_len && out, FP8Q_EINVAL,
                "null pointer");

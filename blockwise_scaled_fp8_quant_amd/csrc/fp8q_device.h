@@ -108,7 +108,9 @@ struct BlockQ {
 
 __device__ __forceinline__ int pow2_exponent(float amax) {
   // amax > 0, finite.  amax = m * 2^E with m in [1,2); 448 = 1.75 * 2^8, so the
-  // smallest e with 448 * 2^e >= amax is E-8 when m <= 1.75, else E-7.
+  // smallest e with 448 * 2^e >= amax is E-8 when m <= 1.75, else E-7.  It is
+  // kept at -127 or above, the E8M0 range of a power-of-two scale (448 * 2^-127
+  // still covers any smaller amax).
   float a = amax;
   int adj = 0;
   if (a < 0x1p-126f) {  // subnormal: scale up exactly first
@@ -117,7 +119,8 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
   }
   uint32_t b = __float_as_uint(a);
   int E = (int)(b >> 23) - 127 - adj;
-  return ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;
+  const int e = ((b & 0x7FFFFFu) <= 0x600000u) ? E - 8 : E - 7;
+  return e < -127 ? -127 : e;
 }
 
 template <int kMode>
@@ -130,7 +133,7 @@ __device__ __forceinline__ BlockQ block_params(float amax) {
     p.slow = amax < 0x1p-100f;
   } else {
     p.e = (amax == 0.0f) ? 0 : pow2_exponent(amax);
-    p.s = __builtin_ldexpf(1.0f, p.e);  // exact: e in [-141, 120]
+    p.s = __builtin_ldexpf(1.0f, p.e);  // exact: e in [-127, 120]
     p.y = 0.0f;
     p.slow = false;
   }

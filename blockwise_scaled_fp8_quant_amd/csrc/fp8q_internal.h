@@ -9,6 +9,9 @@ struct fp8q_weight_job;  // include/fp8q.h
 
 namespace fp8q {
 
+// Devices the library keeps per-device set-up for (ids 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
 hipError_t launch_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
                                   uint8_t *q, float *s, int mode,
                                   hipStream_t stream);

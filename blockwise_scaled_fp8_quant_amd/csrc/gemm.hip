@@ -31,6 +31,8 @@
 //  - Workgroup ids are remapped so that each XCD (own L2) gets a contiguous
 //    range of tiles, enumerated in groups of 8 weight panels so that the tiles
 //    running at the same time share operand panels.
+#include <mutex>
+
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 
@@ -386,7 +388,7 @@ struct BlockFrags {
   float scl[kSubM];
   // power-of-two scales: E8M0 exponent bytes (token rows mi = 0..3 in byte mi;
   // the weight block's), and which of them (bit mi; bit 4: the weight
-  // block's) was, in some K block so far, not a power of two in [2^-126, 2^127]
+  // block's) was, in some K block so far, not a power of two in [2^-127, 2^127]
   uint32_t ea, eb;
   // per-row power-of-two weight-side scales: this lane's row of sub-tile ni
   // in byte ni%4 of ebr[ni/4]; a bad one sets bit 16+ni of bad
@@ -394,12 +396,14 @@ struct BlockFrags {
   uint32_t bad;
 };
 
-// E8M0 byte of a power-of-two fp32 scale 2^(e-127), 1 <= e <= 254: its
-// exponent field.  Sets `bit` in bad for anything else (a mantissa, a sign,
-// zero, subnormal, infinity or NaN).
+// E8M0 byte of a power-of-two fp32 scale 2^(e-127), 0 <= e <= 254: the
+// exponent field for 2^-126 .. 2^127, and 0 for 2^-127 (the fp32 subnormal
+// 0x00400000).  Sets `bit` in bad for anything else (a mantissa, a sign, zero,
+// a smaller subnormal, infinity or NaN).
 __device__ __forceinline__ uint32_t e8m0_of(float s, uint32_t &bad, uint32_t bit) {
   const uint32_t u = __float_as_uint(s);
   const uint32_t e = u >> 23;  // sign bit included: must be 0
+  if (u == 0x00400000u) return 0u;
   if ((u & 0x7FFFFFu) != 0u || e == 0u || e >= 255u) bad |= bit;
   return e & 0xFFu;
 }
@@ -1157,13 +1161,20 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 
 template <class C, class V>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
-  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<C, V>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // The LDS size above the default limit is an attribute of the kernel on the
+  // current device: set once per device (std::call_once, so concurrent first
+  // calls from several host threads are safe), and the outcome kept.
+  static std::once_flag once[kMaxDevices];
+  static hipError_t attr_err[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev]() {
+    attr_err[dev] = hipFuncSetAttribute((const void *)gemm_kernel<C, V>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  });
+  if (attr_err[dev] != hipSuccess) return attr_err[dev];
   const int64_t grid = p.slots_m * p.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<C, V>), dim3((unsigned)grid), dim3(C::kThreads),
                      C::kLdsBytes, stream, p);

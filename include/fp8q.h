@@ -64,7 +64,7 @@ typedef enum fp8q_status {
  * (amax == 0) always gets s = 1. */
 typedef enum fp8q_scale_mode {
     FP8Q_SCALE_AMAX = 0, /* s = amax / 448, rounded to the nearest fp32 */
-    FP8Q_SCALE_POW2 = 1  /* s = 2^e, e the smallest integer with 448 * 2^e >= amax */
+    FP8Q_SCALE_POW2 = 1  /* s = 2^e, e the smallest integer >= -127 with 448 * 2^e >= amax */
 } fp8q_scale_mode;
 
 /*
@@ -77,6 +77,8 @@ typedef enum fp8q_scale_mode {
  * Every element: q = E4M3(RN_fp32(x / s)), rounded to nearest with ties to an
  * even mantissa and saturated to +-448; a zero keeps its sign.
  * The result is bit-identical to that rule for every finite input.
+ * Sizes: M*K/128 < 2^30 (FP8Q_ESHAPE otherwise; the launch's work-items stay
+ * below 2^32).
  */
 fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
                                 uint8_t *q, float *scales, int mode,
@@ -102,6 +104,7 @@ fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,
  * eps = 0 also no row whose mean square is 0 in fp32 (an all-zero row, or
  * values below about 1e-19, whose squares underflow); the outputs of such a
  * row are unspecified.
+ * Sizes: M < 2^26 (one 64-lane wave per row; FP8Q_ESHAPE otherwise).
  */
 fp8q_status fp8_rmsnorm_quant_1x128(const uint16_t *x, const uint16_t *gamma,
                                     int64_t M, int64_t K, float eps,
@@ -307,7 +310,7 @@ fp8q_status fp8_blockscaled_gemm_wgrad(const uint8_t *a_q, const float *a_s,
  * matrix cores apply both operands' per-row scales themselves (E8M0), so no
  * per-block rescaling runs on the vector ALUs.  Same precondition and NaN rule
  * as fp8_blockscaled_gemm_pow2: an output that depends on a scale other than
- * 2^e, -126 <= e <= 127, is NaN.
+ * 2^e, -127 <= e <= 127, is NaN.
  */
 fp8q_status fp8_blockscaled_gemm_wgrad_pow2(const uint8_t *a_q, const float *a_s,
                                             const uint8_t *b_q, const float *b_s,
@@ -346,10 +349,10 @@ fp8q_status fp8_grouped_gemm(const uint8_t *a_q, const float *a_s,
  * themselves (E8M0 block-scale operands), so no per-block rescaling runs on
  * the vector ALUs.  Arguments, layouts, errors and the result (up to the fp32
  * summation order) are those of fp8_blockscaled_gemm / fp8_grouped_gemm.
- * Precondition: every scale an output depends on is 2^e with -126 <= e <= 127;
- * an output that depends on any other scale value is written as NaN instead
- * of a silently different product.  (POW2-mode quantization gives e < -126
- * only for blocks whose largest magnitude is below 448 * 2^-127.)
+ * Precondition: every scale an output depends on is 2^e with -127 <= e <= 127
+ * (an E8M0 value); an output that depends on any other scale value is written
+ * as NaN instead of a silently different product.  POW2-mode quantization
+ * always gives such scales: its exponent is at least -127.
  */
 fp8q_status fp8_blockscaled_gemm_pow2(const uint8_t *a_q, const float *a_s,
                                       const uint8_t *b_q, const float *b_s,
@@ -429,6 +432,7 @@ fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new,
  * softmax and the weighted sum of values run in fp32 on exactly decoded
  * values; out is rounded once to bf16.  Results agree with the exact value
  * to within fp32 arithmetic and that rounding.
+ * Sizes: B * Hkv < 2^24 (FP8Q_ESHAPE otherwise).
  */
 fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s,
                                  const uint8_t *k_cache, const float *k_scale,

@@ -139,7 +139,10 @@ void oracle_e4m3_encode_array(const float *r, int64_t n, uint8_t *q)
 /* Scale of a block with largest magnitude amax (>= 0, finite).
  *  amax mode: s = amax / 448 in fp32, correctly rounded (IEEE division).
  *  pow2 mode [P1-O]: s = 2^e with e the smallest integer such that
- *             448 * 2^e >= amax, decided by exact comparison.
+ *             448 * 2^e >= amax, decided by exact comparison, but not below
+ *             -127: a power-of-two scale is an E8M0 value (2^-127 .. 2^127).
+ *             For amax <= 448 * 2^-127 the scale is 2^-127, which still
+ *             satisfies 448 * s >= amax, so nothing saturates.
  *  amax == 0: s = 1. */
 float oracle_block_scale(float amax, int mode)
 {
@@ -154,6 +157,8 @@ float oracle_block_scale(float amax, int mode)
         e++;
     while (ldexp(448.0, e - 1) >= (double)amax)
         e--;
+    if (e < -127)
+        e = -127;
     return (float)ldexp(1.0, e);
 }
 

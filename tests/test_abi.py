@@ -129,6 +129,19 @@ def test_rmsnorm_quant_argument_errors(lib):
     assert f(GOOD, ODD, 4, 256, e, GOOD, GOOD, 0, None) == 3                      # misaligned gamma
     assert f(GOOD, GOOD, -1, 256, e, GOOD, GOOD, 0, None) == 1
     assert f(None, None, 0, 256, e, None, None, 0, None) == 0                     # empty call
+    assert f(GOOD, GOOD, 1 << 26, 256, e, GOOD, GOOD, 0, None) == 2               # 64*M work-items >= 2^32
+    assert "2^26" in _err(lib)
+
+
+def test_launch_size_bounds(lib):
+    """Sizes whose launch would exceed a dispatch's 2^32 work-items are refused
+    on the host with FP8Q_ESHAPE (checked before any pointer or device)."""
+    f = lib.fp8_quant_act_1x128
+    assert f(GOOD, 1 << 23, 1 << 14, GOOD, GOOD, 0, None) == 2                     # M*K/128 = 2^30
+    assert "2^30" in _err(lib)
+    a = lib.fp8_attention_decode
+    assert a(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 21, 64, 8, 1, None, 0, None) == 2   # B*Hkv = 2^24
+    assert "2^24" in _err(lib)
 
 
 def test_gemm_swiglu_quant_argument_errors(lib):

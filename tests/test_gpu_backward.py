@@ -297,3 +297,36 @@ def test_wgrad_pow2_nan_rule():
     assert not np.isnan(y[~bad]).any()
     ref = oracle.gemm_wgrad_f64(gtq, gts, xtq, xts)
     gemm_tolerance_check(np.where(bad, 0.0, y), np.where(bad, 0.0, ref), "wgrad pow2 other outputs")
+
+
+def test_tiny_gradient_blocks_pow2():
+    """Gradient blocks far below 448 * 2^-127 (down to bf16 subnormals) get the
+    E8M0 floor 2^-127 as their power-of-two scale; the two-layout quantizer
+    matches the oracle and the weight gradient on the matrix cores stays
+    finite and within tolerance (a scale of 2^-127 is E8M0 byte 0x00)."""
+    require_gpu()
+    fp8q = lib()
+    M, N, K = 256, 256, 384
+    g = synth.normal_bf16((M, N), 1e-3, synth.seed_of(15, 901, 2))
+    gb = synth.bf16_bits(g).copy()
+    tiny = synth.bf16_bits(synth.normal_bf16((M, N), 2.0 ** -128, synth.seed_of(15, 901, 3)))
+    gb[:128, :128] = tiny[:128, :128]          # one column block and rows 0..127's first row block
+    gb[200, :] = 0x0001                        # a row of the smallest bf16 subnormal
+    x = synth.normal_bf16((M, K), 1.0, synth.seed_of(15, 901, 0))
+    xb = synth.bf16_bits(x)
+    say("tiny gradient pow2 dual + wgrad_pow2")
+    gq, gs, gtq, gts = fp8q.fp8_quant_act_dual(dev_bf16(gb), 1)
+    _, _, xtq, xts = fp8q.fp8_quant_act_dual(dev_bf16(xb), 1, rowwise=False)
+    y = fp8q.fp8_blockscaled_gemm_wgrad_pow2(gtq, gts, xtq, xts)
+    torch.cuda.synchronize()
+    ogq, ogs = oracle.quant_act_1x128(gb, 1)
+    ogtq, ogts = oracle.quant_act_colwise_t(gb, 1)
+    oxtq, oxts = oracle.quant_act_colwise_t(xb, 1)
+    assert float(ogts.min()) == 2.0 ** -127 and float(ogs.min()) == 2.0 ** -127
+    assert_bytes_equal(host_u8(gq), ogq, "tiny dY row codes")
+    assert_scales_equal(host_f32(gs), ogs, "tiny dY row scales")
+    assert_bytes_equal(host_u8(gtq), ogtq, "tiny dY column codes")
+    assert_scales_equal(host_f32(gts), ogts, "tiny dY column scales")
+    yh = host_bf16_as_f64(y)
+    assert np.isfinite(yh).all()
+    gemm_tolerance_check(yh, oracle.gemm_wgrad_f64(ogtq, ogts, oxtq, oxts), "wgrad pow2 with 2^-127 scales")

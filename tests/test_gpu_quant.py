@@ -70,13 +70,45 @@ def exhaustive_input():
     return _exhaustive_blocks()
 
 
+_EXHAUSTIVE_ORACLE = {}
+
+
+def _exhaustive_oracle(x_bits, mode):
+    """The oracle's codes and scales of the exhaustive input (computed once
+    per mode and shared by the tests below)."""
+    if mode not in _EXHAUSTIVE_ORACLE:
+        _EXHAUSTIVE_ORACLE[mode] = oracle.quant_act_1x128(x_bits, mode)
+    return _EXHAUSTIVE_ORACLE[mode]
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_exhaustive_element_rule(exhaustive_input, mode):
     """The byte of an element depends only on (x, amax of its block); this
     covers every such pair of bf16 values, i.e. the whole element rule,
     including the blocks that take the exact-division path."""
     require_gpu()
-    _act_parity(exhaustive_input, mode, "exhaustive (x, amax)")
+    fp8q = lib()
+    say("quant_act exhaustive (x, amax)", exhaustive_input.shape, "mode", mode)
+    q, s = fp8q.fp8_quant_act_1x128(dev_bf16(exhaustive_input), mode)
+    torch.cuda.synchronize()
+    oq, os_ = _exhaustive_oracle(exhaustive_input, mode)
+    assert_scales_equal(host_f32(s), os_, "exhaustive scales")
+    assert_bytes_equal(host_u8(q), oq, "exhaustive bytes")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_exhaustive_element_rule_dual(exhaustive_input, mode):
+    """The same sweep through the two-layout quantizer's row blocks, whose
+    blocks with a normal scale convert without the explicit +-448 clamp: every
+    (x, amax) pair gives the 1x128 quantizer's byte and scale."""
+    require_gpu()
+    fp8q = lib()
+    say("quant_act_dual exhaustive (x, amax)", exhaustive_input.shape, "mode", mode)
+    q, s, _, _ = fp8q.fp8_quant_act_dual(dev_bf16(exhaustive_input), mode, rowwise=True)
+    torch.cuda.synchronize()
+    oq, os_ = _exhaustive_oracle(exhaustive_input, mode)
+    assert_scales_equal(host_f32(s), os_, "exhaustive dual scales")
+    assert_bytes_equal(host_u8(q), oq, "exhaustive dual bytes")
 
 
 @pytest.mark.parametrize("mode", MODES)

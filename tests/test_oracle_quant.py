@@ -42,6 +42,7 @@ def _exact_block(vals, mode):
             e += 1
         while Fraction(448) * Fraction(2) ** (e - 1) >= amax:
             e -= 1
+        e = max(e, -127)  # a power-of-two scale is an E8M0 value: 2^-127 at least
         s = float(Fraction(2) ** e)
     codes = []
     for v in vals:

@@ -2,7 +2,8 @@
 
 amax mode is pinned to exact rational rounding; pow2 mode to its closed form
 (448 = 1.75 * 2^8, so with amax = m * 2^E, m in [1,2): e = E-8 if m <= 1.75
-else E-7) and to its defining inequality.  Power-of-two scales: page "NVIDIA
+else E-7, kept at -127 or above, the range of an E8M0 scale) and to its
+defining inequality.  Power-of-two scales: page "NVIDIA
 NeMo RL erreicht 48% Geschwindigkeitssteigerung ...", section "Warum dies fuer
 die KI-Oekonomie wichtig ist"; 448: page "FP8 Trainingsinfrastructuur",
 section "Het landschap van numerieke precisie".
@@ -68,10 +69,21 @@ def test_pow2_mode_closed_form(oracle_lib):
         m, E = math.frexp(a)       # a = m * 2^E, m in [0.5,1)
         m, E = 2 * m, E - 1         # m in [1,2)
         e = E - 8 if m <= 1.75 else E - 7
+        e = max(e, -127)
         assert s == math.ldexp(1.0, e), (a, s, e)
-        # defining property: smallest power of two with 448*s >= amax
+        # defining property: smallest power of two, not below 2^-127, with
+        # 448*s >= amax
         assert Fraction(448) * Fraction(s) >= Fraction(a)
-        assert Fraction(448) * Fraction(s) / 2 < Fraction(a)
+        assert s == 2.0 ** -127 or Fraction(448) * Fraction(s) / 2 < Fraction(a)
+
+
+def test_pow2_mode_lower_bound(oracle_lib):
+    """Blocks with amax <= 448 * 2^-127 all get the E8M0 floor 2^-127; the next
+    power of two up is the first above it."""
+    a = np.array([2.0 ** -149, 2.0 ** -140, 448 * 2.0 ** -127, 448 * 2.0 ** -127 * (1 + 2.0 ** -23),
+                  1.75 * 2.0 ** -119], dtype=np.float32)
+    got = oracle_lib.block_scale(a, oracle_lib.MODE_POW2).tolist()
+    assert got == [2.0 ** -127, 2.0 ** -127, 2.0 ** -127, 2.0 ** -126, 2.0 ** -127]
 
 
 def test_zero_block_scale_is_one(oracle_lib):
