@@ -488,3 +488,33 @@ def fp8_attention_decode(q_q, q_s, cache, seq_len, out=None, workspace="auto"):
                _lib.load().fp8_attention_decode(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S, pws, nws,
                                                 _stream(q_q)))
     return y
+
+
+def fp8_attention_decode_noalloc(q_q, q_s, cache, seq_len, out):
+    """fp8_attention_decode without a workspace, for callers that cannot
+    allocate: the library's static per-GPU scratch array takes the chunked
+    path's partial results.  `out` (bf16 [B, Hq, 128], device) is required, so
+    the call allocates nothing.  Calls that overlap on one GPU race."""
+    kq, ks, vq, vs = cache
+    q_q, pq = _as_bytes(q_q, "q_q", 3)
+    pqs = _dev(q_s, "q_s", torch.float32, 2)
+    kq, pkq = _as_bytes(kq, "k_cache", 4)
+    vq, pvq = _as_bytes(vq, "v_cache", 4)
+    pks = _dev(ks, "k_scale", torch.float32, 3)
+    pvs = _dev(vs, "v_scale", torch.float32, 3)
+    plen = _dev(seq_len, "seq_len", torch.int32, 1)
+    B, Hq, Dh = q_q.shape
+    Bk, Hkv, S, Dk = kq.shape
+    if Dh != 128 or Dk != 128 or Bk != B or tuple(q_s.shape) != (B, Hq):
+        raise ValueError("query and cache shapes do not match")
+    if tuple(vq.shape) != (B, Hkv, S, 128) or tuple(ks.shape) != (B, Hkv, S) or tuple(vs.shape) != (B, Hkv, S):
+        raise ValueError("cache shapes do not match")
+    if seq_len.numel() != B:
+        raise ValueError("seq_len must have B entries")
+    py = _dev(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (B, Hq, 128):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_attention_decode_noalloc",
+               _lib.load().fp8_attention_decode_noalloc(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S,
+                                                        _stream(q_q)))
+    return out

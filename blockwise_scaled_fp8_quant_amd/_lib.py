@@ -19,7 +19,7 @@ ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_wei
                 "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
                 "fp8_kv_cache_append",
-                "fp8_attention_decode", "fp8_attention_decode_workspace_size",
+                "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8_attention_decode_noalloc",
                 "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version")
 
 _lib = None
@@ -70,6 +70,8 @@ def load():
     lib.fp8_kv_cache_append.restype = ci
     lib.fp8_attention_decode.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p, i64, p]
     lib.fp8_attention_decode.restype = ci
+    lib.fp8_attention_decode_noalloc.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p]
+    lib.fp8_attention_decode_noalloc.restype = ci
     lib.fp8_attention_decode_workspace_size.argtypes = [i32, i32, i32, i64]
     lib.fp8_attention_decode_workspace_size.restype = i64
     lib.fp8q_status_string.argtypes = [ci]

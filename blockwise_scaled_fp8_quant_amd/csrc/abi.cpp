@@ -418,6 +418,32 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uin
                   __func__);
 }
 
+fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s, const uint8_t *k_cache,
+                                         const float *k_scale, const uint8_t *v_cache, const float *v_scale,
+                                         const int32_t *seq_len, uint16_t *out, int32_t B, int32_t Hq,
+                                         int32_t Hkv, int64_t S, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(B >= 0 && Hq >= 0 && Hkv >= 0 && S >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, FP8Q_ESHAPE, "Hq must be a positive multiple of Hkv");
+  const int32_t grp = Hq / Hkv;
+  FP8Q_REQUIRE(grp == 1 || grp == 2 || grp == 4 || grp == 8, FP8Q_ESHAPE, "Hq / Hkv must be 1, 2, 4 or 8");
+  FP8Q_REQUIRE((int64_t)B * Hkv < ((int64_t)1 << 24), FP8Q_ESHAPE, "B * Hkv must be below 2^24");
+  // the scratch array covers every call the split rule allows; checked anyway
+  FP8Q_REQUIRE(fp8_attention_decode_workspace_size(B, Hq, Hkv, S) <= fp8q::attention_noalloc_scratch_bytes(),
+               FP8Q_ESHAPE, "needs more scratch than FP8Q_NOALLOC_SCRATCH_BYTES");
+  if (B == 0) return FP8Q_OK;
+  FP8Q_REQUIRE(q_q && q_s && k_cache && k_scale && v_cache && v_scale && seq_len && out, FP8Q_EINVAL,
+               "null pointer");
+  FP8Q_REQUIRE(aligned16(q_q) && aligned16(q_s) && aligned16(k_cache) && aligned16(k_scale) &&
+                   aligned16(v_cache) && aligned16(v_scale) && aligned16(seq_len) && aligned16(out),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_attention_decode_noalloc(q_q, q_s, k_cache, k_scale, v_cache, v_scale, seq_len, out,
+                                                        B, Hq, Hkv, S, (hipStream_t)stream),
+                  __func__);
+}
+
 const char *fp8q_status_string(int status) {
   switch (status) {
     case FP8Q_OK: return "ok";

@@ -10,6 +10,9 @@
 // Cache layout: [B][Hkv][S][128] E4M3 bytes, scales [B][Hkv][S] -- the tokens
 // of one sequence and head are contiguous 128-byte rows, the unit every load
 // below reads whole.
+#include <mutex>
+
+#include "../../include/fp8q.h"
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 
@@ -435,6 +438,61 @@ hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uin
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)B * Hq)), dim3(kHeadDim), 0, stream, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention without a caller workspace, for callers that cannot
+// allocate: the chunked path's partial outputs and (max, sum) pairs live in
+// this file-scope device array instead.  Its size covers every valid call:
+// with fewer than kFillWgs (sequence, head) pairs, chunks per sequence <=
+// ceil(kFillWgs / pairs), so pairs * chunks <= kFillWgs + pairs - 1 <= 1022,
+// times at most 8 query heads per key/value head, each row 128 + 2 floats.
+// Each GPU the library runs on holds its own copy until the process ends;
+// calls on one GPU share it, so calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocRows = 8 * (2 * kFillWgs - 2);
+constexpr int64_t kNoAllocFloats = kNoAllocRows * (kHeadDim + 2);
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+static_assert(kNoAllocFloats * sizeof(float) == FP8Q_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+
+int64_t attention_noalloc_scratch_bytes() { return kNoAllocFloats * (int64_t)sizeof(float); }
+
+// The device address of `scratch` on the current device.  In host code the
+// array's name is only a host-side stand-in; the address comes from the
+// runtime, once per device (with that device current), and is kept.
+static hipError_t scratch_address(float **out) {
+  static std::once_flag once[kMaxDevices];
+  static float *addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev]() {
+    void *p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = static_cast<float *>(p);
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  if (addr[dev] == nullptr) return hipErrorInvalidSymbol;
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, const uint8_t *kc,
+                                           const float *ks, const uint8_t *vc, const float *vs,
+                                           const int32_t *len, uint16_t *out, int32_t B, int32_t Hq,
+                                           int32_t Hkv, int64_t S, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  int64_t nch, ct;
+  attention_decode_split((int64_t)B * Hkv, S, nch, ct);
+  float *ws = nullptr;
+  if (nch > 1) {
+    if ((int64_t)B * Hq * nch * (kHeadDim + 2) > kNoAllocFloats) return hipErrorInvalidValue;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_attention_decode(qq, qs, kc, ks, vc, vs, len, out, B, Hq, Hkv, S, ws, stream);
 }
 
 }  // namespace fp8q

@@ -97,4 +97,13 @@ hipError_t launch_attention_decode(const uint8_t *qq, const float *qs, const uin
                                    int32_t B, int32_t Hq, int32_t Hkv, int64_t S, float *workspace,
                                    hipStream_t stream);
 
+// The same attention with the chunked path's workspace in a static device
+// array of attention_noalloc_scratch_bytes() (no allocation, no workspace
+// argument); shared by every call on a device.
+int64_t attention_noalloc_scratch_bytes();
+hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, const uint8_t *kc,
+                                           const float *ks, const uint8_t *vc, const float *vs,
+                                           const int32_t *len, uint16_t *out, int32_t B, int32_t Hq,
+                                           int32_t Hkv, int64_t S, hipStream_t stream);
+
 }  // namespace fp8q

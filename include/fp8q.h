@@ -451,6 +451,28 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s,
  * initialisation; concurrent calls need their own. */
 int64_t fp8_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int64_t S);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fp8_attention_decode
+ * without the workspace argument.  Same arguments otherwise, same results bit
+ * for bit as fp8_attention_decode with a workspace of
+ * fp8_attention_decode_workspace_size() bytes.
+ *   The chunked path's workspace is a static device array of
+ *   FP8Q_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ *   process ends.  That size covers every (B, Hq, Hkv, S) the call accepts
+ *   (FP8Q_ESHAPE otherwise).  The call allocates nothing and calls no
+ *   allocating routine.  Every call on one GPU shares that GPU's array and
+ *   needs none of its contents: calls that overlap on one GPU (several
+ *   streams, or host threads, at once) race and must not be issued.
+ */
+#define FP8Q_NOALLOC_SCRATCH_BYTES 4251520
+fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s,
+                                         const uint8_t *k_cache, const float *k_scale,
+                                         const uint8_t *v_cache, const float *v_scale,
+                                         const int32_t *seq_len, uint16_t *out,
+                                         int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
+                                         void *stream);
+
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -231,6 +231,35 @@ def test_attention_decode_argument_errors(lib):
     assert f(None, None, None, None, None, None, None, None, 0, 32, 8, 64, None, 0, None) == 0    # empty call
 
 
+def test_attention_decode_noalloc_argument_errors(lib):
+    f = lib.fp8_attention_decode_noalloc
+    #        qq    qs    kc    ks    vc    vs    len   out   B  Hq  Hkv S
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 32, 6, 64, None) == 2      # Hq % Hkv
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 48, 3, 64, None) == 2      # 16 per group
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, -1, 32, 8, 64, None) == 1     # negative size
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 2, 32, 8, 64, None) == 1      # null seq_len
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 2, 32, 8, 64, None) == 3       # misaligned out
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 21, 64, 8, 1, None) == 2  # B*Hkv = 2^24
+    assert f(None, None, None, None, None, None, None, None, 0, 32, 8, 64, None) == 0      # empty call
+
+
+def test_noalloc_scratch_covers_every_split():
+    """The static scratch of fp8_attention_decode_noalloc (the header's
+    FP8Q_NOALLOC_SCRATCH_BYTES) is at least the workspace any accepted size
+    asks for: the worst case of the split rule is 511 pairs in two chunks
+    with 8 query heads per key/value head."""
+    from blockwise_scaled_fp8_quant_amd import _lib
+    lib = _lib.load()
+    text = open(HEADER).read()
+    cap = int(re.search(r"#define FP8Q_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    worst = 0
+    for B, Hkv in [(511, 1), (1, 511), (73, 7), (255, 2), (64, 8), (1, 1), (2, 8), (16, 8), (3, 4)]:
+        for grp in (1, 2, 4, 8):
+            for S in (1, 256, 257, 260, 4096, 65536, 1 << 20, (1 << 31) - 1):
+                worst = max(worst, lib.fp8_attention_decode_workspace_size(B, grp * Hkv, Hkv, S))
+    assert worst == cap == 8 * 1022 * 130 * 4
+
+
 def test_gather_argument_errors(lib):
     f = lib.fp8_grouped_gemm_gather
     #      a_q   a_s   T    b_q   b_s   off   idx   G  M   N    K    y     mode
