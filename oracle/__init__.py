@@ -33,5 +33,6 @@ from .oracle import (  # noqa: F401
     gemm_swiglu_quant,
     rmsnorm_f64,
     rmsnorm_quant_1x128,
+    moe_permute,
     num_threads,
 )

@@ -417,3 +417,50 @@ def rmsnorm_quant_1x128(x_bits, gamma_bits, eps, mode=MODE_AMAX):
     """(q uint8 [M, K], s f32 [M, K/128]): bf16(rmsnorm(x)) quantized in 1x128
     blocks, the input of the projection that follows the norm."""
     return quant_act_1x128(round_bf16(rmsnorm_f64(x_bits, gamma_bits, eps)), mode)
+
+
+# ---------------------------------------------------------------------------
+# MoE dispatch order (page "NVIDIA NeMo RL erreicht 48% Geschwindigkeits-
+# steigerung ...", section "Leistungsgewinne in der Praxis": the recipe trains
+# the Qwen3-30B mixture-of-experts model; section "Warum dies fuer die KI-
+# Oekonomie wichtig ist": Moonlight 16B).  The grouped GEMM wants the routed
+# rows grouped by expert.  The pages give no order inside a group; the reading
+# taken here is the plainest one: rows sorted by expert, and within an expert
+# in the order of the routing table read row by row (token t, slot j: entry
+# t*k + j).  Shared experts (every token goes to each of them) follow as
+# groups of all tokens in token order.  An expert id outside [0, E) places its
+# entry in no group; such entries leave rows at the end, after the last group,
+# with token -1.
+# ---------------------------------------------------------------------------
+
+def moe_permute(expert_ids, E, n_shared=0):
+    """expert_ids int [T, k] -> (offsets int32 [E+n_shared+1], row_index int32
+    [T*(k+n_shared)], entry_row int32 [T*k]).
+
+    offsets[g] is the first row of group g (experts 0..E-1, then the shared
+    groups); row_index[r] is the token of row r (-1 for the trailing rows of
+    invalid entries); entry_row[t*k + j] is the row of entry (t, j), -1 for an
+    invalid expert id.  The grouping is one stable sort of the entries by
+    expert (a library sort, stable by position)."""
+    ids = np.asarray(expert_ids).astype(np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    n = flat.size
+    valid = (flat >= 0) & (flat < E)
+    key = np.where(valid, flat, E)                   # invalid entries sort last
+    order = np.argsort(key, kind="stable")           # entries by expert, stable by position
+    counts = np.bincount(flat[valid], minlength=E)[:E]
+    nv = int(counts.sum())
+    G = E + n_shared
+    offsets = np.zeros(G + 1, dtype=np.int64)
+    offsets[1:E + 1] = np.cumsum(counts)
+    for s in range(n_shared):
+        offsets[E + 1 + s] = nv + (s + 1) * T
+    rows = T * (k + n_shared)
+    row_index = np.full(rows, -1, dtype=np.int64)
+    row_index[:nv] = order[:nv] // k                 # the token of each routed entry
+    for s in range(n_shared):
+        row_index[nv + s * T: nv + (s + 1) * T] = np.arange(T)
+    entry_row = np.full(n, -1, dtype=np.int64)
+    entry_row[order[:nv]] = np.arange(nv)
+    return offsets.astype(np.int32), row_index.astype(np.int32), entry_row.astype(np.int32)

@@ -17,7 +17,7 @@ __all__ = [
     "TINY", "LLAMA_TOKENS", "LLAMA_LAYERS", "LLAMA_NUM_LAYERS", "QWEN3", "MOONLIGHT",
     "MoEShape", "seed_of", "normal_bf16", "bf16_bits", "outlier_channels",
     "tiny_inputs", "llama_layer_inputs", "llama_weight", "moe_routing",
-    "moe_group_offsets", "moe_inputs", "moe_dispatch_inputs",
+    "moe_token_matrix", "moe_down_input", "moe_weights",
 ]
 
 # Tiny linear layer: X 256x512 ~ N(0,1), W 256x512 ~ N(0, 0.02).
@@ -101,10 +101,14 @@ def bf16_bits(t):
 
 
 def tiny_inputs(device="cpu"):
-    """(X bf16 [256,512] ~ N(0,1), W bf16 [256,512] ~ N(0,0.02)), seed 0."""
-    x = normal_bf16((TINY["M"], TINY["K"]), 1.0, seed_of(1, 0, 0), device)
-    w = normal_bf16((TINY["N"], TINY["K"]), 0.02, seed_of(1, 0, 1), device)
-    return x, w
+    """(X bf16 [256,512] ~ N(0,1), W bf16 [256,512] ~ N(0,0.02)): literally
+    seed 0 -- numpy's default_rng(0) draws X, then W, in fp32 on the host,
+    rounded to bf16 (RNE)."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((TINY["M"], TINY["K"]), dtype=np.float32)
+    w = rng.standard_normal((TINY["N"], TINY["K"]), dtype=np.float32) * np.float32(0.02)
+    return (torch.from_numpy(x).to(torch.bfloat16).to(device),
+            torch.from_numpy(w).to(torch.bfloat16).to(device))
 
 
 def llama_layer_inputs(layer_idx, device="cpu", tokens=LLAMA_TOKENS):
@@ -124,74 +128,54 @@ def llama_weight(layer, kind, device="cpu"):
 
 
 def moe_routing(shape: MoEShape, seed_parts=None):
-    """Expert choice per token: int64 [tokens, top_k], distinct experts per row.
+    """Expert choice per token: int32 [tokens, top_k], distinct experts per row.
 
-    Gumbel-top-k sampling without replacement from p(e) ~ rank(e)^-alpha,
-    with ranks a seeded permutation of the expert ids (alpha = 0: uniform).
+    Gumbel-top-k sampling without replacement.  Zipf load (alpha > 0): a
+    seeded permutation lists the experts in rank order (the expert it puts
+    first has rank 1) and p(e) ~ rank(e)^-alpha; the permutation is drawn
+    before the Gumbel noise.  Uniform load (alpha = 0): the Gumbel noise
+    alone, with no permutation drawn.  This is the recipe the survey of the
+    workloads states its expert-load figures for (Qwen3: max 7397 / median
+    196 / min 79 rows per expert; Moonlight: 1477..1662).
     """
     wid = 4 if shape.zipf_alpha > 0 else 5
     rng = np.random.default_rng(np.random.SeedSequence(seed_parts or [wid, 0, 3]))
     E = shape.routed_experts
-    ranks = rng.permutation(E) + 1
-    logp = -shape.zipf_alpha * np.log(ranks.astype(np.float64))
+    if shape.zipf_alpha > 0:
+        by_rank = rng.permutation(E)
+        ranks = np.empty(E, dtype=np.float64)
+        ranks[by_rank] = np.arange(1, E + 1)
+        logp = -shape.zipf_alpha * np.log(ranks)
+    else:
+        logp = np.zeros(E)
     g = rng.gumbel(size=(shape.tokens, E))
     keys = logp[None, :] + g
     choice = np.argsort(-keys, axis=1, kind="stable")[:, : shape.top_k]
-    return choice
+    return choice.astype(np.int32)
 
 
-def moe_group_offsets(shape: MoEShape, choice):
-    """Rows sorted by expert (stable in token order); shared experts follow as
-    groups of all tokens.  Returns (offsets int32 [G+1], row_token int64 [rows])."""
-    E = shape.routed_experts
-    tok = np.repeat(np.arange(shape.tokens), shape.top_k)
-    exp = choice.reshape(-1)
-    order = np.argsort(exp, kind="stable")
-    row_token = tok[order]
-    counts = np.bincount(exp, minlength=E)
-    counts = np.concatenate([counts, np.full(shape.shared_experts, shape.tokens)])
-    row_token = np.concatenate([row_token] + [np.arange(shape.tokens)] * shape.shared_experts)
-    offsets = np.zeros(len(counts) + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(counts)
-    return offsets, row_token
-
-
-def moe_inputs(shape: MoEShape, layer, device="cpu"):
-    """Inputs of one expert layer ("gate_up" or "down").
-
-    gate_up: the routed rows are copies of the tokens' hidden states
-    (~N(0,1); Moonlight with 1% outlier channels x20); down: an independent
-    N(0,1) matrix of the FFN width.  Weights [G, N, K] ~ N(0,0.02).
-    Returns (X bf16 [rows, K], W bf16 [G, N, K], offsets int32 [G+1]).
-    """
+def moe_token_matrix(shape: MoEShape, device="cpu"):
+    """The tokens' hidden states before dispatch, bf16 [tokens, hidden] ~ N(0,1)
+    (Moonlight: 1% outlier channels x20): the expert gate+up layer's input,
+    whose row r after dispatch is the state of the token the dispatch order
+    assigns to row r."""
     wid = 4 if shape.zipf_alpha > 0 else 5
-    choice = moe_routing(shape)
-    offsets, row_token = moe_group_offsets(shape, choice)
     outl = 0.01 if shape.zipf_alpha == 0 else 0.0
+    return normal_bf16((shape.tokens, shape.hidden), 1.0, seed_of(wid, 0, 0), device, outlier_frac=outl)
+
+
+def moe_down_input(shape: MoEShape, device="cpu"):
+    """The expert down layer's input, an independent bf16 [rows, ffn] ~ N(0,1)
+    (Moonlight: 1% outlier channels x20)."""
+    wid = 4 if shape.zipf_alpha > 0 else 5
+    outl = 0.01 if shape.zipf_alpha == 0 else 0.0
+    return normal_bf16((shape.rows, shape.ffn), 1.0, seed_of(wid, 1, 0), device, outlier_frac=outl)
+
+
+def moe_weights(shape: MoEShape, layer, device="cpu"):
+    """Expert weights of one layer ("gate_up" or "down"), bf16 [G, N, K] ~ N(0, 0.02)."""
+    wid = 4 if shape.zipf_alpha > 0 else 5
     names = [l[0] for l in shape.layers()]
     li = names.index(layer)
     _, N, K = shape.layers()[li]
-    if layer == "gate_up":
-        xt = normal_bf16((shape.tokens, K), 1.0, seed_of(wid, li, 0), device, outlier_frac=outl)
-        x = xt[torch.from_numpy(row_token).to(device)]
-    else:
-        x = normal_bf16((shape.rows, K), 1.0, seed_of(wid, li, 0), device, outlier_frac=outl)
-    w = normal_bf16((shape.groups, N, K), 0.02, seed_of(wid, li, 1), device)
-    return x.contiguous(), w, offsets
-
-
-def moe_dispatch_inputs(shape: MoEShape, device="cpu"):
-    """The expert gate_up layer before dispatch: the token matrix and the
-    routed row -> token map instead of the gathered rows.
-
-    Returns (XT bf16 [tokens, hidden], row_token int64 [rows], W bf16
-    [G, N, K], offsets int32 [G+1]); XT[row_token] is exactly the X that
-    moe_inputs(shape, "gate_up") returns, and W and offsets are its own.
-    """
-    wid = 4 if shape.zipf_alpha > 0 else 5
-    offsets, row_token = moe_group_offsets(shape, moe_routing(shape))
-    outl = 0.01 if shape.zipf_alpha == 0 else 0.0
-    _, N, K = shape.layers()[0]
-    xt = normal_bf16((shape.tokens, K), 1.0, seed_of(wid, 0, 0), device, outlier_frac=outl)
-    w = normal_bf16((shape.groups, N, K), 0.02, seed_of(wid, 0, 1), device)
-    return xt, row_token, w, offsets
+    return normal_bf16((shape.groups, N, K), 0.02, seed_of(wid, li, 1), device)

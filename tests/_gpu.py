@@ -87,3 +87,46 @@ def quantize_pair_oracle(x_bf16, w_bf16, mode=0):
     xq, xs = oracle.quant_act_1x128(bf16_bits(x_bf16), mode)
     wq, ws = oracle.quant_weight_128x128(bf16_bits(w_bf16), mode)
     return xq, xs, wq, ws
+
+
+def moe_layer_inputs(shape, layer, device="cuda"):
+    """One expert layer of a synthetic MoE workload: (X bf16 [rows, K], W bf16
+    [G, N, K], offsets int32 [G+1], row_index int32 [rows]).  The rows are in
+    the oracle's dispatch order (sorted by expert, stable by table position,
+    shared experts last); the gate+up input row r is the hidden state of token
+    row_index[r], the down input an independent matrix."""
+    import synth
+    ids = synth.moe_routing(shape)
+    off, rows, _ = oracle.moe_permute(ids, shape.routed_experts, shape.shared_experts)
+    w = synth.moe_weights(shape, layer, device)
+    if layer == "gate_up":
+        xt = synth.moe_token_matrix(shape, device)
+        x = xt[torch.from_numpy(rows.astype(np.int64)).to(xt.device)].contiguous()
+    else:
+        x = synth.moe_down_input(shape, device)
+    return x, w, off, rows
+
+
+def moe_rows(off, seed, per_group=2):
+    """Whole rows to check in every non-empty group: its first and last row and
+    `per_group` random ones (group of each row returned alongside)."""
+    rng = np.random.default_rng(seed)
+    ms, gs = [], []
+    for g in range(len(off) - 1):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        if r1 > r0:
+            pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, per_group)]))
+            ms.append(pick)
+            gs.append(np.full(pick.size, g))
+    return np.concatenate(ms), np.concatenate(gs)
+
+
+def moe_whole_rows_check(y_rows, aq_rows, as_rows, bq, bs, gs, what):
+    """GEMM tolerance on whole output rows of a grouped GEMM: y_rows [R, N]
+    (f64) against the oracle for the operand rows aq_rows/as_rows of groups gs,
+    rms taken over those rows."""
+    R, N = y_rows.shape
+    ms = np.repeat(np.arange(R), N)
+    ns = np.tile(np.arange(N), R)
+    ref = oracle.grouped_gemm_sampled_f64(aq_rows, as_rows, bq, bs, np.repeat(gs, N), ms, ns)
+    return gemm_tolerance_check(y_rows.reshape(-1), ref, what)

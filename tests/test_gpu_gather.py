@@ -17,7 +17,7 @@ import torch
 import oracle
 import synth
 from tests._gpu import (assert_bytes_equal, assert_scales_equal, gemm_tolerance_check, host_bf16_as_f64,
-                        host_f32, host_u8, lib, require_gpu, say)
+                        host_f32, host_u8, lib, moe_rows, moe_whole_rows_check, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -126,14 +126,17 @@ def test_quantize_before_dispatch_commutes():
     fp8q = lib()
     shape = synth.MoEShape("small", tokens=700, hidden=1024, routed_experts=16, top_k=4,
                            shared_experts=1, ffn=256, zipf_alpha=1.1)
-    xt, row_token, w, off = synth.moe_dispatch_inputs(shape, device="cuda")
+    off, row_token, _ = oracle.moe_permute(synth.moe_routing(shape), shape.routed_experts,
+                                           shape.shared_experts)
+    xt = synth.moe_token_matrix(shape, "cuda")
+    w = synth.moe_weights(shape, "gate_up", "cuda")
     G, N, K = w.shape
     say("gather commute", xt.shape, w.shape)
     bq = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
     bs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
     for g in range(G):
         fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
-    idx64 = torch.from_numpy(row_token).to("cuda")
+    idx64 = torch.from_numpy(row_token.astype(np.int64)).to("cuda")
     aq_t, as_t = fp8q.fp8_quant_act_1x128(xt)
     aq_r, as_r = fp8q.fp8_quant_act_1x128(xt[idx64].contiguous())
     torch.cuda.synchronize()
@@ -149,11 +152,14 @@ def test_quantize_before_dispatch_commutes():
 @pytest.mark.parametrize("shape", [synth.QWEN3, synth.MOONLIGHT], ids=lambda s: s.name)
 def test_moe_full_size(shape):
     """Full-size Qwen3-30B-A3B and Moonlight-16B gate_up layers: the gathered
-    GEMM equals the grouped GEMM on the gathered operands bit for bit, and
-    sampled outputs in every group match the oracle."""
+    GEMM equals the grouped GEMM on the gathered operands bit for bit, and in
+    every group its first, last and two random rows match the oracle whole."""
     require_gpu()
     fp8q = lib()
-    xt, row_token, w, off = synth.moe_dispatch_inputs(shape, device="cuda")
+    off, row_token, _ = oracle.moe_permute(synth.moe_routing(shape), shape.routed_experts,
+                                           shape.shared_experts)
+    xt = synth.moe_token_matrix(shape, "cuda")
+    w = synth.moe_weights(shape, "gate_up", "cuda")
     G, N, K = w.shape
     say("gather moe", shape.name, xt.shape, w.shape)
     bq = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
@@ -161,27 +167,15 @@ def test_moe_full_size(shape):
     for g in range(G):
         fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
     del w
-    idx64 = torch.from_numpy(row_token).to("cuda")
+    idx64 = torch.from_numpy(row_token.astype(np.int64)).to("cuda")
     offd = torch.from_numpy(off).to("cuda")
     aq, as_ = fp8q.fp8_quant_act_1x128(xt)
     yg = fp8q.fp8_grouped_gemm_gather(aq, as_, bq, bs, offd, idx64.to(torch.int32))
     yr = fp8q.fp8_grouped_gemm(aq[idx64].contiguous(), as_[idx64].contiguous(), bq, bs, offd)
     torch.cuda.synchronize()
     assert torch.equal(yg.view(torch.int16), yr.view(torch.int16)), f"{shape.name}: gather != grouped"
-    haq, has, hbq, hbs = aq.cpu().numpy(), as_.cpu().numpy(), bq.cpu().numpy(), bs.cpu().numpy()
-    rng = np.random.default_rng(5)
-    ms, gs = [], []
-    for g in range(G):
-        r0, r1 = int(off[g]), int(off[g + 1])
-        if r1 > r0:
-            pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 4)]))
-            ms.append(pick)
-            gs.append(np.full(pick.size, g))
-    ms = np.concatenate(ms)
-    gs = np.concatenate(gs)
-    ns = rng.integers(0, N, ms.size)
-    # sampled oracle rows are the tokens the routed rows point at
-    ref = oracle.grouped_gemm_sampled_f64(haq[row_token[ms]], has[row_token[ms]], hbq, hbs, gs,
-                                          np.arange(ms.size), ns)
-    got = yg.float().cpu().numpy().astype(np.float64)[ms, ns]
-    gemm_tolerance_check(got, ref, f"{shape.name} gather sampled")
+    ms, gs = moe_rows(off, seed=5)
+    tok = row_token[ms]
+    haq, has = aq.cpu().numpy()[tok], as_.cpu().numpy()[tok]   # the tokens the routed rows point at
+    yr_rows = yg.float().cpu().numpy().astype(np.float64)[ms]
+    moe_whole_rows_check(yr_rows, haq, has, bq.cpu().numpy(), bs.cpu().numpy(), gs, f"{shape.name} gather rows")

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import gemm_tolerance_check, host_bf16_as_f64, lib, require_gpu, say
+from tests._gpu import (gemm_tolerance_check, host_bf16_as_f64, lib, moe_layer_inputs, moe_rows,
+                        moe_whole_rows_check, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,13 +70,14 @@ def test_single_group_equals_dense():
 
 @pytest.mark.parametrize("shape", [synth.QWEN3, synth.MOONLIGHT], ids=lambda s: s.name)
 @pytest.mark.parametrize("layer", ["gate_up", "down"])
-def test_moe_full_size_sampled(shape, layer):
+def test_moe_full_size_rows(shape, layer):
     """Full-size Qwen3-30B-A3B (128 experts, Zipf(1.1) load) and Moonlight-16B
     (64 routed + 2 shared experts) expert layers: quantize + grouped GEMM on the
-    GPU, sampled outputs in every group checked against the oracle."""
+    GPU; in every group its first, last and two random rows are checked whole
+    (all N outputs) against the oracle."""
     require_gpu()
     fp8q = lib()
-    x, w, off = synth.moe_inputs(shape, layer, device="cuda")
+    x, w, off, _ = moe_layer_inputs(shape, layer)
     G, N, K = w.shape
     say("grouped moe", shape.name, layer, x.shape, w.shape)
     aq, as_ = fp8q.fp8_quant_act_1x128(x)
@@ -85,18 +87,7 @@ def test_moe_full_size_sampled(shape, layer):
         fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
     y = fp8q.fp8_grouped_gemm(aq, as_, bq, bs, torch.from_numpy(off).to("cuda"))
     torch.cuda.synchronize()
-    haq, has, hbq, hbs = aq.cpu().numpy(), as_.cpu().numpy(), bq.cpu().numpy(), bs.cpu().numpy()
-    rng = np.random.default_rng(3)
-    ms, gs = [], []
-    for g in range(G):
-        r0, r1 = int(off[g]), int(off[g + 1])
-        if r1 > r0:
-            pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 6)]))
-            ms.append(pick)
-            gs.append(np.full(pick.size, g))
-    ms = np.concatenate(ms)
-    gs = np.concatenate(gs)
-    ns = rng.integers(0, N, ms.size)
-    ref = oracle.grouped_gemm_sampled_f64(haq, has, hbq, hbs, gs, ms, ns)
-    got = y.float().cpu().numpy().astype(np.float64)[ms, ns]
-    gemm_tolerance_check(got, ref, f"{shape.name} {layer} sampled")
+    ms, gs = moe_rows(off, seed=3)
+    haq, has = aq.cpu().numpy()[ms], as_.cpu().numpy()[ms]
+    yr = y.float().cpu().numpy().astype(np.float64)[ms]
+    moe_whole_rows_check(yr, haq, has, bq.cpu().numpy(), bs.cpu().numpy(), gs, f"{shape.name} {layer} rows")
