@@ -93,24 +93,51 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.neg(src, out=dst)
-    t = time_loop(lambda: torch.neg(src, out=dst), reps, torch)
+    t = time_loop(lambda: torch.neg(src, out=dst), reps, torch, label="copy_1gib")
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / t / 1e9
 
 
-def time_loop(fn, reps, torch):
-    """Average duration (s) of fn() over reps launches, HIP events on the
-    current stream (the stream the library enqueues on)."""
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+# Per-launch statistics of every timed figure: label -> mean, median and
+# minimum in microseconds over the launches of its loop.
+STATS = {}
+
+
+def _stat(label, mean_s, durs_us):
+    """mean_us: the loop's back-to-back mean; median_us, min_us: over the same
+    number of launches, each bracketed by its own events."""
+    d = sorted(durs_us)
+    n = len(d)
+    med = d[n // 2] if n % 2 else 0.5 * (d[n // 2 - 1] + d[n // 2])
+    STATS[label] = {"mean_us": round(mean_s * 1e6, 2), "median_us": round(med, 2), "min_us": round(d[0], 2),
+                    "n": n}
+
+
+def time_loop(fn, reps, torch, label=None):
+    """Average duration (s) of fn() over reps back-to-back launches, HIP events
+    on the current stream (the stream the library enqueues on).  With a label,
+    a second loop brackets every launch with its own events and its median and
+    minimum go to STATS beside this mean (the per-launch event records add
+    gaps between launches, so the mean comes from the first loop only)."""
+    Ev = torch.cuda.Event
+    start, end = Ev(enable_timing=True), Ev(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(reps):
         fn()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / reps
+    mean = start.elapsed_time(end) / 1e3 / reps
+    if label:
+        evs = [(Ev(enable_timing=True), Ev(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        _stat(label, mean, [a.elapsed_time(b) * 1e3 for a, b in evs])
+    return mean
 
 
 def main():
@@ -118,8 +145,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="tokens per layer in the oracle's CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="tokens per layer in the oracle's single-thread CPU-baseline sample")
     ap.add_argument("--sections", default="pow2,fused,norm,backward,recal,moe,dispatch,attention,smallm,bf16,cpu",
                     help="extra measurements after the step (comma list of pow2, fused, norm, backward, recal, "
                          "moe, dispatch, attention, smallm, bf16, cpu)")
@@ -199,6 +226,12 @@ def main():
         for l, (e0, e1, e2) in zip(layers, marks[s]):
             in_step[l["name"]]["quant_s"] += e0.elapsed_time(e1) / 1e3 / args.steps
             in_step[l["name"]]["gemm_s"] += e1.elapsed_time(e2) / 1e3 / args.steps
+    _stat("step", step_s, [marks[s][0][0].elapsed_time(marks[s][-1][2]) * 1e3 for s in range(args.steps)])
+    for i, l in enumerate(layers):
+        _stat(f"step/{l['name']}/gemm", in_step[l["name"]]["gemm_s"],
+              [marks[s][i][1].elapsed_time(marks[s][i][2]) * 1e3 for s in range(args.steps)])
+        _stat(f"step/{l['name']}/act_quant", in_step[l["name"]]["quant_s"],
+              [marks[s][i][0].elapsed_time(marks[s][i][1]) * 1e3 for s in range(args.steps)])
 
     result = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)",
@@ -224,7 +257,7 @@ def main():
     }
 
     # ---- per-kernel figures from the timed region ----
-    reps = max(10, args.steps)
+    reps = max(20, args.steps)
     gemm_s, gemm_flops, per_layer = 0.0, 0.0, {}
     for l in layers:
         t = in_step[l["name"]]["gemm_s"]
@@ -251,7 +284,7 @@ def main():
         def qa(l=l, xs=xs, ctr=ctr):
             fp8q.fp8_quant_act_1x128(xs[ctr[0] % len(xs)], out=(l["aq"], l["as_"]))
             ctr[0] += 1
-        t = time_loop(qa, reps * len(xs), torch)
+        t = time_loop(qa, reps * len(xs), torch, label=f"act_quant/{l['name']}")
         b = act_quant_bytes(M, K)
         q_s += t
         q_bytes += b
@@ -306,9 +339,8 @@ def main():
     if "bf16" in sections:
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
     if "cpu" in sections:
-        for l in layers:
-            del l["w"]
         result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
+    result["timing_stats"] = STATS
     print(json.dumps(result), flush=True)
 
 
@@ -324,12 +356,10 @@ def small_m(fp8q, layers, torch, dev, reps, M=2048):
         def g(aq=aq, as_=as_, l=l, y=y):
             fp8q.fp8_blockscaled_gemm(aq, as_, l["bq"], l["bs"], out=y)
         g()
-        t = time_loop(g, reps, torch)
-        tiles256 = -(-M // 256) * -(-l["N"] // 256)
-        tiles128 = -(-M // 128) * -(-l["N"] // 256)
-        rows = 256 if -(-tiles256 // 256) * 10 <= -(-tiles128 // 256) * 7 else 128  # the library's choice
+        t = time_loop(g, reps, torch, label=f"small_m/{l['name']}")
+        big, small = fp8q.fp8_blockscaled_gemm_tile_plan(M, l["N"])  # the library's own choice
         out[l["name"]] = {"gemm_us": round(t * 1e6, 2), "tflops": round(2.0 * M * l["N"] * l["K"] / t / 1e12, 1),
-                          "tile_rows": rows}
+                          "panels_on_256_token_tiles": big, "panels_on_128_token_tiles": small}
         log(f"M={M} {l['name']}: {out[l['name']]}")
     return {"tokens": M, "per_layer": out}
 
@@ -347,7 +377,8 @@ def pow2_gemm(fp8q, layers, torch, M, reps):
     per, g_s, g_f = {}, 0.0, 0.0
     for l, aq, as_, bq, bs in ops:
         fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"])
-        t = time_loop(lambda: fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"]), reps, torch)
+        t = time_loop(lambda: fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"]), reps, torch,
+                      label=f"pow2_gemm/{l['name']}")
         f = 2.0 * M * l["N"] * l["K"]
         g_s += t
         g_f += f
@@ -358,7 +389,7 @@ def pow2_gemm(fp8q, layers, torch, M, reps):
             fp8q.fp8_quant_act_1x128(l["x"], "pow2", out=(aq, as_))
             fp8q.fp8_blockscaled_gemm_pow2(aq, as_, bq, bs, out=l["y"])
     step()
-    t_step = time_loop(step, reps, torch)
+    t_step = time_loop(step, reps, torch, label="pow2_step")
     tf = g_f / g_s / 1e12
     log(f"pow2 gemm {tf:.1f} TFLOP/s; pow2 step {g_f / t_step / 1e12:.1f} TFLOP/s")
     del ops
@@ -385,8 +416,8 @@ def fused_output_quant(fp8q, layers, torch, M, reps):
             fp8q.fp8_blockscaled_gemm_quant(aq, as_, bq, bs, "amax", out=(yq, ys))
         separate()
         fused()
-        ts = time_loop(separate, reps, torch)
-        tf = time_loop(fused, reps, torch)
+        ts = time_loop(separate, reps, torch, label=f"fused_output_quant/{l['name']}/separate")
+        tf = time_loop(fused, reps, torch, label=f"fused_output_quant/{l['name']}/fused")
         f = 2.0 * M * l["N"] * l["K"]
         t_sep += ts
         t_fus += tf
@@ -427,9 +458,9 @@ def fused_swiglu(fp8q, layers, torch, M, reps):
         fp8q.fp8_blockscaled_gemm_swiglu_quant(aq, as_, bq, bs, "amax", out=(hq, hs))
     separate()
     fused()
-    tg = time_loop(gemm, reps, torch)
-    ts = time_loop(separate, reps, torch)
-    tf = time_loop(fused, reps, torch)
+    tg = time_loop(gemm, reps, torch, label="swiglu/gemm_alone")
+    ts = time_loop(separate, reps, torch, label="swiglu/separate")
+    tf = time_loop(fused, reps, torch, label="swiglu/fused")
     f = 2.0 * M * l["N"] * l["K"]
     log(f"fused swiglu: {tf * 1e6:.1f} us ({f / tf / 1e12:.1f} TFLOP/s) vs {ts * 1e6:.1f} us separate, "
         f"{tg * 1e6:.1f} us bf16 GEMM alone")
@@ -469,9 +500,9 @@ def rmsnorm_quant(fp8q, torch, dev, M, reps, copy_gbs):
         ctr[0] += 1
     fused()
     separate()
-    tf = time_loop(fused, reps * nrot, torch)
-    ts = time_loop(separate, reps * nrot, torch)
-    tq = time_loop(quant_only, reps * nrot, torch)
+    tf = time_loop(fused, reps * nrot, torch, label="rmsnorm_quant/fused")
+    ts = time_loop(separate, reps * nrot, torch, label="rmsnorm_quant/separate")
+    tq = time_loop(quant_only, reps * nrot, torch, label="rmsnorm_quant/quant_alone")
     b = act_quant_bytes(M, K)
     log(f"rmsnorm+quant {b / tf / 1e9:.1f} GB/s ({tf * 1e6:.1f} us) vs {ts * 1e6:.1f} us separate, "
         f"{tq * 1e6:.1f} us quantizer alone")
@@ -508,7 +539,7 @@ def recalibration(fp8q, synth, torch, dev, copy_gbs=None):
             fp8q.fp8_quant_weight_128x128_batched(batch, mode)
         for name, fn in (("per_matrix", one_pass), ("batched", batched)):
             fn()
-            t = time_loop(fn, 3, torch)
+            t = time_loop(fn, 3, torch, label=f"recalibration/{mode}/{name}")
             gbs = total / t / 1e9
             r = {"ms_per_pass": round(t * 1e3, 3), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             if copy_gbs:
@@ -520,34 +551,60 @@ def recalibration(fp8q, synth, torch, dev, copy_gbs=None):
     return res
 
 
+def moe_dispatch_order(fp8q, synth, torch, dev, shape):
+    """The routing table of a synthetic MoE workload on the device and its
+    dispatch order from the library (offsets, row index)."""
+    ids = torch.from_numpy(synth.moe_routing(shape)).to(dev)
+    off, rows, _ = fp8q.fp8_moe_permute(ids, shape.routed_experts, shape.shared_experts)
+    return ids, off, rows
+
+
 def moe(fp8q, synth, torch, dev, reps):
-    """Grouped GEMM on the Qwen3-30B-A3B and Moonlight-16B expert shapes."""
+    """Grouped GEMM on the Qwen3-30B-A3B and Moonlight-16B expert shapes, rows
+    in the library's dispatch order; beside it a dense bf16 torch.matmul with
+    the same M_total x N x K (one weight for all rows) as a labelled proxy for
+    a bf16 grouped GEMM (the FP8/BF16 ratio of the pages' linear layers)."""
     out = {}
     for shape in (synth.QWEN3, synth.MOONLIGHT):
+        _, offd, rows = moe_dispatch_order(fp8q, synth, torch, dev, shape)
         for layer in ("gate_up", "down"):
-            x, w, off = synth.moe_inputs(shape, layer, device=dev)
+            w = synth.moe_weights(shape, layer, device=dev)
+            if layer == "gate_up":
+                xt = synth.moe_token_matrix(shape, device=dev)
+                x = torch.index_select(xt, 0, rows.long())
+                del xt
+            else:
+                x = synth.moe_down_input(shape, device=dev)
             G, N, K = w.shape
             Mt = x.shape[0]
             bq = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
             bs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
             for g in range(G):
                 fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
-            del w
-            offd = torch.from_numpy(off).to(dev)
             aq, as_ = fp8q.fp8_quant_act_1x128(x)
             y = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
-            t = time_loop(lambda: fp8q.fp8_grouped_gemm(aq, as_, bq, bs, offd, out=y), reps, torch)
+            label = f"moe/{shape.name}/{layer}"
+            t = time_loop(lambda: fp8q.fp8_grouped_gemm(aq, as_, bq, bs, offd, out=y), reps, torch, label=label)
             flops = 2.0 * Mt * N * K
             tf = flops / t / 1e12
             hbm_bytes = Mt * K + G * N * K + 2 * Mt * N + Mt * (K // 128) * 4 + G * (N // 128) * (K // 128) * 4
             roof = min(FP8_PEAK_TFLOPS, flops / (hbm_bytes / (HBM_PEAK_GBS * 1e9)) / 1e12)
+            w0 = w[0]
+            for _ in range(3):
+                torch.matmul(x, w0.t(), out=y)
+            tb = time_loop(lambda: torch.matmul(x, w0.t(), out=y), reps, torch, label=label + "/bf16_dense_proxy")
             out[f"{shape.name}/{layer}"] = {
                 "rows": Mt, "groups": G, "N": N, "K": K, "us": round(t * 1e6, 2),
                 "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
-                "roof_tflops": round(roof, 1), "frac_roof": round(tf / roof, 4)}
-            log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}")
-            del x, bq, bs, aq, as_, y
+                "roof_tflops": round(roof, 1), "frac_roof": round(tf / roof, 4),
+                "bf16_dense_proxy_tflops": round(flops / tb / 1e12, 1),
+                "fp8_over_bf16_dense_proxy": round(tb / t, 3)}
+            log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}; "
+                f"bf16 dense proxy {flops / tb / 1e12:.1f}")
+            del x, w, w0, bq, bs, aq, as_, y
             torch.cuda.empty_cache()
+    out["bf16_dense_proxy"] = ("torch.matmul in bf16 of all M_total rows against one expert's weight: the same "
+                               "flops as the grouped GEMM in one dense call, standing in for a bf16 grouped GEMM")
     return out
 
 
@@ -590,10 +647,12 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
         fp8q.fp8_quant_act_dual(l["x"], mode="pow2", rowwise=False, out=(None, None, xtq2, xts2))
         wg2 = lambda: fp8q.fp8_blockscaled_gemm_wgrad_pow2(gtq2, gts2, xtq2, xts2, out=dw)
         wg2()
-        t_wg2 = time_loop(wg2, reps, torch)
+        t_wg2 = time_loop(wg2, reps, torch, label=f"backward/{l['name']}/wgrad_pow2")
         del gtq2, gts2, xtq2, xts2
-        t_qg, t_qx, t_qw = (time_loop(f, reps, torch) for f in (qg, qx, qw))
-        t_dg, t_wg = time_loop(dg, reps, torch), time_loop(wg, reps, torch)
+        t_qg, t_qx, t_qw = (time_loop(f, reps, torch, label=f"backward/{l['name']}/{n}")
+                            for f, n in ((qg, "quant_dy_dual"), (qx, "quant_x_colwise"), (qw, "quant_w_dual")))
+        t_dg = time_loop(dg, reps, torch, label=f"backward/{l['name']}/dgrad")
+        t_wg = time_loop(wg, reps, torch, label=f"backward/{l['name']}/wgrad")
         f_dg, f_wg = 2.0 * M * N * K, 2.0 * N * K * Mp
         b_qg = M * N * 4 + 2 * M * (N // 128) * 4         # bf16 in, two code layouts, two scale sets
         b_qx = M * K * 3 + K * (Mp // 128) * 4
@@ -635,7 +694,7 @@ def backward(fp8q, synth, layers, torch, dev, M, reps):
             fp8q.fp8_quant_act_dual(xs[ctr[0] % len(xs)], out=bufs)
             ctr[0] += 1
         qd()
-        t = time_loop(qd, reps * len(xs), torch)
+        t = time_loop(qd, reps * len(xs), torch, label=f"backward/{l['name']}/act_dual_rotating")
         b = M * K * 4 + M * (K // 128) * 4 + K * (Mp // 128) * 4
         q_s += t
         q_b += b
@@ -680,11 +739,11 @@ def attention(fp8q, synth, torch, dev, reps):
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     run = lambda: fp8q.fp8_attention_decode(q_q, q_s, cache, dlen, out=out)
     run()
-    t = time_loop(run, reps * 5, torch)
+    t = time_loop(run, reps * 5, torch, label="attention_decode/b64")
     # the same without a workspace: one workgroup per (sequence, head), unsplit
     run1 = lambda: fp8q.fp8_attention_decode(q_q, q_s, cache, dlen, out=out, workspace=None)
     run1()
-    t1 = time_loop(run1, reps * 5, torch)
+    t1 = time_loop(run1, reps * 5, torch, label="attention_decode/b64_unsplit")
     kv = int(lens.sum()) * Hkv * 2 * (D + 4)
     nbytes = kv + B * Hq * (D + 4) + B * Hq * D * 2
     # a small batch (the last sequences of a rollout): 8 sequences give 64
@@ -697,7 +756,8 @@ def attention(fp8q, synth, torch, dev, reps):
     r8u = lambda: fp8q.fp8_attention_decode(q8, s8, cache8, d8, out=out8, workspace=None)
     r8()
     r8u()
-    t8, t8u = time_loop(r8, reps * 5, torch), time_loop(r8u, reps * 5, torch)
+    t8 = time_loop(r8, reps * 5, torch, label="attention_decode/b8_split")
+    t8u = time_loop(r8u, reps * 5, torch, label="attention_decode/b8_unsplit")
     nb8 = int(lens[:b8].sum()) * Hkv * 2 * (D + 4) + b8 * Hq * (D + 4) + b8 * Hq * D * 2
     # the cache append of one decode step (one key and value row per sequence and head)
     kn = torch.randn((B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
@@ -705,7 +765,7 @@ def attention(fp8q, synth, torch, dev, reps):
     pos = torch.from_numpy(np.minimum(lens, S - 1)).to(dev)
     app = lambda: fp8q.fp8_kv_cache_append(kn, vn, pos, cache)
     app()
-    t_app = time_loop(app, reps * 5, torch)
+    t_app = time_loop(app, reps * 5, torch, label="attention_decode/append")
     res = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "cache_tokens": S,
            "mean_len": float(lens.mean()), "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1),
            "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
@@ -723,24 +783,29 @@ def attention(fp8q, synth, torch, dev, reps):
 
 
 def dispatch(fp8q, synth, torch, dev, reps):
-    """MoE gate_up layer with the tokens quantized before dispatch (quantize T
-    token rows once, then the grouped GEMM gathers each routed row's FP8 bytes
-    by index) against quantizing after dispatch (gather the bf16 rows, quantize
-    all M_total routed rows, grouped GEMM).  The bf16 gather is torch's index
-    copy, standing in for the dispatch of bf16 rows on one GPU."""
+    """MoE gate_up layer from the routing table to the expert outputs.  Route:
+    the library's dispatch order (fp8_moe_permute: group offsets and row ->
+    token map on the device).  Quantize before dispatch: quantize the T token
+    rows once, then the grouped GEMM gathers each routed row's FP8 bytes by
+    index.  Against quantize after dispatch: gather the bf16 rows (torch's
+    index copy, standing in for the dispatch of bf16 rows on one GPU),
+    quantize all M_total routed rows, grouped GEMM."""
     out = {}
     for shape in (synth.QWEN3, synth.MOONLIGHT):
-        xt, row_token, w, off = synth.moe_dispatch_inputs(shape, device=dev)
+        ids, offd, idx = moe_dispatch_order(fp8q, synth, torch, dev, shape)
+        xt = synth.moe_token_matrix(shape, device=dev)
+        w = synth.moe_weights(shape, "gate_up", device=dev)
         G, N, K = w.shape
-        T, Mt = xt.shape[0], row_token.size
+        T, Mt = xt.shape[0], idx.numel()
+        E, ns = shape.routed_experts, shape.shared_experts
         bq = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
         bs = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=dev)
         for g in range(G):
             fp8q.fp8_quant_weight_128x128(w[g], out=(bq[g], bs[g]))
         del w
-        offd = torch.from_numpy(off).to(dev)
-        idx64 = torch.from_numpy(row_token).to(dev)
-        idx = idx64.to(torch.int32)
+        ws = torch.empty(fp8q.fp8_moe_permute_workspace_size(T, shape.top_k, E), dtype=torch.uint8, device=dev)
+        entry = torch.empty(T * shape.top_k, dtype=torch.int32, device=dev)
+        idx64 = idx.long()
         xr = torch.empty((Mt, K), dtype=torch.bfloat16, device=dev)
         aq_r = torch.empty((Mt, K), dtype=torch.uint8, device=dev)
         as_r = torch.empty((Mt, K // 128), dtype=torch.float32, device=dev)
@@ -748,37 +813,49 @@ def dispatch(fp8q, synth, torch, dev, reps):
         as_t = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
         y = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
 
+        def route():
+            fp8q.fp8_moe_permute(ids, E, ns, out=(offd, idx, entry), workspace=ws)
+
         def after():
+            route()
             torch.index_select(xt, 0, idx64, out=xr)
             fp8q.fp8_quant_act_1x128(xr, out=(aq_r, as_r))
             fp8q.fp8_grouped_gemm(aq_r, as_r, bq, bs, offd, out=y)
 
         def before():
+            route()
             fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t))
             fp8q.fp8_grouped_gemm_gather(aq_t, as_t, bq, bs, offd, idx, out=y)
 
         after()
         before()
-        t_after = time_loop(after, reps, torch)
-        t_before = time_loop(before, reps, torch)
-        t_copy = time_loop(lambda: torch.index_select(xt, 0, idx64, out=xr), reps, torch)
-        t_qr = time_loop(lambda: fp8q.fp8_quant_act_1x128(xr, out=(aq_r, as_r)), reps, torch)
-        t_qt = time_loop(lambda: fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t)), reps, torch)
-        t_gr = time_loop(lambda: fp8q.fp8_grouped_gemm(aq_r, as_r, bq, bs, offd, out=y), reps, torch)
-        t_gg = time_loop(lambda: fp8q.fp8_grouped_gemm_gather(aq_t, as_t, bq, bs, offd, idx, out=y), reps, torch)
+        lb = f"dispatch/{shape.name}"
+        t_after = time_loop(after, reps, torch, label=lb + "/after")
+        t_before = time_loop(before, reps, torch, label=lb + "/before")
+        t_route = time_loop(route, reps, torch, label=lb + "/route")
+        t_copy = time_loop(lambda: torch.index_select(xt, 0, idx64, out=xr), reps, torch, label=lb + "/bf16_gather")
+        t_qr = time_loop(lambda: fp8q.fp8_quant_act_1x128(xr, out=(aq_r, as_r)), reps, torch,
+                         label=lb + "/quant_routed_rows")
+        t_qt = time_loop(lambda: fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t)), reps, torch,
+                         label=lb + "/quant_tokens")
+        t_gr = time_loop(lambda: fp8q.fp8_grouped_gemm(aq_r, as_r, bq, bs, offd, out=y), reps, torch,
+                         label=lb + "/grouped_gemm")
+        t_gg = time_loop(lambda: fp8q.fp8_grouped_gemm_gather(aq_t, as_t, bq, bs, offd, idx, out=y), reps, torch,
+                         label=lb + "/gather_gemm")
         us = lambda t: round(t * 1e6, 2)
         out[shape.name] = {
             "tokens": T, "rows": Mt, "groups": G, "N": N, "K": K,
             "after_us": us(t_after), "before_us": us(t_before),
             "before_speedup": round(t_after / t_before, 3),
-            "bf16_gather_copy_us": us(t_copy), "quant_routed_rows_us": us(t_qr), "quant_tokens_us": us(t_qt),
-            "grouped_gemm_us": us(t_gr), "gather_gemm_us": us(t_gg),
+            "route_us": us(t_route), "bf16_gather_copy_us": us(t_copy), "quant_routed_rows_us": us(t_qr),
+            "quant_tokens_us": us(t_qt), "grouped_gemm_us": us(t_gr), "gather_gemm_us": us(t_gg),
             "gather_gemm_over_grouped": round(t_gg / t_gr, 3),
             "dispatched_bytes_bf16": Mt * K * 2, "dispatched_bytes_fp8": Mt * K + Mt * (K // 128) * 4,
+            "chain": "route (fp8_moe_permute) + quantize + GEMM, from the routing table to the expert outputs",
         }
-        log(f"dispatch {shape.name}: after {t_after * 1e6:.1f} us, before {t_before * 1e6:.1f} us "
-            f"(gather GEMM {t_gg * 1e6:.1f} vs grouped {t_gr * 1e6:.1f} us)")
-        del xt, bq, bs, xr, aq_r, as_r, aq_t, as_t, y
+        log(f"dispatch {shape.name}: route {t_route * 1e6:.1f} us; after {t_after * 1e6:.1f} us, "
+            f"before {t_before * 1e6:.1f} us (gather GEMM {t_gg * 1e6:.1f} vs grouped {t_gr * 1e6:.1f} us)")
+        del xt, bq, bs, xr, aq_r, as_r, aq_t, as_t, y, ws, entry
         torch.cuda.empty_cache()
     return out
 
@@ -790,7 +867,7 @@ def bf16_compare(layers, torch, M, reps, fp8_gemm_tflops):
         x, w = l["x"], l["w"]
         for _ in range(3):  # library heuristics / first-call setup stay out of the timing
             torch.matmul(x, w.t())
-        t = time_loop(lambda: torch.matmul(x, w.t()), reps, torch)
+        t = time_loop(lambda: torch.matmul(x, w.t()), reps, torch, label=f"bf16_matmul/{l['name']}")
         f = 2.0 * M * l["N"] * l["K"]
         tot_s += t
         tot_f += f
@@ -816,7 +893,7 @@ def vendor_fp8_tensorwise(layers, torch, M, reps, fp8_gemm_tflops):
             run = lambda: torch._scaled_mm(xq, wq.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
             for _ in range(3):
                 run()
-            t = time_loop(run, reps, torch)
+            t = time_loop(run, reps, torch, label=f"vendor_fp8_tensorwise/{l['name']}")
             f = 2.0 * M * l["N"] * l["K"]
             tot_s += t
             tot_f += f
@@ -830,31 +907,73 @@ def vendor_fp8_tensorwise(layers, torch, M, reps, fp8_gemm_tflops):
             "blockscaled_over_tensorwise": round(fp8_gemm_tflops / tf, 3)}
 
 
-def cpu_baseline(layers, synth, M, rows):
-    """The CPU oracle, as it stands, on a bounded sample of the same step: the
-    first `rows` tokens of each of the four layers (activation quantization of
-    those rows + their GEMM rows in fp64)."""
+def _cpu_model():
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(layers, synth, M, one_thread_rows):
+    """The CPU oracle, as it stands, on the step's workload: the full step
+    (1x128 quantization of each layer's 4096 activation rows + the fp64
+    block-scaled GEMM) on all host threads.  The weights are quantized by the
+    oracle itself, outside the timing (as they are once per policy update).
+    Also: a labelled single-thread run on the first rows of each layer, and
+    the oracle's quantizers in GB/s (one Llama activation, one recalibration
+    matrix)."""
     import oracle
-    log(f"cpu baseline: oracle on {rows} of {M} tokens per layer")
+    import numpy as np
+    log(f"cpu baseline: oracle on the full step ({M} tokens x 4 layers)")
     inputs = []
     for l in layers:
-        xs = synth.bf16_bits(l["x"][:rows])
-        bq = l["bq"].cpu().numpy()
-        bs = l["bs"].cpu().numpy()
+        xs = synth.bf16_bits(l["x"])
+        bq, bs = oracle.quant_weight_128x128(synth.bf16_bits(l["w"]))
         inputs.append((xs, bq, bs, l["N"], l["K"]))
-    flops = 0.0
-    t0 = time.perf_counter()
-    for xs, bq, bs, N, K in inputs:
-        aq, as_ = oracle.quant_act_1x128(xs)
-        oracle.gemm_f64(aq, as_, bq, bs)
-        flops += 2.0 * rows * N * K
-    dt = time.perf_counter() - t0
+    threads = oracle.num_threads()
+
+    def run(rows):
+        flops, t0 = 0.0, time.perf_counter()
+        for xs, bq, bs, N, K in inputs:
+            aq, as_ = oracle.quant_act_1x128(np.ascontiguousarray(xs[:rows]))
+            oracle.gemm_f64(aq, as_, bq, bs)
+            flops += 2.0 * rows * N * K
+        return flops, time.perf_counter() - t0
+    flops, dt = run(M)
     v = flops / dt / 1e12
-    log(f"cpu baseline {v * 1e3:.2f} GFLOP/s in {dt:.1f} s")
-    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"first {rows} of {M} tokens of each of the 4 Llama layers: "
-                      "1x128 quantization + fp64 block-scaled GEMM rows"}
+    log(f"cpu baseline {v * 1e3:.2f} GFLOP/s in {dt:.1f} s on {threads} threads")
+    oracle.set_num_threads(1)
+    try:
+        f1, d1 = run(one_thread_rows)
+    finally:
+        oracle.set_num_threads(0)
+    log(f"cpu baseline, 1 thread: {f1 / d1 / 1e9:.2f} GFLOP/s in {d1:.1f} s")
+    # quantizers: a 4096 x 4096 activation and the largest recalibration matrix
+    xq = inputs[1][0]
+    t0 = time.perf_counter()
+    oracle.quant_act_1x128(xq)
+    ta = time.perf_counter() - t0
+    wq = synth.bf16_bits(layers[2]["w"])
+    t0 = time.perf_counter()
+    oracle.quant_weight_128x128(wq)
+    tw = time.perf_counter() - t0
+    ga = act_quant_bytes(*xq.shape) / ta / 1e9
+    gw = weight_quant_bytes(*wq.shape) / tw / 1e9
+    log(f"cpu oracle quantizers: activation {ga:.2f} GB/s, weight {gw:.2f} GB/s")
+    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2), "cpu_model": _cpu_model(),
+            "sample": f"the full step: all {M} tokens of each of the 4 Llama layers, 1x128 activation "
+                      "quantization + fp64 block-scaled GEMM (weights quantized by the oracle, untimed)",
+            "one_thread": {"value": round(f1 / d1 / 1e12, 6), "unit": "TFLOP/s", "seconds": round(d1, 2),
+                           "sample": f"first {one_thread_rows} tokens of each of the 4 layers"},
+            "quantizers": {"act_gbs": round(ga, 3), "act_shape": list(xq.shape),
+                           "weight_gbs": round(gw, 3), "weight_shape": list(wq.shape),
+                           "bytes": "algorithmic: 2 read + 1 written per element + 4 per scale"}}
 
 
 if __name__ == "__main__":

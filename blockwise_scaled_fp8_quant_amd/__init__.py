@@ -518,3 +518,53 @@ def fp8_attention_decode_noalloc(q_q, q_s, cache, seq_len, out):
                _lib.load().fp8_attention_decode_noalloc(pq, pqs, pkq, pks, pvq, pvs, plen, py, B, Hq, Hkv, S,
                                                         _stream(q_q)))
     return out
+
+
+def fp8_moe_permute_workspace_size(T, k, E):
+    return _lib.load().fp8_moe_permute_workspace_size(T, k, E)
+
+
+def fp8_moe_permute(expert_ids, E, n_shared=0, out=None, workspace=None):
+    """Routing table int32 [T, k] (device) -> (group_offsets int32 [E+n_shared+1],
+    row_index int32 [T*(k+n_shared)], entry_row int32 [T*k]): rows sorted by
+    expert, stable in table order, shared experts last -- the offsets and
+    row map of fp8_grouped_gemm / fp8_grouped_gemm_gather.  out: optional
+    (offsets, row_index, entry_row) tensors (entry_row may be None);
+    workspace: optional device tensor of fp8_moe_permute_workspace_size
+    bytes (allocated here if None)."""
+    ids = _dev(expert_ids, "expert_ids", torch.int32, 2)
+    T, k = expert_ids.shape
+    dev = expert_ids.device
+    rows = T * (k + n_shared)
+    if out is None:
+        off = torch.empty(E + n_shared + 1, dtype=torch.int32, device=dev)
+        row_index = torch.empty(rows, dtype=torch.int32, device=dev)
+        entry_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    else:
+        off, row_index, entry_row = out
+    poff = _dev(off, "group_offsets", torch.int32, 1)
+    prow = _dev(row_index, "row_index", torch.int32, 1)
+    pent = None if entry_row is None else _dev(entry_row, "entry_row", torch.int32, 1)
+    if off.numel() != E + n_shared + 1 or row_index.numel() != rows or (
+            entry_row is not None and entry_row.numel() != T * k):
+        raise ValueError("output sizes do not match the routing table")
+    need = fp8_moe_permute_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    pws = ctypes.c_void_p(int(workspace.data_ptr()))
+    nws = workspace.numel() * workspace.element_size()
+    _lib.check("fp8_moe_permute", _lib.load().fp8_moe_permute(ids, T, k, E, n_shared, poff, prow, pent, pws, nws,
+                                                              _stream(expert_ids)))
+    return off, row_index, entry_row
+
+
+def fp8_blockscaled_gemm_tile_plan(M, N, bf16_output=True):
+    """(panels on 256-token tiles, panels on 128-token tiles) of a dense
+    M x N GEMM: how the library splits its output's 256-row weight panels
+    between its two tile shapes."""
+    n1 = _lib.load().fp8_blockscaled_gemm_tile_plan(M, N, 1 if bf16_output else 0)
+    if n1 < 0:
+        raise ValueError("invalid GEMM size")
+    return n1, -(-N // 256) - n1

@@ -20,6 +20,7 @@ ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_wei
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
                 "fp8_kv_cache_append",
                 "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8_attention_decode_noalloc",
+                "fp8_moe_permute", "fp8_moe_permute_workspace_size", "fp8_blockscaled_gemm_tile_plan",
                 "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version")
 
 _lib = None
@@ -70,6 +71,12 @@ def load():
     lib.fp8_kv_cache_append.restype = ci
     lib.fp8_attention_decode.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p, i64, p]
     lib.fp8_attention_decode.restype = ci
+    lib.fp8_blockscaled_gemm_tile_plan.argtypes = [i64, i64, ci]
+    lib.fp8_blockscaled_gemm_tile_plan.restype = i32
+    lib.fp8_moe_permute.argtypes = [p, i64, i32, i32, i32, p, p, p, p, i64, p]
+    lib.fp8_moe_permute.restype = ci
+    lib.fp8_moe_permute_workspace_size.argtypes = [i64, i32, i32]
+    lib.fp8_moe_permute_workspace_size.restype = i64
     lib.fp8_attention_decode_noalloc.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p]
     lib.fp8_attention_decode_noalloc.restype = ci
     lib.fp8_attention_decode_workspace_size.argtypes = [i32, i32, i32, i64]

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["quant.hip", "gemm.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "attention.hip", "moe.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

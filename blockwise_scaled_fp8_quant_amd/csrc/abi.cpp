@@ -418,6 +418,39 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uin
                   __func__);
 }
 
+int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int bf16_output) {
+  if (M < 1 || N < 128 || N % 128 != 0 || M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return -1;
+  return (int32_t)fp8q::dense_large_panels(M, N, bf16_output != 0);
+}
+
+int64_t fp8_moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > 1024 || T > (((int64_t)1 << 31) - 1) / k) return 0;
+  return fp8q::moe_permute_workspace_bytes(T * k, E);
+}
+
+fp8q_status fp8_moe_permute(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                            int32_t *group_offsets, int32_t *row_index, int32_t *entry_row, void *workspace,
+                            int64_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(T >= 0 && n_shared >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(k >= 1, FP8Q_EINVAL, "k must be at least 1");
+  FP8Q_REQUIRE(E >= 1 && E <= 1024, FP8Q_ESHAPE, "E must be in [1, 1024]");
+  FP8Q_REQUIRE(T <= (((int64_t)1 << 31) - 1) / ((int64_t)k + n_shared), FP8Q_ESHAPE,
+               "T * (k + n_shared) must be below 2^31");
+  FP8Q_REQUIRE(group_offsets && workspace, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(T == 0 || (expert_ids && row_index), FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(expert_ids) && aligned16(group_offsets) && aligned16(row_index) && aligned16(entry_row) &&
+                   aligned16(workspace),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  FP8Q_REQUIRE(workspace_bytes >= fp8_moe_permute_workspace_size(T, k, E), FP8Q_EINVAL,
+               "workspace smaller than fp8_moe_permute_workspace_size()");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_moe_permute(expert_ids, T, k, E, n_shared, group_offsets, row_index, entry_row,
+                                           workspace, (hipStream_t)stream),
+                  __func__);
+}
+
 fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s, const uint8_t *k_cache,
                                          const float *k_scale, const uint8_t *v_cache, const float *v_scale,
                                          const int32_t *seq_len, uint16_t *out, int32_t B, int32_t Hq,

@@ -39,6 +39,11 @@ hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
                                          uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
                                          int mode, hipStream_t stream);
 
+// Weight panels (256 rows each) of a dense M x N GEMM output that run on
+// 256-row tiles; the others run on 128-row tiles (bf16_out: a bf16 output,
+// which may be split between the two shapes).
+int64_t dense_large_panels(int64_t M, int64_t N, bool bf16_out);
+
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const uint8_t *b_q, const float *b_s,
                                const int32_t *group_offsets, int32_t G,
@@ -80,6 +85,14 @@ hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int6
                                       const int32_t *group_offsets, const int32_t *row_index, int32_t G,
                                       int64_t M_total, int64_t N, int64_t K, uint16_t *y, bool pow2,
                                       hipStream_t stream);
+
+// MoE dispatch order: routing table ids [T][k] -> offsets [E+n_shared+1],
+// row_index [T*(k+n_shared)], entry_row [T*k] (may be null), through a
+// workspace of moe_permute_workspace_bytes(T*k, E).  1 <= E <= 1024.
+int64_t moe_permute_workspace_bytes(int64_t n, int32_t E);
+hipError_t launch_moe_permute(const int32_t *ids, int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                              int32_t *offsets, int32_t *row_index, int32_t *entry_row, void *workspace,
+                              hipStream_t stream);
 
 // FP8 KV cache: quantize one new key and value row per sequence and head
 // (1x128 blocks) into [B][H][S][128] caches at token position pos[b].

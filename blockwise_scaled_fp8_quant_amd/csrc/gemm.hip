@@ -1181,6 +1181,32 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Weight panels (256 rows each) of an M x N output that go on 256-row tiles;
+// the rest go on 128-row tiles.  The shape with the shortest estimated time:
+// rounds of tiles over the 256 CUs times a tile's time, a 128-row tile taking
+// about 0.7 of a 256-row one (measured on the Llama shapes).  A bf16 output
+// may also be split by weight panels: the first n1 panels on 256-row tiles,
+// the rest on 128-row tiles, as two launches into column slices of Y.  At 4096
+// tokens QKV's 24 panels make 384 large tiles (two rounds, the second half
+// empty); 16 panels on large tiles (one round) and 8 on small ones (one round)
+// cost 1.7 instead of 2.  At 2048 tokens QKV's 192 large tiles (one round)
+// beat 384 small ones (+37%), while O and down (128 large tiles, half the CUs
+// idle) take small tiles.
+int64_t dense_large_panels(int64_t M, int64_t N, bool bf16_out) {
+  const int64_t tiles_n = (N + kBN - 1) / kBN;
+  const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
+  const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  auto cost = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
+    return (mt_large * n1 + 255) / 256 * 10 + (mt_small * (tiles_n - n1) + 255) / 256 * 7;
+  };
+  int64_t n1 = cost(tiles_n) <= cost(0) ? tiles_n : 0;
+  if (bf16_out) {
+    for (int64_t c = 1; c < tiles_n; ++c)
+      if (cost(c) < cost(n1)) n1 = c;
+  }
+  return n1;
+}
+
 template <bool kPow2, int kOut = kOutBf16, bool kBRow = false, bool kSwiGLU = false>
 static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                         uint16_t *y, uint8_t *yq, float *ys, int64_t M, int64_t N, int64_t K,
@@ -1189,26 +1215,9 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N};
-  // The tile shapes with the shortest estimated time: rounds of tiles over
-  // the 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a
-  // 256-row one (measured on the Llama shapes).  A bf16 output may also be
-  // split by weight panels: the first n1 panels on 256-row tiles, the rest on
-  // 128-row tiles, as two launches into column slices of Y.  At 4096 tokens
-  // QKV's 24 panels make 384 large tiles (two rounds, the second half
-  // empty); 16 panels on large tiles (one round) and 8 on small ones (one
-  // round) cost 1.7 instead of 2.  At 2048 tokens QKV's 192 large tiles (one
-  // round) beat 384 small ones (+37%), while O and down (128 large tiles,
-  // half the CUs idle) take small tiles.
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  auto cost = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
-    return (mt_large * n1 + 255) / 256 * 10 + (mt_small * (tiles_n - n1) + 255) / 256 * 7;
-  };
-  int64_t n1 = cost(tiles_n) <= cost(0) ? tiles_n : 0;
-  if constexpr (kOut == kOutBf16) {
-    for (int64_t c = 1; c < tiles_n; ++c)
-      if (cost(c) < cost(n1)) n1 = c;
-  }
+  const int64_t n1 = dense_large_panels(M, N, kOut == kOutBf16);
   if (n1 == tiles_n) {
     p.slots_m = mt_large;
     return launch<CfgLarge, V>(p, stream);

@@ -452,6 +452,36 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s,
 int64_t fp8_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int64_t S);
 
 /*
+ * MoE dispatch order on the device (the recipe's mixture-of-experts models:
+ * page 1, "Leistungsgewinne in der Praxis" (Qwen3-30B) and "Warum dies fuer
+ * die KI-Oekonomie wichtig ist" (Moonlight 16B)): from the routing table to
+ * the group offsets and row map that fp8_grouped_gemm and
+ * fp8_grouped_gemm_gather take, with no host synchronisation.
+ *   expert_ids [T][k] int32 (in): expert of slot j of token t, entry t*k + j
+ *   E          routed experts, 1 <= E <= 1024; n_shared >= 0 shared experts
+ *   group_offsets [E+n_shared+1] int32 (out): first row of each group
+ *   row_index  [T*(k+n_shared)] int32 (out): the token of every row
+ *   entry_row  [T*k] int32 (out, may be NULL): the row of every entry
+ *   workspace, workspace_bytes: DEVICE memory of at least
+ *              fp8_moe_permute_workspace_size(T, k, E) bytes; its contents
+ *              need no initialisation; concurrent calls need their own.
+ * Rows: the entries sorted by expert, stable in entry order (so inside an
+ * expert by token, then slot), group e = rows [offsets[e], offsets[e+1]);
+ * then each shared expert as a group of all T tokens in order.  An id outside
+ * [0, E) puts its entry in no group (entry_row -1); those entries leave the
+ * last rows of row_index, after offsets[E+n_shared], holding -1.  With valid
+ * ids offsets[E+n_shared] = T*(k+n_shared).  The result is deterministic and
+ * equals the stable sort exactly.  T*(k+n_shared) < 2^31.
+ */
+fp8q_status fp8_moe_permute(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                            int32_t *group_offsets, int32_t *row_index, int32_t *entry_row,
+                            void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fp8_moe_permute needs (a function of the sizes only; 0
+ * for invalid sizes). */
+int64_t fp8_moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
+
+/*
  * For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): fp8_attention_decode
  * without the workspace argument.  Same arguments otherwise, same results bit
@@ -472,6 +502,13 @@ fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s,
                                          const int32_t *seq_len, uint16_t *out,
                                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
                                          void *stream);
+
+/* Informational: how many 256-row weight panels of an M x N dense GEMM
+ * output (fp8_blockscaled_gemm and its variants; bf16_output != 0 for the
+ * bf16-output GEMMs, 0 for those that quantize their output) run on
+ * 256-token x 256 tiles; the other ceil(N/256) - that many run on 128-token
+ * tiles.  -1 for invalid sizes.  No device access. */
+int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int bf16_output);
 
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);

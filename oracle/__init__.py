@@ -35,4 +35,5 @@ from .oracle import (  # noqa: F401
     rmsnorm_quant_1x128,
     moe_permute,
     num_threads,
+    set_num_threads,
 )

@@ -336,3 +336,17 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* Threads for the following parallel regions of this library (the CPU
+ * baseline's single-thread run); n < 1 restores the default. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0)
+        dflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : dflt);
+#else
+    (void)n;
+#endif
+}

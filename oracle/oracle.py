@@ -59,6 +59,8 @@ def _load():
     lib.oracle_grouped_gemm_f64.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
     lib.oracle_grouped_gemm_sampled_f64.argtypes = [p, p, p, p, i64, i64, p, p, p, i64, p]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -76,6 +78,11 @@ def _c(a, dtype):
 
 def num_threads():
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the following oracle calls (n < 1: the OpenMP default)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def e4m3_decode_table():

@@ -260,6 +260,35 @@ def test_noalloc_scratch_covers_every_split():
     assert worst == cap == 8 * 1022 * 130 * 4
 
 
+def test_gemm_tile_plan(lib):
+    """Weight panels on 256-token tiles: all of them for gate+up and down at 4096
+    tokens, 16 of QKV's 24 (one round on each shape), none for O at 2048
+    tokens; a quantized output is not split."""
+    f = lib.fp8_blockscaled_gemm_tile_plan
+    assert f(4096, 28672, 1) == 112 and f(4096, 4096, 1) == 16
+    assert f(4096, 6144, 1) == 16 and f(4096, 6144, 0) in (0, 24)
+    assert f(2048, 4096, 1) == 0
+    assert f(0, 128, 1) == -1 and f(64, 100, 1) == -1
+
+
+def test_moe_permute_argument_errors(lib):
+    f = lib.fp8_moe_permute
+    ws = lib.fp8_moe_permute_workspace_size(100, 8, 128)
+    assert ws == (100 * 8 * 4 + 255) // 256 * 256 + 128 * 4     # ranks, then 128 experts x 1 block of counts
+    assert lib.fp8_moe_permute_workspace_size(100, 8, 2048) == 0     # too many experts
+    assert lib.fp8_moe_permute_workspace_size(-1, 8, 128) == 0
+    #        ids   T    k  E    ns off   rows  entry ws    bytes
+    assert f(GOOD, -1, 8, 128, 0, GOOD, GOOD, None, GOOD, ws, None) == 1           # negative T
+    assert f(GOOD, 100, 0, 128, 0, GOOD, GOOD, None, GOOD, ws, None) == 1          # k = 0
+    assert f(GOOD, 100, 8, 0, 0, GOOD, GOOD, None, GOOD, ws, None) == 2            # E = 0
+    assert f(GOOD, 100, 8, 1025, 0, GOOD, GOOD, None, GOOD, ws, None) == 2         # E > 1024
+    assert f(GOOD, 1 << 28, 8, 128, 0, GOOD, GOOD, None, GOOD, ws, None) == 2      # rows >= 2^31
+    assert f(GOOD, 100, 8, 128, 0, None, GOOD, None, GOOD, ws, None) == 1          # null offsets
+    assert f(GOOD, 100, 8, 128, 0, GOOD, GOOD, ODD, GOOD, ws, None) == 3           # misaligned entry_row
+    assert f(GOOD, 100, 8, 128, 0, GOOD, GOOD, None, GOOD, ws - 4, None) == 1      # workspace too small
+    assert "workspace" in _err(lib)
+
+
 def test_gather_argument_errors(lib):
     f = lib.fp8_grouped_gemm_gather
     #      a_q   a_s   T    b_q   b_s   off   idx   G  M   N    K    y     mode
