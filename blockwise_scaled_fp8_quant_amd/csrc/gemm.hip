@@ -77,8 +77,11 @@ struct Variant {
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
 
-template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_, int kWAhead_ = 1, int kWavesN_ = 2>
+template <int kBM_, int kWaves_, int kStages_, int kLoaders_, int kDmaStep_, int kWAhead_ = 1, int kWavesN_ = 2,
+          bool kPingPong_ = false>
 struct TileCfg {
+  // The ping-pong main loop (gemm_main_pp) instead of the lockstep one.
+  static constexpr bool kPingPong = kPingPong_;
   static constexpr int kBM = kBM_;
   static constexpr int kWaves = kWaves_;
   static constexpr int kStages = kStages_;
@@ -122,12 +125,24 @@ struct TileCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-using CfgLarge = TileCfg<256, 8, 2, 8, 4>;
+// 256 x 256 tiles: on the ping-pong schedule (gemm_main_pp) when the
+// matrix cores apply power-of-two scales, on the lockstep one when the VALU
+// folds the scales in.  A VALU read of a register an MFMA wrote stalls the
+// wave (measured on gfx950: an MFMA stream with a 4-FMA fold of an earlier
+// product per MFMA reaches ~3.3 PFLOP/s against ~4.2 without, whatever the
+// distance to the MFMA that wrote it; independent FMAs cost ~5%).  In
+// lockstep the other wave of the SIMD keeps the matrix core busy through
+// such a stall; in ping-pong it is reading LDS, so the folds cost 10% more
+// (Llama gate+up and down).  Without folds the ping-pong loop is 3-6% ahead.
+using CfgLarge = TileCfg<256, 8, 2, 8, 0, 1, 2, true>;
+using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 4>;
 using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
 // 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD) for
 // bf16 outputs without per-row weight scales, whose epilogues do not need a
 // wave to hold 128 weight rows.
 using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
+template <class V>
+using LargeCfg = typename std::conditional<V::kPow2 && !V::kBRow, CfgLarge, CfgLargeLockstep>::type;
 template <class V>
 using SmallCfg = typename std::conditional<V::kOut == kOutBf16 && !V::kBRow && !V::kSwiGLU, CfgSmall8, CfgSmall>::type;
 
@@ -762,67 +777,293 @@ struct TileOut {
   float *ys;     // E4M3: tile origin of the scales [M][N/128]
 };
 
-// One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
-// n_valid), written at the tile origins in o (row stride N).
+// ---------------------------------------------------------------------------
+// Ping-pong main loop of the 256 x 256 tile (8 waves, two stage buffers).
+//
+// The eight waves form two groups, waves 0-3 and waves 4-7; a CU places wave
+// w and wave w+4 on the same SIMD (checked on the hardware), so every SIMD
+// holds one wave of each group.  A K block is cut into two halves along the
+// wave's weight rows (sub-tile rows 0-3 and 4-7), and the work runs in
+// phases separated by workgroup barriers.  In each phase one group computes
+// a half (16 MFMAs and their scale folds, operands already in registers)
+// while the other reads the fragments of its next half from LDS and issues
+// its share of the DMA.  So the matrix core of every SIMD always has one
+// wave feeding it, and the LDS reads and DMA of a block spread over the
+// whole block instead of meeting at its start.
+//
+//   phase 4k-1: group 0 reads (k,0) and issues the weight tile of k+1
+//   phase 4k  : group 0 computes (k,0); group 1 reads (k,0) and issues the
+//               token tile of k+1
+//   phase 4k+1: group 0 reads (k,1);    group 1 computes (k,0)
+//   phase 4k+2: group 0 computes (k,1); group 1 reads (k,1); both wait for
+//               their DMA of block k+1 before the barrier
+//   phase 4k+3: group 0 reads (k+1,0);  group 1 computes (k,1)
+//
+// Block k's stage buffer is read in phases 4k-1 .. 4k+2; block k+2 goes into
+// it from phase 4k+3 on (the barrier ending 4k+2 orders every read before
+// that DMA) and is first read in phase 4k+7, so its DMA has a whole K block
+// of time.  The last two scale folds of a compute phase are left to the
+// wave's next (read) phase, when its VALU is otherwise idle.
+// ---------------------------------------------------------------------------
+constexpr int kPPPieces = 8;  // 1 KB DMA pieces per wave and operand tile
+
+// Per-lane DMA offsets.  Group 0 loads the weight tile (wave l: pieces
+// 8l .. 8l+7) and the two weight-block scales; group 1 the token tile and 64
+// activation scales per wave.
+struct PPLane {
+  uint32_t rc[2];               // (row in piece)*K + chunk offset, even / odd pieces
+  uint32_t s;                   // scale offset
+  uint32_t ga[kPPPieces];       // gathered token rows: byte offset of this lane's row per piece
+};
+
+template <class V>
+__device__ __forceinline__ PPLane pp_lane(const TileJob &t, int grp, int l, int lane) {
+  PPLane d;
+  const uint32_t row = (uint32_t)(lane >> 3);
+  const uint32_t c0 = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t K = (uint32_t)t.K;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) d.rc[par] = row * K + ((c0 ^ par) << 4);
+  if (grp == 0) {
+    d.s = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
+  } else {
+    const int srow = sa_row_of_pos(l * 64 + lane);
+    d.s = (uint32_t)srow * (uint32_t)t.KB * 4u;
+    if constexpr (V::kGather) {
+      auto src = [&](int r) -> int64_t {  // source token row of tile row r, or -1
+        if (r >= t.m_valid) return -1;
+        const int64_t s = t.gidx[r];
+        return (s >= 0 && s < t.T) ? s : -1;
+      };
+#pragma unroll
+      for (int i = 0; i < kPPPieces; ++i) {
+        const int piece = l * kPPPieces + i;
+        const int64_t s = src(8 * piece + (int)row);
+        d.ga[i] = s < 0 ? kGatherOOB : (uint32_t)s * K + ((c0 ^ (uint32_t)(piece & 1)) << 4);
+      }
+      const int64_t s = src(srow);
+      d.s = s < 0 ? kGatherOOB : (uint32_t)s * (uint32_t)t.KB * 4u;
+    }
+  }
+  return d;
+}
+
+// Resource over the 64 rows (8 pieces) a wave loads of an operand tile: based
+// at row 64l and byte kbyte of the row, bounded to the valid rows among them
+// (0..64).  A lane's offset inside it, (8q + row) * K + chunk, is below the
+// bound exactly when its row is valid, so rows past the tile's last valid
+// one read zeros and no access leaves the tensor.  Wave-uniform, so it lives
+// in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const uint8_t *rows, int valid_rows, int64_t K, int l,
+                                                             uint32_t kbyte) {
+  int nr = valid_rows - 64 * l;
+  nr = nr < 0 ? 0 : (nr > 64 ? 64 : nr);
+  const uint64_t base = (uint64_t)(uintptr_t)(rows + (int64_t)(64 * l) * K + kbyte);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(nr * (int)K);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcWord3);
+}
+
+// Pieces [kQ0, kQ1) of this wave's share of block k's DMA into stage buffer
+// buf, and (kScales) its scale load.
+template <class C, class V, int kQ0, int kQ1, bool kScales>
+__device__ __forceinline__ void pp_issue(const TileJob &t, const TileRsrc &rs, const PPLane &d, int k, uint8_t *buf,
+                                         int grp, int l, int lane) {
+  const uint32_t kbyte = (uint32_t)k * kBK;
+  const uint32_t K8 = (uint32_t)t.K * 8u;
+  if (grp == 0) {
+    const __amdgpu_buffer_rsrc_t r = wave_rsrc(t.b_q, t.n_valid, t.K, l, kbyte);
+#pragma unroll
+    for (int q = kQ0; q < kQ1; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(buf + (l * kPPPieces + q) * 1024), 16,
+                                               d.rc[q & 1] + (uint32_t)q * K8, 0, 0, 0);
+    if (kScales && l == 0 && lane < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.s + (uint32_t)k * 4u,
+                                               0, 0, 0);
+  } else {
+    if constexpr (V::kGather) {
+      const __amdgpu_buffer_rsrc_t r = gather_rsrc(t.a_q, t.T, t.K, kbyte);
+#pragma unroll
+      for (int q = kQ0; q < kQ1; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(buf + C::kOffA + (l * kPPPieces + q) * 1024), 16,
+                                                 d.ga[q], 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = wave_rsrc(t.a_q, t.m_valid, t.K, l, kbyte);
+#pragma unroll
+      for (int q = kQ0; q < kQ1; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(buf + C::kOffA + (l * kPPPieces + q) * 1024), 16,
+                                                 d.rc[q & 1] + (uint32_t)q * K8, 0, 0, 0);
+    }
+    if (kScales)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
+                                               d.s + (uint32_t)k * 4u, 0, 0, 0);
+  }
+}
+
+// The 16 MFMAs of half kH of a K block (weight sub-tile rows 4kH .. 4kH+3,
+// all four token sub-tiles), j = 4*(ni - 4kH) + mi.  amax scales: after
+// MFMA j the fold of MFMA j-2; the folds of j = 14 and 15 are left to
+// pp_fold_tail.  Power-of-two scales: the MFMA applies them and accumulates.
+template <class V, int kH>
+__device__ __forceinline__ void pp_compute(const v8i (&wf)[4], const v8i (&xf)[kSubM], const float (&scl)[kSubM],
+                                           uint32_t ea, uint32_t eb, v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing]) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int ni = j / kSubM, mi = j % kSubM;
+    if constexpr (V::kPow2) {
+      acc[4 * kH + ni][mi] = mfma_pow2(wf[ni], xf[mi], acc[4 * kH + ni][mi], eb, ea, mi);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    } else {
+      // MFMA j, then the fold of MFMA j-2, step by step.  Left to itself the
+      // compiler clumps the MFMAs and leaves the folds to the end of the
+      // phase (or pairs each MFMA with the fold of its own result, which
+      // stalls the wave until the MFMA completes).  Two empty asm statements
+      // fix the order: MFMA j takes its zero accumulator through one, so it
+      // cannot rise above step j-1, and the fold's result passes through the
+      // other, so it cannot sink below step j+1.  Two MFMAs after its MFMA a
+      // fold's product is ready, and its four FMAs run while MFMA j does.
+      v4f z = zero;
+      asm volatile("" : "+v"(z));
+      p[j % kRing] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], xf[mi], z, 0, 0, 0, 127, 0, 127);
+      if (j >= 2) {
+        const int jj = j - 2;
+        v4f &a = acc[4 * kH + jj / kSubM][jj % kSubM];
+        fold1(a, p[jj % kRing], scl[jj % kSubM]);
+        asm volatile("" : "+v"(a));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The two folds a compute phase of half kH left (MFMAs 14 and 15).
+template <int kH>
+__device__ __forceinline__ void pp_fold_tail(v4f (&acc)[kSubN][kSubM], const v4f (&p)[kRing],
+                                             const float (&scl)[kSubM]) {
+  fold1(acc[4 * kH + 3][2], p[14 % kRing], scl[2]);
+  fold1(acc[4 * kH + 3][3], p[15 % kRing], scl[3]);
+}
+
+// Weight fragments of half kH: sub-tile rows 4kH .. 4kH+3 of this wave's 128.
+__device__ __forceinline__ void pp_read_w(const uint8_t *buf, int wn, int h, int lane, v8i (&wf)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wf[i] = frag(buf, wn * 128 + (4 * h + i) * 16, lane);
+}
+
+// Everything of a phase stays in its phase: the barrier is a fence for the
+// scheduler, and the accumulators and partial products are pinned on both
+// sides of it (register-only work could otherwise move across).
+__device__ __forceinline__ void pp_barrier(v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing]) {
+#pragma unroll
+  for (int ni = 0; ni < kSubN; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) pin(acc[ni][mi]);
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) pin(p[r]);
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_nofence();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <class C, class V>
-__device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds) {
+__device__ __forceinline__ void gemm_main_pp(const TileJob &t, uint8_t *lds, int wave, int lane, int wn, int wm,
+                                             v4f (&acc)[kSubN][kSubM], uint32_t &bad) {
+  static_assert(C::kBM == 256 && C::kWaves == 8 && C::kWavesN == 2 && C::kStages == 2, "ping-pong tile shape");
+  static_assert(!V::kBRow, "per-row weight-side scales: lockstep loop");
+  constexpr bool kPow2 = V::kPow2;
+  const int grp = wave >> 2, l = wave & 3;
+  const int KB = t.KB;
+  const TileRsrc rs = make_rsrc<V>(t);
+  const PPLane d = pp_lane<V>(t, grp, l, lane);
+  v8i xf[kSubM], wf[4];
+  float scl[kSubM] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t ea = 0, eb = 0;
+  v4f p[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) p[r] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Block k+1's DMA goes out in three parts (pieces 0-2 with the scales, 3-5,
+  // 6-7), spread over the phases between the end of the last read of its
+  // stage buffer (block k-1's, phase 4k-2) and the wait before its first read
+  // (end of phase 4k+2): group 0 in its phases 4k-1 .. 4k+1, group 1 in
+  // 4k-1 .. 4k+1 as well (its part 0 in the previous iteration's last
+  // segment).  So no phase carries more than a quarter of a block's DMA.
+  auto part = [&](int which, int kk) {
+    uint8_t *b = lds + (kk & 1) * C::kStageBytes;
+    if (which == 0) pp_issue<C, V, 0, 3, true>(t, rs, d, kk, b, grp, l, lane);
+    else if (which == 1) pp_issue<C, V, 3, 6, false>(t, rs, d, kk, b, grp, l, lane);
+    else pp_issue<C, V, 6, kPPPieces, false>(t, rs, d, kk, b, grp, l, lane);
+  };
+  part(0, 0);
+  part(1, 0);
+  part(2, 0);
+  wait_vmcnt<0>();
+  pp_barrier(acc, p);
+  if (grp == 1) {
+    if (1 < KB) part(0, 1);
+    pp_barrier(acc, p);  // phase -1: group 0 reads the first half of block 0
+  }
+  for (int k = 0; k < KB; ++k) {
+    const uint8_t *buf = lds + (k & 1) * C::kStageBytes;
+    const bool more = k + 1 < KB;
+    // read (k, 0): token fragments, weight rows 0-3, scale words
+    HeadRaw h;
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) wf[mi] = frag(buf, wn * 128 + mi * 16, lane);
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
+    h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
+    h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + wn * 4);
+    if (more) part(grp == 0 ? 0 : 1, k + 1);
+    if constexpr (!kPow2)
+      if (k > 0) pp_fold_tail<1>(acc, p, scl);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (kPow2) {
+      BlockFrags g;
+      g.bad = bad;
+      finish_head<V>(h, g);
+      ea = g.ea;
+      eb = g.eb;
+      bad = g.bad;
+    } else {
+      scl[0] = h.sa4.x * h.sb;
+      scl[1] = h.sa4.y * h.sb;
+      scl[2] = h.sa4.z * h.sb;
+      scl[3] = h.sa4.w * h.sb;
+    }
+    pp_barrier(acc, p);
+    if (more) part(grp == 0 ? 1 : 2, k + 1);
+    pp_compute<V, 0>(wf, xf, scl, ea, eb, acc, p);
+    pp_barrier(acc, p);
+    // read (k, 1): weight rows 4-7
+    pp_read_w(buf, wn, 1, lane, wf);
+    if (more && grp == 0) part(2, k + 1);
+    if constexpr (!kPow2) pp_fold_tail<0>(acc, p, scl);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (grp == 1) wait_vmcnt<0>();
+    pp_barrier(acc, p);
+    if (grp == 1 && k + 2 < KB) part(0, k + 2);
+    pp_compute<V, 1>(wf, xf, scl, ea, eb, acc, p);
+    if (grp == 0) wait_vmcnt<0>();
+    pp_barrier(acc, p);
+  }
+  if constexpr (!kPow2) pp_fold_tail<1>(acc, p, scl);
+  if (grp == 0) pp_barrier(acc, p);  // the last phase: group 1 computes block KB-1's second half
+}
+
+
+// After the main loop: the power-of-two NaN rule, zero rows of invalid
+// gathered indices, then the epilogue of the variant (bf16, quantized or
+// SwiGLU output).  bad: the pow2 scale-check bits of this lane.
+template <class C, class V>
+__device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds,
+                                            v4f (&acc)[kSubN][kSubM], uint32_t bad, int wave, int wn, int wm,
+                                            int lane) {
   constexpr bool kPow2 = V::kPow2;
   constexpr int kOut = V::kOut;
   constexpr bool kGather = V::kGather;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
-  const int wn = wave & (C::kWavesN - 1), wm = wave / C::kWavesN;
-  const int KB = t.KB;
-
-  v4f acc[kSubN][kSubM];  // rows ni >= C::kSubN unused
-#pragma unroll
-  for (int ni = 0; ni < C::kSubN; ++ni)
-#pragma unroll
-    for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-  const TileRsrc rs = make_rsrc<V>(t);
-  const DmaLane dl = dma_lane<C, V>(t, wave, lane);
-
-  // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
-#pragma unroll
-  for (int s = 0; s < C::kStages - 1; ++s)
-    if (s < KB && wave >= C::kFirstLoader)
-      issue_stage<C, V>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
-
-  wait_block<C, V>(0, KB, wave);
-  BlockFrags f;
-  f.bad = 0;
-  load_block<C, V>(lds, wave, wn, wm, lane, f);
-
-  v4f p[kRing];
-  float4 sbq[2];  // per-row weight-side scales of two sub-tile rows (kBRow)
-  int cur = 0;  // stage buffer of block k
-  StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
-               C::kStages - 1 < KB};
-  v8i wlast;
-  for (int k = 0; k + 1 < KB; ++k) {
-    mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
-    // Block k's buffer is free once every wave is past the barrier in
-    // block_boundary; block k + kStages goes into it during the next block.
-    dma.k = k + C::kStages;
-    dma.buf = lds + cur * C::kStageBytes;
-    dma.on = k + C::kStages < KB;
-    cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-    block_boundary<C, V>(lds + cur * C::kStageBytes, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
-  }
-  // the last block: its last row's MFMAs and the trailing folds, no barrier
-  mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
-#pragma unroll
-  for (int mi = 0; mi < kSubM; ++mi) {
-    const int j = C::kMfma - kSubM + mi;
-    mma_one<V>(C::kSubN - 1, mi, j, wlast, f, acc, p);
-    if constexpr (!kPow2) fold_one<V>(j - 2, f.scl, acc, p, sbq);
-  }
-  if constexpr (!kPow2) {
-    fold_one<V>(C::kMfma - 2, f.scl, acc, p, sbq);
-    fold_one<V>(C::kMfma - 1, f.scl, acc, p, sbq);
-  }
-  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   // A scale outside the power-of-two contract turns the outputs that depend
   // on it into NaN rather than into a silently wrong product.
   if constexpr (kPow2 && V::kBRow) {
@@ -832,7 +1073,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int ni = 0; ni < kSubN; ++ni) {
-      const uint64_t rb = __ballot((f.bad >> (16 + ni)) & 1u);
+      const uint64_t rb = __ballot((bad >> (16 + ni)) & 1u);
       if (rb != 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -843,14 +1084,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
     }
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi)
-      if (f.bad & (1u << mi))
+      if (bad & (1u << mi))
 #pragma unroll
         for (int ni = 0; ni < C::kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
-  } else if (kPow2 && f.bad) {
+  } else if (kPow2 && bad) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int mi = 0; mi < kSubM; ++mi)
-      if (f.bad & ((1u << mi) | 16u))
+      if (bad & ((1u << mi) | 16u))
 #pragma unroll
         for (int ni = 0; ni < C::kSubN; ++ni) acc[ni][mi] = (v4f){nan, nan, nan, nan};
   }
@@ -1017,6 +1258,74 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
       }
     }
   }
+}
+
+// One output tile: token rows t.a_q[0 .. m_valid), weight rows t.b_q[0 ..
+// n_valid), written at the tile origins in o (row stride N).
+template <class C, class V>
+__device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds) {
+  constexpr bool kPow2 = V::kPow2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
+  const int wn = wave & (C::kWavesN - 1), wm = wave / C::kWavesN;
+  const int KB = t.KB;
+
+  v4f acc[kSubN][kSubM];  // rows ni >= C::kSubN unused
+#pragma unroll
+  for (int ni = 0; ni < C::kSubN; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < kSubM; ++mi) acc[ni][mi] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  if constexpr (C::kPingPong) {
+    uint32_t bad = 0;
+    gemm_main_pp<C, V>(t, lds, wave, lane, wn, wm, acc, bad);
+    tile_finish<C, V>(t, o, N, lds, acc, bad, wave, wn, wm, lane);
+    return;
+  }
+  const TileRsrc rs = make_rsrc<V>(t);
+  const DmaLane dl = dma_lane<C, V>(t, wave, lane);
+
+  // Blocks 0 .. kStages-2 in flight; block kk lives in stage buffer kk % kStages.
+#pragma unroll
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < KB && wave >= C::kFirstLoader)
+      issue_stage<C, V>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
+
+  wait_block<C, V>(0, KB, wave);
+  BlockFrags f;
+  f.bad = 0;
+  load_block<C, V>(lds, wave, wn, wm, lane, f);
+
+  v4f p[kRing];
+  float4 sbq[2];  // per-row weight-side scales of two sub-tile rows (kBRow)
+  int cur = 0;  // stage buffer of block k
+  StageDma dma{&t, &rs, &dl, C::kStages - 1, lds + (C::kStages - 1) * C::kStageBytes, wave, lane,
+               C::kStages - 1 < KB};
+  v8i wlast;
+  for (int k = 0; k + 1 < KB; ++k) {
+    mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+    // Block k's buffer is free once every wave is past the barrier in
+    // block_boundary; block k + kStages goes into it during the next block.
+    dma.k = k + C::kStages;
+    dma.buf = lds + cur * C::kStageBytes;
+    dma.on = k + C::kStages < KB;
+    cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
+    block_boundary<C, V>(lds + cur * C::kStageBytes, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
+  }
+  // the last block: its last row's MFMAs and the trailing folds, no barrier
+  mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) {
+    const int j = C::kMfma - kSubM + mi;
+    mma_one<V>(C::kSubN - 1, mi, j, wlast, f, acc, p);
+    if constexpr (!kPow2) fold_one<V>(j - 2, f.scl, acc, p, sbq);
+  }
+  if constexpr (!kPow2) {
+    fold_one<V>(C::kMfma - 2, f.scl, acc, p, sbq);
+    fold_one<V>(C::kMfma - 1, f.scl, acc, p, sbq);
+  }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
+  tile_finish<C, V>(t, o, N, lds, acc, f.bad, wave, wn, wm, lane);
 }
 
 // Workgroup id -> logical tile id such that XCD x (which receives ids
@@ -1220,7 +1529,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   const int64_t n1 = dense_large_panels(M, N, kOut == kOutBf16);
   if (n1 == tiles_n) {
     p.slots_m = mt_large;
-    return launch<CfgLarge, V>(p, stream);
+    return launch<LargeCfg<V>, V>(p, stream);
   }
   if (n1 > 0) {
     // panels [0, n1) on 256-row tiles, then the rest on 128-row tiles
@@ -1229,7 +1538,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
     q.N = n_off;
     q.tiles_n = (int32_t)n1;
     q.slots_m = mt_large;
-    hipError_t e = launch<CfgLarge, V>(q, stream);
+    hipError_t e = launch<LargeCfg<V>, V>(q, stream);
     if (e != hipSuccess) return e;
     p.b_q = b_q + n_off * K;
     p.b_s = b_s + (kBRow ? n_off : n_off / 128) * (K / kBK);
@@ -1253,7 +1562,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
     p.slots_m = M_total / CfgLarge::kBM + G;
-    return launch<CfgLarge, V>(p, stream);
+    return launch<LargeCfg<V>, V>(p, stream);
   }
   p.slots_m = M_total / CfgSmall::kBM + G;
   return launch<SmallCfg<V>, V>(p, stream);
