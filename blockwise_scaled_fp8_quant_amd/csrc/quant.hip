@@ -20,10 +20,13 @@ namespace fp8q {
 // sequence of M*K/128 blocks, and block b's scale is scales[b].  Eight lanes
 // own one block (256 bytes of bf16): lane j of the group reads chunks j and
 // j+8 (16 bytes each), so one load instruction of the group covers one full
-// 128-byte line.  A workgroup of 256 lanes handles 32 blocks per unroll step.
+// 128-byte line.  One wave per workgroup, one block per lane group: many
+// small workgroups ramp up and drain faster than fewer large ones (measured
+// on 4096 x 4096 bf16: 10.1 us against 10.9 us for 256 lanes with two blocks
+// per group, the same as a plain copy with this access pattern).
 // ---------------------------------------------------------------------------
-constexpr int kActThreads = 256;
-constexpr int kActUnroll = 2;
+constexpr int kActThreads = 64;
+constexpr int kActUnroll = 1;
 constexpr int kActBlocksPerStep = kActThreads / 8;
 
 template <int kMode>
@@ -505,12 +508,16 @@ hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q
 // 16 lanes of each DPP row hold one 1x128 block (block 4 i + l / 16).  Every
 // load is unconditional (addresses clamped into the tensors, values past the
 // row masked) and all of them are issued before any math, so each wait counts
-// only the loads it needs.  The block |max| is taken over the fp32 values
-// before their bf16 rounding and rounded once: the rounding is monotonic, so
-// this is the |max| of the rounded values.  With one row per wave the chip
-// keeps 16 rows per CU in flight; giving a wave several rows, with the next
-// row's loads overlapping the current row's math, measured slower (fewer
-// waves to hide the per-element VALU work).
+// only the loads it needs.  The 16 lanes of a block all hold its |max|; each
+// derives the parameters (scale, reciprocal) of one of its kChunks blocks
+// and passes them to the others through DPP row_share.  The block |max| is
+// taken over the fp32 values before their bf16 rounding and rounded once:
+// the rounding is monotonic, so this is the |max| of the rounded values.
+// With one row per wave the chip keeps 16 rows per CU in flight; giving a
+// wave several rows, with the next row's loads overlapping the current row's
+// math, measured slower, and so did two to eight waves per row.  The kernel
+// is bound by its VALU work (about 12 instructions per element, ~5.5 us at
+// 4096 x 4096) run after the row's data has arrived.
 // ---------------------------------------------------------------------------
 constexpr int kNormThreads = 256;
 constexpr int kNormMaxK = 8192;
@@ -529,23 +536,53 @@ __device__ __forceinline__ float dot2_sq(uint32_t a, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, c, false);
 }
 
+// Lane i of each 16-lane DPP row -> every lane of that row.
+template <int i>
+__device__ __forceinline__ uint32_t row_share(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + i, 0xF, 0xF, false);
+}
+
+// Parameters of the kChunks blocks a lane touches (block i: chunk i of its
+// DPP row; every lane of the row holds the same amax[i]).  Lane j of the row
+// derives those of block j % kChunks once, and row_share hands them out: one
+// division pair per lane instead of one per chunk (measured 8% of the fused
+// norm's time at K = 4096).
+template <int kMode, int kChunks, int i = 0>
+__device__ __forceinline__ void share_params(const BlockQ &mine, const float (&amax)[kChunks],
+                                             BlockQ (&p)[kChunks]) {
+  if constexpr (i < kChunks) {
+    p[i].s = __uint_as_float(row_share<i>(__float_as_uint(mine.s)));
+    if constexpr (kMode == kModeAmax) {
+      p[i].y = __uint_as_float(row_share<i>(__float_as_uint(mine.y)));
+      p[i].e = 0;
+      p[i].slow = amax[i] < 0x1p-100f;  // as block_params decides it
+    } else {
+      p[i].y = 0.0f;
+      p[i].e = (int)row_share<i>((uint32_t)mine.e);
+      p[i].slow = false;
+    }
+    share_params<kMode, kChunks, i + 1>(mine, amax, p);
+  }
+}
+
 template <int kMode, int kChunks>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma, int64_t M, int K, float eps,
     uint8_t *__restrict__ q, float *__restrict__ scales) {
+  static_assert(kChunks >= 1 && kChunks <= 16 && (kChunks & (kChunks - 1)) == 0, "chunks per lane");
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
   const uint16_t *xr = x + (row < M ? row : M - 1) * K;
   uint4 gam[kChunks], w[kChunks];
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
+  for (int i = 0; i < kChunks; ++i) {  // the row first: its data decides when the math can start
     const int col = 512 * i + 8 * lane;
-    gam[i] = *reinterpret_cast<const uint4 *>(gamma + (col < K ? col : K - 8));
+    w[i] = load_stream16(xr + (col < K ? col : K - 8));
   }
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
     const int col = 512 * i + 8 * lane;
-    w[i] = load_stream16(xr + (col < K ? col : K - 8));
+    gam[i] = *reinterpret_cast<const uint4 *>(gamma + (col < K ? col : K - 8));
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
 
@@ -564,10 +601,10 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   const float r = 1.0f / __builtin_sqrtf(ss * (1.0f / (float)K) + eps);
 
-  const int nb = K >> 7;
+  float f[kChunks][8];
+  float amax[kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    const int col = 512 * i + 8 * lane;
     const uint32_t xw[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
     const uint32_t gw[4] = {gam[i].x, gam[i].y, gam[i].z, gam[i].w};
     float yf[8];
@@ -578,18 +615,32 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
       yf[2 * k + 1] = (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]);
       m = max3_abs(m, yf[2 * k], yf[2 * k + 1]);
     }
-    float f[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t b = to_bf16x2(yf[2 * k], yf[2 * k + 1]);
-      f[2 * k] = bf16_lo(b);
-      f[2 * k + 1] = bf16_hi(b);
+      f[i][2 * k] = bf16_lo(b);
+      f[i][2 * k + 1] = bf16_hi(b);
     }
-    const float amax = bf16_lo(to_bf16x2(group16_max(m), 0.0f));
-    const BlockQ p = block_params<kMode>(amax);
-    const uint2 o = quant8<kMode>(p, f);
+    amax[i] = bf16_lo(to_bf16x2(group16_max(m), 0.0f));
+  }
+  BlockQ p[kChunks];
+  if constexpr (kChunks == 1) {
+    p[0] = block_params<kMode>(amax[0]);
+  } else {
+    const int j = lane & (kChunks - 1);
+    float a = amax[0];
+#pragma unroll
+    for (int i = 1; i < kChunks; ++i) a = j == i ? amax[i] : a;
+    share_params<kMode, kChunks>(block_params<kMode>(a), amax, p);
+  }
+
+  const int nb = K >> 7;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    const uint2 o = quant8<kMode>(p[i], f[i]);
     if (col < K && row < M) {  // (col < K is uniform over each 16-lane block)
-      if ((lane & 15) == 0) scales[row * nb + (col >> 7)] = p.s;
+      if ((lane & 15) == 0) scales[row * nb + (col >> 7)] = p[i].s;
       *reinterpret_cast<uint2 *>(q + row * K + col) = o;
     }
   }
