@@ -560,11 +560,12 @@ def fp8_moe_permute(expert_ids, E, n_shared=0, out=None, workspace=None):
     return off, row_index, entry_row
 
 
-def fp8_blockscaled_gemm_tile_plan(M, N, bf16_output=True):
+def fp8_blockscaled_gemm_tile_plan(M, N, swiglu=False):
     """(panels on 256-token tiles, panels on 128-token tiles) of a dense
     M x N GEMM: how the library splits its output's 256-row weight panels
-    between its two tile shapes."""
-    n1 = _lib.load().fp8_blockscaled_gemm_tile_plan(M, N, 1 if bf16_output else 0)
+    between its two tile shapes (swiglu: for fp8_blockscaled_gemm_swiglu_quant,
+    else for the other dense GEMMs)."""
+    n1 = _lib.load().fp8_blockscaled_gemm_tile_plan(M, N, 1 if swiglu else 0)
     if n1 < 0:
         raise ValueError("invalid GEMM size")
     return n1, -(-N // 256) - n1

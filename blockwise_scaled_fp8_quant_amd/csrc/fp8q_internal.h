@@ -42,7 +42,7 @@ hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
 // Weight panels (256 rows each) of a dense M x N GEMM output that run on
 // 256-row tiles; the others run on 128-row tiles (bf16_out: a bf16 output,
 // which may be split between the two shapes).
-int64_t dense_large_panels(int64_t M, int64_t N, bool bf16_out);
+int64_t dense_large_panels(int64_t M, int64_t N, bool may_split);
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const uint8_t *b_q, const float *b_s,

@@ -1466,9 +1466,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   } else if constexpr (V::kSwiGLU) {  // h [M][N/2]: this tile's 128 columns start at n0/2
     o.yq = p.yq + m0 * (p.N >> 1) + (n0 >> 1);
     o.ys = p.ys + m0 * (p.N >> 8) + (n0 >> 8);
-  } else {
-    o.yq = p.yq + m0 * p.N + n0;
-    o.ys = p.ys + m0 * (p.N >> 7) + (n0 >> 7);
+  } else {  // a quantized output may be a column slice of a wider one (row stride ldy)
+    o.yq = p.yq + m0 * p.ldy + n0;
+    o.ys = p.ys + m0 * (p.ldy >> 7) + (n0 >> 7);
   }
   if constexpr (kGrouped && C::kBM == 256 && kOut == kOutBf16 && V::kPow2 && !V::kBRow) {
     // A group's last slot with at most 128 rows runs as a 128-row tile (same
@@ -1481,7 +1481,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
       return;
     }
   }
-  gemm_tile<C, V>(t, o, kOut == kOutBf16 ? p.ldy : p.N, lds);
+  gemm_tile<C, V>(t, o, V::kSwiGLU ? p.N : p.ldy, lds);
 }
 
 template <class C, class V>
@@ -1509,15 +1509,16 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
 // Weight panels (256 rows each) of an M x N output that go on 256-row tiles;
 // the rest go on 128-row tiles.  The shape with the shortest estimated time:
 // rounds of tiles over the 256 CUs times a tile's time, a 128-row tile taking
-// about 0.7 of a 256-row one (measured on the Llama shapes).  A bf16 output
-// may also be split by weight panels: the first n1 panels on 256-row tiles,
-// the rest on 128-row tiles, as two launches into column slices of Y.  At 4096
-// tokens QKV's 24 panels make 384 large tiles (two rounds, the second half
-// empty); 16 panels on large tiles (one round) and 8 on small ones (one round)
-// cost 1.7 instead of 2.  At 2048 tokens QKV's 192 large tiles (one round)
-// beat 384 small ones (+37%), while O and down (128 large tiles, half the CUs
-// idle) take small tiles.
-int64_t dense_large_panels(int64_t M, int64_t N, bool bf16_out) {
+// about 0.7 of a 256-row one (measured on the Llama shapes).  The output of
+// all but the SwiGLU GEMM may also be split by weight panels: the first n1
+// panels on 256-row tiles, the rest on 128-row tiles, as two launches into
+// column slices of the output (bf16 Y, or the E4M3 codes and their scales).
+// At 4096 tokens QKV's 24 panels make 384 large tiles (two rounds, the second
+// half empty); 16 panels on large tiles (one round) and 8 on small ones (one
+// round) cost 1.7 instead of 2 (measured on the quantized output: 1.09x).  At 2048 tokens QKV's 192 large tiles (one round) beat 384 small
+// ones (+37%), while O and down (128 large tiles, half the CUs idle) take
+// small tiles.
+int64_t dense_large_panels(int64_t M, int64_t N, bool may_split) {
   const int64_t tiles_n = (N + kBN - 1) / kBN;
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
@@ -1525,7 +1526,7 @@ int64_t dense_large_panels(int64_t M, int64_t N, bool bf16_out) {
     return (mt_large * n1 + 255) / 256 * 10 + (mt_small * (tiles_n - n1) + 255) / 256 * 7;
   };
   int64_t n1 = cost(tiles_n) <= cost(0) ? tiles_n : 0;
-  if (bf16_out) {
+  if (may_split) {
     for (int64_t c = 1; c < tiles_n; ++c)
       if (cost(c) < cost(n1)) n1 = c;
   }
@@ -1542,7 +1543,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N};
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  const int64_t n1 = dense_large_panels(M, N, kOut == kOutBf16);
+  const int64_t n1 = dense_large_panels(M, N, !kSwiGLU);
   if (n1 == tiles_n) {
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
@@ -1558,7 +1559,12 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
     if (e != hipSuccess) return e;
     p.b_q = b_q + n_off * K;
     p.b_s = b_s + (kBRow ? n_off : n_off / 128) * (K / kBK);
-    p.y = y + n_off;
+    if constexpr (kOut == kOutBf16) {
+      p.y = y + n_off;
+    } else {
+      p.yq = yq + n_off;
+      p.ys = ys + n_off / 128;
+    }
     p.N = N - n_off;
     p.tiles_n = (int32_t)(tiles_n - n1);
   }

@@ -504,11 +504,12 @@ fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s,
                                          void *stream);
 
 /* Informational: how many 256-row weight panels of an M x N dense GEMM
- * output (fp8_blockscaled_gemm and its variants; bf16_output != 0 for the
- * bf16-output GEMMs, 0 for those that quantize their output) run on
- * 256-token x 256 tiles; the other ceil(N/256) - that many run on 128-token
- * tiles.  -1 for invalid sizes.  No device access. */
-int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int bf16_output);
+ * output run on 256-token x 256 tiles; the other ceil(N/256) - that many run
+ * on 128-token tiles.  swiglu = 0 for fp8_blockscaled_gemm and its pow2,
+ * weight-gradient and quantized-output variants (their output may be split
+ * between the two tile heights), 1 for fp8_blockscaled_gemm_swiglu_quant (all
+ * panels on one height).  -1 for invalid sizes.  No device access. */
+int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int swiglu);
 
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);

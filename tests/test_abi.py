@@ -263,12 +263,12 @@ def test_noalloc_scratch_covers_every_split():
 def test_gemm_tile_plan(lib):
     """Weight panels on 256-token tiles: all of them for gate+up and down at 4096
     tokens, 16 of QKV's 24 (one round on each shape), none for O at 2048
-    tokens; a quantized output is not split."""
+    tokens; the SwiGLU GEMM's output is not split."""
     f = lib.fp8_blockscaled_gemm_tile_plan
-    assert f(4096, 28672, 1) == 112 and f(4096, 4096, 1) == 16
-    assert f(4096, 6144, 1) == 16 and f(4096, 6144, 0) in (0, 24)
-    assert f(2048, 4096, 1) == 0
-    assert f(0, 128, 1) == -1 and f(64, 100, 1) == -1
+    assert f(4096, 28672, 0) == 112 and f(4096, 4096, 0) == 16
+    assert f(4096, 6144, 0) == 16 and f(4096, 6144, 1) in (0, 24)
+    assert f(2048, 4096, 0) == 0
+    assert f(0, 128, 0) == -1 and f(64, 100, 0) == -1
 
 
 def test_moe_permute_argument_errors(lib):

@@ -103,6 +103,30 @@ def test_fused_exact_integer_products(mode):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
+def test_fused_llama_qkv_panel_split(mode):
+    # The QKV projection at 4096 tokens: 16 weight panels on 256-row tiles and
+    # 8 on 128-row tiles, two launches into column slices of the codes and
+    # scales.  Whole output, bit for bit against quantizing the bf16 output.
+    require_gpu()
+    M, N, K = 4096, 6144, 4096
+    big, small = lib().fp8_blockscaled_gemm_tile_plan(M, N)
+    assert big > 0 and small > 0, (big, small)
+    aq, as_, bq, bs = _operands(M, N, K, seed=43 + mode)
+    say("gemm_quant qkv split", M, N, K, MODES[mode], big, small)
+    q, s, ybits = _run(aq, as_, bq, bs, mode)
+    q_ref, s_ref = oracle.quant_act_1x128(ybits, mode)
+    assert_bytes_equal(q, q_ref, "qkv bytes")
+    assert_scales_equal(s, s_ref, "qkv scales")
+    _check_half_step(q, s, ybits, "qkv")
+    rows = np.arange(3, M, 89)
+    cols = np.concatenate([np.arange(7, N, 61), [big * 256 - 1, big * 256, N - 1]])
+    ms, ns = np.meshgrid(rows, cols, indexing="ij")
+    ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms.reshape(-1), ns.reshape(-1))
+    ybf = (ybits.astype(np.uint32) << 16).view(np.float32)[ms.reshape(-1), ns.reshape(-1)]
+    gemm_tolerance_check(ybf, ref, "qkv sampled bf16 Y", frob=2e-3)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
 def test_fused_llama_o_full_size(mode):
     # The Llama-3.1-8B O projection at 4096 tokens (256x256 tiles, one per CU).
     require_gpu()
