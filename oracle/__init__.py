@@ -27,6 +27,8 @@ from .oracle import (  # noqa: F401
     gemm_wgrad_sampled_f64,
     kv_cache_append,
     attention_decode_f64,
+    kv_cache_append_tokens,
+    attention_prefill_f64,
     swiglu_split,
     bf16_to_f64,
     swiglu_h_f64,

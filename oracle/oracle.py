@@ -306,7 +306,10 @@ def gemm_wgrad_sampled_f64(gtq, gts, xtq, xts, ns, ks):
 # key/value head (head dimension 128) is one 1x128 block with its own scale,
 # and so is every query row of one query head.  Decode attention is the
 # standard softmax(q k^T / sqrt(D)) v over the cached tokens, with grouped
-# query heads (query head h reads key/value head h // (Hq / Hkv)).
+# query heads (query head h reads key/value head h // (Hq / Hkv)).  With many
+# query tokens (prefill, chunked prefill, a training forward pass) the plainest
+# reading is causal attention over the cache: the query at position p sees the
+# cached tokens 0..p, its own included.
 # ---------------------------------------------------------------------------
 
 def kv_cache_append(new_bits, pos, cache_q, cache_s, mode=MODE_AMAX):
@@ -355,6 +358,66 @@ def attention_decode_f64(qq, qs, kq, ks, vq, vs, seq_len):
             p = np.exp(sc)
             p /= p.sum(axis=1, keepdims=True)
             o[b, g * grp:(g + 1) * grp] = p @ v
+    return o
+
+
+def kv_cache_append_tokens(new_bits, start, cache_q, cache_s, mode=MODE_AMAX):
+    """Quantize T new rows per sequence and key/value head and store token t of
+    sequence b at position start[b] + t: new_bits uint16 [B, T, Hkv, D] (bf16,
+    token-major as a projection writes its output), cache_q uint8
+    [B, Hkv, S, D], cache_s f32 [B, Hkv, S] (updated in place and returned).
+    A position outside [0, S) stores nothing."""
+    new = _c(new_bits, np.uint16)
+    B, T, H, D = new.shape
+    q, s = quant_act_1x128(new.reshape(B * T * H, D), mode)
+    q, s = q.reshape(B, T, H, D), s.reshape(B, T, H)
+    S = cache_q.shape[2]
+    for b in range(B):
+        for t in range(T):
+            p = int(start[b]) + t
+            if 0 <= p < S:
+                cache_q[b, :, p] = q[b, t]
+                cache_s[b, :, p] = s[b, t]
+    return cache_q, cache_s
+
+
+def attention_prefill_f64(qq, qs, kq, ks, vq, vs, start):
+    """Many query tokens per sequence (prefill, or a training forward pass)
+    against the cached keys and values, causal.
+
+    qq uint8 [B, T, Hq, D], qs f32 [B, T, Hq]   query rows (1x128 blocks),
+        token-major as a projection writes them
+    kq, vq uint8 [B, Hkv, S, D], ks, vs f32 [B, Hkv, S]
+    start [B]: query t of sequence b sits at position start[b] + t and attends
+    to the cached tokens 0 .. start[b] + t (itself included), those below S; a
+    query with none gives a zero output.
+    Returns o [B, T, Hq, D] (fp64): operands dequantized exactly, scores,
+    softmax and the weighted sum of values in fp64.
+    """
+    table = e4m3_decode_table()
+    qq, kq, vq = _c(qq, np.uint8), _c(kq, np.uint8), _c(vq, np.uint8)
+    B, T, Hq, D = qq.shape
+    Hkv, S = kq.shape[1], kq.shape[2]
+    grp = Hq // Hkv
+    o = np.zeros((B, T, Hq, D), dtype=np.float64)
+    keys = np.arange(S)
+    for b in range(B):
+        pos = int(start[b]) + np.arange(T)
+        allowed = keys[None, :] <= pos[:, None]                  # [T, S]
+        live = allowed.any(axis=1)
+        q = table[qq[b]] * np.asarray(qs[b], dtype=np.float64)[:, :, None]    # [T, Hq, D]
+        for g in range(Hkv):
+            k = table[kq[b, g]] * np.asarray(ks[b, g], dtype=np.float64)[:, None]
+            v = table[vq[b, g]] * np.asarray(vs[b, g], dtype=np.float64)[:, None]
+            for j in range(grp):
+                h = g * grp + j
+                sc = q[:, h, :] @ k.T / np.sqrt(D)                # [T, S]
+                sc = np.where(allowed, sc, -np.inf)
+                mx = np.where(live, sc.max(axis=1), 0.0)
+                p = np.where(allowed, np.exp(sc - mx[:, None]), 0.0)
+                den = p.sum(axis=1)
+                p = p / np.where(live, den, 1.0)[:, None]
+                o[b, :, h, :] = p @ v
     return o
 
 

@@ -10,6 +10,13 @@ Praxis").  Pins, none of which uses the function under test:
     mean of the value rows; two tokens give sigmoid weights;
   - tokens at or past seq_len, and other key/value heads, change nothing;
   - the cache append against the 1x128 row quantizer, placed by position.
+Many query tokens (causal over the cache, query t at position start + t):
+  - torch's scaled_dot_product_attention in float64 with an explicit boolean
+    mask (key position <= query position);
+  - closed forms: position 0 gives value row 0, equal scores give prefix means;
+  - later cache rows and other heads change nothing; a query before position
+    0 gives zeros; one query token at position p equals decode over p + 1;
+  - the multi-token append against the row quantizer, placed at start + t.
 """
 import math
 
@@ -132,3 +139,108 @@ def test_cache_append_places_quantized_rows(oracle_lib, mode):
         for t in range(S):
             if untouched[b, t]:
                 assert (cq[b, :, t] == 0x11).all() and (cs[b, :, t] == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# Many query tokens (prefill / training forward): causal over the cache, query
+# t of sequence b at position start[b] + t.
+# ---------------------------------------------------------------------------
+
+def _prefill_inputs(rng, B, T, Hq, Hkv, S):
+    qq = _codes(rng, (B, T, Hq, D))
+    qs = rng.uniform(1e-3, 4e-3, size=(B, T, Hq)).astype(np.float32)
+    kq, vq = _codes(rng, (B, Hkv, S, D)), _codes(rng, (B, Hkv, S, D))
+    ks = rng.uniform(1e-3, 4e-3, size=(B, Hkv, S)).astype(np.float32)
+    vs = rng.uniform(1e-3, 1e-2, size=(B, Hkv, S)).astype(np.float32)
+    return qq, qs, kq, ks, vq, vs
+
+
+def test_prefill_against_torch_sdpa_causal_mask(oracle_lib):
+    """torch's scaled_dot_product_attention in float64 with an explicit boolean
+    mask (key position <= query position, below S), heads expanded."""
+    rng = np.random.default_rng(11)
+    B, T, Hq, Hkv, S = 3, 21, 8, 2, 40
+    qq, qs, kq, ks, vq, vs = _prefill_inputs(rng, B, T, Hq, Hkv, S)
+    start = np.array([0, 12, 30], dtype=np.int32)       # the last runs past S
+    o = oracle_lib.attention_prefill_f64(qq, qs, kq, ks, vq, vs, start)
+    for b in range(B):
+        pos = start[b] + np.arange(T)
+        mask = torch.from_numpy(np.arange(S)[None, :] <= pos[:, None])           # [T, S]
+        q = torch.from_numpy((_dec(qq[b]) * qs[b][:, :, None].astype(np.float64)).transpose(1, 0, 2))  # [Hq, T, D]
+        k = torch.from_numpy(_dec(kq[b]) * ks[b][:, :, None].astype(np.float64))
+        v = torch.from_numpy(_dec(vq[b]) * vs[b][:, :, None].astype(np.float64))
+        k = k.repeat_interleave(Hq // Hkv, dim=0)
+        v = v.repeat_interleave(Hq // Hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask).numpy()
+        assert np.allclose(o[b].transpose(1, 0, 2), ref, rtol=1e-12, atol=1e-15), b
+
+
+def test_prefill_position_zero_and_prefix_means(oracle_lib):
+    """The query at position 0 returns value row 0; with every score equal the
+    query at position p returns the mean of value rows 0..p."""
+    rng = np.random.default_rng(12)
+    B, T, Hq, Hkv, S = 1, 9, 4, 1, 9
+    qq, qs, kq, ks, vq, vs = _prefill_inputs(rng, B, T, Hq, Hkv, S)
+    o = oracle_lib.attention_prefill_f64(qq, qs, kq, ks, vq, vs, np.array([0]))
+    v = _dec(vq[0, 0]) * vs[0, 0, :, None].astype(np.float64)
+    assert np.array_equal(o[0, 0], np.broadcast_to(v[0], (Hq, D)))
+    kq[:] = 0
+    o = oracle_lib.attention_prefill_f64(qq, qs, kq, ks, vq, vs, np.array([0]))
+    for t in range(T):
+        assert np.allclose(o[0, t], v[:t + 1].mean(axis=0)[None, :], rtol=1e-14, atol=0), t
+
+
+def test_prefill_future_tokens_and_other_heads_do_not_enter(oracle_lib):
+    """Cache rows after a query's position, and the other key/value heads, do not
+    change its output; a query before position 0 gives zeros."""
+    rng = np.random.default_rng(13)
+    B, T, Hq, Hkv, S = 2, 6, 4, 2, 20
+    qq, qs, kq, ks, vq, vs = _prefill_inputs(rng, B, T, Hq, Hkv, S)
+    start = np.array([4, -3])
+    o = oracle_lib.attention_prefill_f64(qq, qs, kq, ks, vq, vs, start)
+    kq2, vq2 = kq.copy(), vq.copy()
+    kq2[0, :, 7:] = _codes(rng, kq2[0, :, 7:].shape)      # positions 7.. (queries 0..3 sit at 4..7)
+    vq2[0, :, 7:] = _codes(rng, vq2[0, :, 7:].shape)
+    kq2[0, 1] = _codes(rng, kq2[0, 1].shape)              # head 1 serves query heads 2, 3
+    o2 = oracle_lib.attention_prefill_f64(qq, qs, kq2, ks, vq2, vs, start)
+    assert np.array_equal(o[0, :3, :2], o2[0, :3, :2])
+    assert not np.allclose(o[0, :3, 2:], o2[0, :3, 2:])
+    assert not o[1, :3].any() and o[1, 3:].any()            # positions -3..-1 see nothing
+
+
+def test_prefill_single_query_is_decode(oracle_lib):
+    """One query token at position p is decode attention over p + 1 tokens."""
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, S = 3, 8, 2, 30
+    qq, qs, kq, ks, vq, vs = _prefill_inputs(rng, B, 1, Hq, Hkv, S)
+    start = np.array([0, 17, 40])
+    o = oracle_lib.attention_prefill_f64(qq, qs, kq, ks, vq, vs, start)
+    od = oracle_lib.attention_decode_f64(qq[:, 0], qs[:, 0], kq, ks, vq, vs, start + 1)
+    assert np.allclose(o[:, 0], od, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_cache_append_tokens_places_quantized_rows(oracle_lib, mode):
+    """T rows per sequence land at start[b] + t as the 1x128 row quantizer
+    codes them; positions outside the cache store nothing."""
+    rng = np.random.default_rng(15 + mode)
+    B, T, H, S = 3, 4, 2, 6
+    new = _bf16(rng.standard_normal((B, T, H, D)).astype(np.float32))
+    cq = np.full((B, H, S, D), 0x11, np.uint8)
+    cs = np.full((B, H, S), 7.0, np.float32)
+    start = np.array([0, 4, -2])
+    cq, cs = oracle_lib.kv_cache_append_tokens(new, start, cq, cs, mode)
+    q, s = oracle_lib.quant_act_1x128(new.reshape(B * T * H, D), mode)
+    q, s = q.reshape(B, T, H, D), s.reshape(B, T, H)
+    written = np.zeros((B, S), bool)
+    for b in range(B):
+        for t in range(T):
+            p = start[b] + t
+            if 0 <= p < S:
+                written[b, p] = True
+                assert np.array_equal(cq[b, :, p], q[b, t]) and np.array_equal(cs[b, :, p], s[b, t])
+    assert written.sum() == 4 + 2 + 2
+    for b in range(B):
+        for p in range(S):
+            if not written[b, p]:
+                assert (cq[b, :, p] == 0x11).all() and (cs[b, :, p] == 7.0).all()
