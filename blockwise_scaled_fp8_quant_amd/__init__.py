@@ -444,6 +444,65 @@ def fp8_kv_cache_append(k_new, v_new, pos, cache, mode="amax"):
     return cache
 
 
+def fp8_kv_cache_append_tokens(k_new, v_new, start, cache, mode="amax"):
+    """Quantize T new key and value rows per sequence and head (bf16
+    [B, T, Hkv, 128] each, token-major) into the FP8 cache: token t of sequence
+    b at position start[b] + t (start int32 [B], device).  cache as for
+    fp8_kv_cache_append, updated in place."""
+    kq, ks, vq, vs = cache
+    pk = _dev(k_new, "k_new", torch.bfloat16, 4)
+    pv = _dev(v_new, "v_new", torch.bfloat16, 4)
+    pst = _dev(start, "start", torch.int32, 1)
+    kq, pkq = _as_bytes(kq, "k_cache", 4)
+    vq, pvq = _as_bytes(vq, "v_cache", 4)
+    pks = _dev(ks, "k_scale", torch.float32, 3)
+    pvs = _dev(vs, "v_scale", torch.float32, 3)
+    B, H, S, Dh = kq.shape
+    T = k_new.shape[1]
+    if Dh != 128 or tuple(k_new.shape) != (B, T, H, 128) or tuple(v_new.shape) != (B, T, H, 128):
+        raise ValueError("new rows must be [B, T, Hkv, 128] matching the cache")
+    if tuple(vq.shape) != (B, H, S, 128) or tuple(ks.shape) != (B, H, S) or tuple(vs.shape) != (B, H, S):
+        raise ValueError("cache shapes do not match")
+    if start.numel() != B:
+        raise ValueError("start must have B entries")
+    _lib.check("fp8_kv_cache_append_tokens",
+               _lib.load().fp8_kv_cache_append_tokens(pk, pv, pst, pkq, pks, pvq, pvs, B, T, H, S, _mode(mode),
+                                                      _stream(k_new)))
+    return cache
+
+
+def fp8_attention_prefill(q_q, q_s, cache, start, out=None):
+    """Causal attention of T query tokens per sequence over the FP8 cache:
+    query t of sequence b at position start[b] + t sees cached tokens
+    0 .. start[b] + t.  q_q uint8 [B, T, Hq, 128] and q_s f32 [B, T, Hq] (query
+    rows in 1x128 blocks), cache as for fp8_kv_cache_append, start int32 [B]
+    (device).  Returns bf16 [B, T, Hq, 128]."""
+    kq, ks, vq, vs = cache
+    q_q, pq = _as_bytes(q_q, "q_q", 4)
+    pqs = _dev(q_s, "q_s", torch.float32, 3)
+    kq, pkq = _as_bytes(kq, "k_cache", 4)
+    vq, pvq = _as_bytes(vq, "v_cache", 4)
+    pks = _dev(ks, "k_scale", torch.float32, 3)
+    pvs = _dev(vs, "v_scale", torch.float32, 3)
+    pst = _dev(start, "start", torch.int32, 1)
+    B, T, Hq, Dh = q_q.shape
+    Bk, Hkv, S, Dk = kq.shape
+    if Dh != 128 or Dk != 128 or Bk != B or tuple(q_s.shape) != (B, T, Hq):
+        raise ValueError("query and cache shapes do not match")
+    if tuple(vq.shape) != (B, Hkv, S, 128) or tuple(ks.shape) != (B, Hkv, S) or tuple(vs.shape) != (B, Hkv, S):
+        raise ValueError("cache shapes do not match")
+    if start.numel() != B:
+        raise ValueError("start must have B entries")
+    y = torch.empty((B, T, Hq, 128), dtype=torch.bfloat16, device=q_q.device) if out is None else out
+    py = _dev(y, "out", torch.bfloat16, 4)
+    if tuple(y.shape) != (B, T, Hq, 128):
+        raise ValueError("output shape does not match")
+    _lib.check("fp8_attention_prefill",
+               _lib.load().fp8_attention_prefill(pq, pqs, pkq, pks, pvq, pvs, pst, py, B, T, Hq, Hkv, S,
+                                                 _stream(q_q)))
+    return y
+
+
 def fp8_attention_decode_workspace_size(B, Hq, Hkv, S):
     return _lib.load().fp8_attention_decode_workspace_size(B, Hq, Hkv, S)
 

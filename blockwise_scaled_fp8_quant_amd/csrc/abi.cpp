@@ -379,8 +379,49 @@ fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, co
                FP8Q_EALIGN, "pointers must be 16-byte aligned");
   fp8q_status st = check_device(__func__);
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_kv_cache_append(k_new, v_new, pos, k_cache, k_scale, v_cache, v_scale, B, Hkv, S,
+  return launched(fp8q::launch_kv_cache_append(k_new, v_new, pos, k_cache, k_scale, v_cache, v_scale, B, 1, Hkv, S,
                                                mode, (hipStream_t)stream),
+                  __func__);
+}
+
+fp8q_status fp8_kv_cache_append_tokens(const uint16_t *k_new, const uint16_t *v_new, const int32_t *start,
+                                       uint8_t *k_cache, float *k_scale, uint8_t *v_cache, float *v_scale,
+                                       int32_t B, int32_t T, int32_t Hkv, int64_t S, int mode, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
+  FP8Q_REQUIRE(B >= 0 && T >= 0 && Hkv >= 0 && S >= 0, FP8Q_EINVAL, "negative size");
+  if ((int64_t)B * T * Hkv == 0) return FP8Q_OK;
+  FP8Q_REQUIRE((int64_t)B * T * Hkv < ((int64_t)1 << 34), FP8Q_ESHAPE, "B*T*Hkv must be below 2^34");
+  FP8Q_REQUIRE(k_new && v_new && start && k_cache && k_scale && v_cache && v_scale, FP8Q_EINVAL, "null pointer");
+  FP8Q_REQUIRE(aligned16(k_new) && aligned16(v_new) && aligned16(start) && aligned16(k_cache) &&
+                   aligned16(k_scale) && aligned16(v_cache) && aligned16(v_scale),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_kv_cache_append(k_new, v_new, start, k_cache, k_scale, v_cache, v_scale, B, T, Hkv,
+                                               S, mode, (hipStream_t)stream),
+                  __func__);
+}
+
+fp8q_status fp8_attention_prefill(const uint8_t *q_q, const float *q_s, const uint8_t *k_cache,
+                                  const float *k_scale, const uint8_t *v_cache, const float *v_scale,
+                                  const int32_t *start, uint16_t *out, int32_t B, int32_t T, int32_t Hq,
+                                  int32_t Hkv, int64_t S, void *stream) {
+  g_last_error.clear();
+  FP8Q_REQUIRE(B >= 0 && T >= 0 && Hq >= 0 && Hkv >= 0 && S >= 0, FP8Q_EINVAL, "negative size");
+  FP8Q_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, FP8Q_ESHAPE, "Hq must be a positive multiple of Hkv");
+  if ((int64_t)B * T * Hq == 0) return FP8Q_OK;
+  FP8Q_REQUIRE((int64_t)(T + 63) / 64 * B * Hq < ((int64_t)1 << 31), FP8Q_ESHAPE,
+               "ceil(T/64)*B*Hq must be below 2^31");
+  FP8Q_REQUIRE(q_q && q_s && k_cache && k_scale && v_cache && v_scale && start && out, FP8Q_EINVAL,
+               "null pointer");
+  FP8Q_REQUIRE(aligned16(q_q) && aligned16(q_s) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
+                   aligned16(v_scale) && aligned16(start) && aligned16(out),
+               FP8Q_EALIGN, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(__func__);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_attention_prefill(q_q, q_s, k_cache, k_scale, v_cache, v_scale, start, out, B, T, Hq,
+                                                 Hkv, S, (hipStream_t)stream),
                   __func__);
 }
 

@@ -24,49 +24,52 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kHeadDim = 128;
 
 // ---------------------------------------------------------------------------
-// Cache append: one new key row and one new value row per sequence and head,
-// quantized with the activation rule and stored at token position pos[b].
-// Eight lanes per row (as in the activation quantizer); row r of the 2*B*Hkv
-// rows is a key row for r < B*Hkv, else a value row.
+// Cache append: T new key rows and T new value rows per sequence and head,
+// token-major ([B][T][Hkv][128], as a projection writes them), quantized with
+// the activation rule; token t of sequence b goes to position start[b] + t.
+// Eight lanes per row (as in the activation quantizer); row r of the
+// 2*B*T*Hkv rows is a key row for r < B*T*Hkv, else a value row.
 // ---------------------------------------------------------------------------
 template <int kMode>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new,
-                                                        const int32_t *__restrict__ pos, uint8_t *__restrict__ kc,
+                                                        const int32_t *__restrict__ start, uint8_t *__restrict__ kc,
                                                         float *__restrict__ ks, uint8_t *__restrict__ vc,
-                                                        float *__restrict__ vs, int32_t B, int32_t H, int64_t S) {
+                                                        float *__restrict__ vs, int32_t B, int32_t T, int32_t H,
+                                                        int64_t S) {
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int sub = threadIdx.x & 7;
-  const int64_t rows = (int64_t)B * H;
+  const int64_t rows = (int64_t)B * T * H;
   if (row >= 2 * rows) return;  // uniform over the 8 lanes of a row
   const bool is_v = row >= rows;
-  const int64_t r = is_v ? row - rows : row;  // = b * H + h
-  const int64_t b = r / H;
+  const int64_t r = is_v ? row - rows : row;  // = (b * T + t) * H + h
+  const int64_t h = r % H, bt = r / H;
+  const int64_t b = bt / T, t = bt - b * T;
   const uint4 *src = reinterpret_cast<const uint4 *>((is_v ? v_new : k_new) + r * kHeadDim);
   const uint4 x0 = src[sub], x1 = src[sub + 8];
   float amax = group8_max(chunk_absmax(x1, chunk_absmax(x0, 0.0f)));
   const BlockQ p = block_params<kMode>(amax);
-  const int64_t t = pos[b];
-  if (t < 0 || t >= S) return;
-  const int64_t slot = r * S + t;  // (b, h, t)
+  const int64_t pos = (int64_t)start[b] + t;
+  if (pos < 0 || pos >= S) return;
+  const int64_t slot = (b * H + h) * S + pos;  // (b, h, pos)
   uint2 *dst = reinterpret_cast<uint2 *>((is_v ? vc : kc) + slot * kHeadDim);
   dst[sub] = quant_chunk<kMode>(p, x0);
   dst[sub + 8] = quant_chunk<kMode>(p, x1);
   if (sub == 0) (is_v ? vs : ks)[slot] = p.s;
 }
 
-hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, uint8_t *kc,
-                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t H, int64_t S, int mode,
-                                  hipStream_t stream) {
-  const int64_t rows = 2 * (int64_t)B * H;
+hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *start, uint8_t *kc,
+                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t T, int32_t H, int64_t S,
+                                  int mode, hipStream_t stream) {
+  const int64_t rows = 2 * (int64_t)B * T * H;
   if (rows == 0) return hipSuccess;
   const int64_t grid = (rows + 31) / 32;
   if (mode == kModeAmax)
-    hipLaunchKernelGGL(kv_append_kernel<kModeAmax>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, pos,
-                       kc, ks, vc, vs, B, H, S);
+    hipLaunchKernelGGL(kv_append_kernel<kModeAmax>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, start,
+                       kc, ks, vc, vs, B, T, H, S);
   else
-    hipLaunchKernelGGL(kv_append_kernel<kModePow2>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, pos,
-                       kc, ks, vc, vs, B, H, S);
+    hipLaunchKernelGGL(kv_append_kernel<kModePow2>, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new, start,
+                       kc, ks, vc, vs, B, T, H, S);
   return hipGetLastError();
 }
 
@@ -493,6 +496,264 @@ hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, c
     if (e != hipSuccess) return e;
   }
   return launch_attention_decode(qq, qs, kc, ks, vc, vs, len, out, B, Hq, Hkv, S, ws, stream);
+}
+
+
+// ---------------------------------------------------------------------------
+// Attention for many query tokens (prefill, chunked prefill, a training
+// forward pass) over the FP8 cache, causal: query t of sequence b sits at
+// position start[b] + t and attends to the cached tokens 0 .. start[b] + t
+// below S (the queries' own keys and values are appended to the cache
+// first).  Queries are token-major, q [B][T][Hq][128] E4M3 with one scale per
+// row, as the QKV projection's quantized output holds them.
+//
+// One workgroup per (sequence, query head, 64 query tokens); its four waves
+// own 16 query tokens each.  Workgroups are ordered longest first (the last
+// query tiles of every head start first).  Per 64-key tile:
+//  - the workgroup stages the tile in LDS: the E4M3 key rows as they are, the
+//    value rows decoded exactly to bf16 (every E4M3 value is a bf16 value) and
+//    transposed to [dim][key], and the 64 key and value scales;
+//  - scores S^T = K Q^T on the matrix cores in FP8: one
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 keys (the whole head dimension
+//    in one instruction), key rows as A and the wave's query rows as B, so
+//    lane l holds keys 4(l/16)..+3 of query l%16 and every per-query quantity
+//    (running maximum, sum, output column) lives in one lane column;
+//  - online softmax in base 2, one rescale per tile; the weights p * v_scale
+//    are rounded to bf16 (relative error at most 2^-8 each) and go straight
+//    from the score registers into the B operand of the value product;
+//  - O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, eight per 32 keys (16 dims
+//    each), fp32 accumulation: lane l holds dims 4(l/16)..+3 of each 16-dim
+//    block for query l%16.  The MFMA's k slots of lane group q are keys
+//    4q..4q+3 and 16+4q..16+4q+3 of the 32 (the keys whose scores that lane
+//    group holds); V^T is stored with its keys in that order.
+// LDS rows are XOR-swizzled in 16-byte chunks by row so that the 16 lanes
+// reading one chunk of 16 different rows hit different banks.
+// ---------------------------------------------------------------------------
+constexpr int kPfWaves = 4;
+constexpr int kPfQ = 16 * kPfWaves;  // query tokens per workgroup
+constexpr int kPfKeys = 64;          // keys per staged tile
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+struct PrefillArgs {
+  const uint8_t *qq;
+  const float *qs;
+  const uint8_t *kc;
+  const float *ks;
+  const uint8_t *vc;
+  const float *vs;
+  const int32_t *start;
+  uint16_t *out;
+  int32_t B, T, Hq, Hkv;
+  int64_t S;
+  int32_t qtiles;  // ceil(T / kPfQ)
+};
+
+struct PrefillLds {
+  uint8_t k[kPfKeys * kHeadDim];        // key rows, chunk c of row r at c ^ (r & 7)
+  uint16_t vt[kHeadDim * kPfKeys];      // V^T bf16: row d, key slot j at chunk (j / 8) ^ (d & 7)
+  float ks[kPfKeys], vs[kPfKeys];
+};
+
+// Slot of key j (0..63) in a V^T row: inside each 32-key half, keys 4q..4q+3
+// go to slots 8q..8q+3 and keys 16+4q..16+4q+3 to slots 8q+4..8q+7.
+__device__ __forceinline__ int vt_slot(int j) {
+  const int half = j & 32, k = j & 31;
+  return half + (k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3));
+}
+
+__device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));  // RNE
+}
+
+__global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) PrefillLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t BH = (int64_t)a.B * a.Hq;
+  const int64_t blk = blockIdx.x;
+  const int qt = a.qtiles - 1 - (int)(blk / BH);  // longest first
+  const int64_t bh = blk - (int64_t)(a.qtiles - 1 - qt) * BH;
+  const int64_t b = bh / a.Hq, h = bh - b * a.Hq;
+  const int64_t g = h / (a.Hq / a.Hkv);
+  const int64_t st = a.start[b];
+  const int t0 = qt * kPfQ;
+  const int tlast = (t0 + kPfQ < a.T ? t0 + kPfQ : a.T) - 1;  // last query token of the workgroup
+  // keys [0, kend) can enter any of the workgroup's outputs
+  int64_t kend = st + tlast + 1;
+  kend = kend < a.S ? kend : a.S;
+  const int ntiles = kend > 0 ? (int)((kend + kPfKeys - 1) / kPfKeys) : 0;
+
+  // This lane's query (column l%16 of the wave's 16) and its key limit.
+  const int tq = t0 + 16 * wave + (lane & 15);
+  const bool qvalid = tq < a.T;
+  int64_t lim = st + tq;  // last key position it may see
+  lim = lim < a.S - 1 ? lim : a.S - 1;
+  if (!qvalid) lim = -1;
+  // the wave's own last key (uniform): tiles past it hold nothing for the wave
+  const int twl = t0 + 16 * wave + 15 < a.T ? t0 + 16 * wave + 15 : a.T - 1;
+  int64_t wlim = st + twl;
+  wlim = wlim < a.S - 1 ? wlim : a.S - 1;
+  if (t0 + 16 * wave >= a.T) wlim = -1;
+
+  // Query rows as the B operand: lane l gives query l%16, bytes 32(l/16)..+31.
+  v8i_t qf = {0, 0, 0, 0, 0, 0, 0, 0};
+  float qmul = 0.0f;
+  constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
+  if (qvalid) {
+    const int64_t qrow = (b * a.T + tq) * a.Hq + h;
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.qq + qrow * kHeadDim + 32 * (lane >> 4));
+    const uint4 x = qp[0], y = qp[1];
+    qf[0] = x.x; qf[1] = x.y; qf[2] = x.z; qf[3] = x.w;
+    qf[4] = y.x; qf[5] = y.y; qf[6] = y.z; qf[7] = y.w;
+    qmul = a.qs[qrow] * kL2eRsqrtD;
+  }
+
+  const int64_t base = (b * a.Hkv + g) * a.S;  // (b, g, token 0) in the cache
+  const uint8_t *kc = a.kc + base * kHeadDim;
+  const uint8_t *vc = a.vc + base * kHeadDim;
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;  // per query (lane column); l_run per lane
+  v4f_t acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int64_t k0 = (int64_t)kt * kPfKeys;
+    __syncthreads();  // every wave is done with the previous tile
+    {
+      // key rows: 512 chunks of 16 bytes, two per thread
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i;
+        const int r = c >> 3, cc = c & 7;
+        int64_t key = k0 + r;
+        key = key < a.S ? key : a.S - 1;
+        const uint4 v = *reinterpret_cast<const uint4 *>(kc + key * kHeadDim + 16 * cc);
+        *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = v;
+      }
+      // value rows: thread = 4 keys x 8 dims, decoded to bf16 and transposed
+      const int kg = tid >> 4, d8 = tid & 15;
+      float f[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int64_t key = k0 + 4 * kg + j;
+        key = key < a.S ? key : a.S - 1;
+        dec8(*reinterpret_cast<const uint2 *>(vc + key * kHeadDim + 8 * d8), f[j]);
+      }
+      const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * d8 + e;
+        uint2 w;
+        w.x = bf16x2_of(f[0][e], f[1][e]);
+        w.y = bf16x2_of(f[2][e], f[3][e]);
+        *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
+      }
+      if (tid < kPfKeys) {
+        int64_t key = k0 + tid;
+        key = key < a.S ? key : a.S - 1;
+        L.ks[tid] = a.ks[base + key];
+        L.vs[tid] = a.vs[base + key];
+      }
+    }
+    __syncthreads();
+    if (k0 > wlim) continue;  // the whole tile lies after the wave's last query
+
+    // scores of the 64 keys: four MFMAs of 16 keys
+    float sc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + (lane & 15);
+      const uint4 x = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4)) ^ (r & 7))]);
+      const uint4 y = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4) + 1) ^ (r & 7))]);
+      const v8i_t kf = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, zero, 0, 0, 0, 127, 0, 127);
+      const float4 ksc = *reinterpret_cast<const float4 *>(&L.ks[16 * j + 4 * (lane >> 4)]);
+      const float kv[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = k0 + 16 * j + 4 * (lane >> 4) + i;
+        sc[j][i] = key <= lim ? d[i] * (qmul * kv[i]) : -__builtin_inff();
+      }
+    }
+    // online softmax over the tile (the four lanes l, l^16, l^32, l^48 share a query)
+    float mt = sc[0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = __builtin_fmaxf(mt, sc[j][i]);
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = __builtin_fmaxf(m_run, mt);
+    const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;  // no key yet: keep everything at 0
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.0f;
+    uint32_t pw[2][4];  // bf16 pairs of p * v_scale: [32-key half][k-slot pair]
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const float4 va = *reinterpret_cast<const float4 *>(&L.vs[32 * hf + 4 * (lane >> 4)]);
+      const float4 vb = *reinterpret_cast<const float4 *>(&L.vs[32 * hf + 16 + 4 * (lane >> 4)]);
+      const float vsa[4] = {va.x, va.y, va.z, va.w}, vsb[4] = {vb.x, vb.y, vb.z, vb.w};
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(sc[2 * hf][i] - m_use);
+        p[4 + i] = __builtin_amdgcn_exp2f(sc[2 * hf + 1][i] - m_use);
+        psum += p[i] + p[4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        pw[hf][i] = bf16x2_of(p[2 * i] * vsa[2 * i], p[2 * i + 1] * vsa[2 * i + 1]);
+        pw[hf][2 + i] = bf16x2_of(p[4 + 2 * i] * vsb[2 * i], p[4 + 2 * i + 1] * vsb[2 * i + 1]);
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    // O^T += V^T P^T, 32 keys at a time
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, (uint4){pw[hf][0], pw[hf][1], pw[hf][2], pw[hf][3]});
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int d = 16 * db + (lane & 15);
+        const int chunk = 4 * hf + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4 *>(&L.vt[d * kPfKeys + 8 * (chunk ^ (d & 7))]);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v), pb, acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // Normalize and store: lane l holds dims 16db + 4(l/16) .. +3 of query l%16.
+  float ltot = l_run + __shfl_xor(l_run, 16);
+  ltot += __shfl_xor(ltot, 32);
+  if (!qvalid) return;
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  uint16_t *o = a.out + ((b * a.T + tq) * a.Hq + h) * kHeadDim + 4 * (lane >> 4);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    uint2 w;
+    w.x = bf16x2_of(acc[db][0] * inv, acc[db][1] * inv);
+    w.y = bf16x2_of(acc[db][2] * inv, acc[db][3] * inv);
+    *reinterpret_cast<uint2 *>(o + 16 * db) = w;
+  }
+}
+
+hipError_t launch_attention_prefill(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
+                                    const uint8_t *vc, const float *vs, const int32_t *start, uint16_t *out,
+                                    int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int64_t S,
+                                    hipStream_t stream) {
+  if ((int64_t)B * T * Hq == 0) return hipSuccess;
+  PrefillArgs a{qq, qs, kc, ks, vc, vs, start, out, B, T, Hq, Hkv, S, (T + kPfQ - 1) / kPfQ};
+  const int64_t grid = (int64_t)a.qtiles * B * Hq;
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace fp8q

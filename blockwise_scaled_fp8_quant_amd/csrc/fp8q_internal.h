@@ -94,11 +94,19 @@ hipError_t launch_moe_permute(const int32_t *ids, int64_t T, int32_t k, int32_t 
                               int32_t *offsets, int32_t *row_index, int32_t *entry_row, void *workspace,
                               hipStream_t stream);
 
-// FP8 KV cache: quantize one new key and value row per sequence and head
-// (1x128 blocks) into [B][H][S][128] caches at token position pos[b].
-hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, uint8_t *kc,
-                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t H, int64_t S, int mode,
-                                  hipStream_t stream);
+// FP8 KV cache: quantize T new key and value rows per sequence and head
+// ([B][T][H][128] bf16, 1x128 blocks) into [B][H][S][128] caches, token t of
+// sequence b at position start[b] + t.
+hipError_t launch_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *start, uint8_t *kc,
+                                  float *ks, uint8_t *vc, float *vs, int32_t B, int32_t T, int32_t H, int64_t S,
+                                  int mode, hipStream_t stream);
+
+// Causal attention of T query tokens per sequence ([B][T][Hq][128] E4M3)
+// over the FP8 cache; query t of sequence b at position start[b] + t.
+hipError_t launch_attention_prefill(const uint8_t *qq, const float *qs, const uint8_t *kc, const float *ks,
+                                    const uint8_t *vc, const float *vs, const int32_t *start, uint16_t *out,
+                                    int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int64_t S,
+                                    hipStream_t stream);
 
 // Decode attention over the FP8 KV cache (Hq / Hkv in {1, 2, 4, 8}).  With a
 // workspace of B*Hq*nch*130 floats (nch from attention_decode_split) and

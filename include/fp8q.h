@@ -415,6 +415,52 @@ fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new,
                                 void *stream);
 
 /*
+ * Append T tokens per sequence to the FP8 KV cache (prefill, chunked prefill;
+ * same passage and layout as fp8_kv_cache_append).
+ *   k_new, v_new  [B][T][Hkv][128] bf16 bits (in), token-major as the QKV
+ *                 projection writes them
+ *   start         [B] int32, DEVICE memory: token t of sequence b goes to
+ *                 position start[b] + t; positions outside [0, S) store
+ *                 nothing
+ *   k_cache .. v_scale, mode  as for fp8_kv_cache_append
+ * With T = 1 this is fp8_kv_cache_append.  Sizes: B*T*Hkv < 2^34.
+ */
+fp8q_status fp8_kv_cache_append_tokens(const uint16_t *k_new, const uint16_t *v_new,
+                                       const int32_t *start,
+                                       uint8_t *k_cache, float *k_scale,
+                                       uint8_t *v_cache, float *v_scale,
+                                       int32_t B, int32_t T, int32_t Hkv, int64_t S, int mode,
+                                       void *stream);
+
+/*
+ * FP8 attention for many query tokens (prefill, chunked prefill, a training
+ * forward pass) over the FP8 KV cache (same passage), causal: query t of
+ * sequence b sits at position p = start[b] + t and
+ *   out[b][t][h] = sum_j softmax_j(q[b][t][h] . k[b][g][j] / sqrt(128)) v[b][g][j]
+ * over the cached tokens j <= p, j < S, with g = h / (Hq / Hkv); a query with
+ * no such token gives zeros.  The queries' own keys and values are in the
+ * cache already (fp8_kv_cache_append_tokens first).
+ *   q_q [B][T][Hq][128] E4M3, q_s [B][T][Hq] fp32: query rows in 1x128 blocks
+ *       (fp8_quant_act_1x128 of the projection's [B*T][Hq*128] output)
+ *   k_cache, k_scale, v_cache, v_scale as for fp8_kv_cache_append
+ *   start [B] int32, DEVICE memory
+ *   out [B][T][Hq][128] bf16 bits (out)
+ * q.k runs on the matrix cores in FP8 (E4M3 x E4M3, fp32 accumulation), the
+ * softmax in fp32 (base 2); the weights p_j * v_scale_j are rounded to bf16
+ * (relative error at most 2^-8 each) and multiplied with the exactly decoded
+ * values on the bf16 matrix cores (fp32 accumulation); out is rounded once to
+ * bf16.  Against the exact result the error is at most about
+ * 2^-8 (sum_j p_j |v_j| / sum_j p_j + |out|).
+ * Any Hq that is a multiple of Hkv.  Sizes: ceil(T/64) * B * Hq < 2^31.
+ */
+fp8q_status fp8_attention_prefill(const uint8_t *q_q, const float *q_s,
+                                  const uint8_t *k_cache, const float *k_scale,
+                                  const uint8_t *v_cache, const float *v_scale,
+                                  const int32_t *start, uint16_t *out,
+                                  int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int64_t S,
+                                  void *stream);
+
+/*
  * FP8 decode attention over the FP8 KV cache (same passage): one query token
  * per sequence,
  *   out[b][h] = sum_t softmax_t(q[b][h] . k[b][g][t] / sqrt(128)) * v[b][g][t]
