@@ -777,9 +777,43 @@ def attention(fp8q, synth, torch, dev, reps):
     log(f"attention decode {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s (unsplit {t1 * 1e6:.1f} us); "
         f"8 sequences: split {t8 * 1e6:.1f} us ({nb8 / t8 / 1e9:.0f} GB/s), unsplit {t8u * 1e6:.1f} us; "
         f"cache append {t_app * 1e6:.1f} us")
+    res["prefill"] = prefill(fp8q, torch, dev, g, cache, reps)
     del kq, vq, ks, vs, cache
     torch.cuda.empty_cache()
     return res
+
+
+def prefill(fp8q, torch, dev, g, cache, reps):
+    """FP8 attention for many query tokens, Llama-3.1-8B attention shape: one
+    4096-token sequence prefilled from position 0 (causal: token t sees cache
+    rows 0..t) over the first sequence of the decode cache, 32 query and 8
+    key/value heads.  Matrix-core bound: flops 2*128 for q.k plus 2*128 for
+    p.v per (query, visible key) pair and query head, T(T+1)/2 pairs per
+    head.  Beside it the multi-token append of the 4096 tokens' K and V."""
+    import numpy as np
+    T, Hq, Hkv, D = 4096, 32, 8, 128
+    c1 = tuple(c[:1] for c in cache)
+    q = torch.randn((T * Hq, D), device=dev, generator=g).to(torch.bfloat16)
+    q_q, q_s = fp8q.fp8_quant_act_1x128(q)
+    q_q, q_s = q_q.view(1, T, Hq, D), q_s.view(1, T, Hq)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((1, T, Hq, D), dtype=torch.bfloat16, device=dev)
+    run = lambda: fp8q.fp8_attention_prefill(q_q, q_s, c1, start, out=out)
+    run()
+    t = time_loop(run, reps, torch, label="attention_prefill/llama4096")
+    flops = 4.0 * D * Hq * T * (T + 1) / 2
+    kn = torch.randn((1, T, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    vn = torch.randn((1, T, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    app = lambda: fp8q.fp8_kv_cache_append_tokens(kn, vn, start, c1)
+    app()
+    t_app = time_loop(app, reps, torch, label="attention_prefill/append_tokens")
+    app_bytes = 2 * T * Hkv * (2 * D + D + 4)
+    log(f"attention prefill 4096 tokens: {t * 1e6:.1f} us, {flops / t / 1e12:.1f} TFLOP/s; "
+        f"append of 4096 tokens {t_app * 1e6:.1f} us ({app_bytes / t_app / 1e9:.0f} GB/s)")
+    return {"tokens": T, "q_heads": Hq, "kv_heads": Hkv, "causal": True, "us": round(t * 1e6, 2),
+            "tflops": round(flops / t / 1e12, 1), "frac_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "flops": flops, "append_tokens_us": round(t_app * 1e6, 2),
+            "append_tokens_gbs": round(app_bytes / t_app / 1e9, 1)}
 
 
 def dispatch(fp8q, synth, torch, dev, reps):

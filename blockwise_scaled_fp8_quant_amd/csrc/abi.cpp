@@ -411,8 +411,8 @@ fp8q_status fp8_attention_prefill(const uint8_t *q_q, const float *q_s, const ui
   FP8Q_REQUIRE(B >= 0 && T >= 0 && Hq >= 0 && Hkv >= 0 && S >= 0, FP8Q_EINVAL, "negative size");
   FP8Q_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, FP8Q_ESHAPE, "Hq must be a positive multiple of Hkv");
   if ((int64_t)B * T * Hq == 0) return FP8Q_OK;
-  FP8Q_REQUIRE((int64_t)(T + 63) / 64 * B * Hq < ((int64_t)1 << 31), FP8Q_ESHAPE,
-               "ceil(T/64)*B*Hq must be below 2^31");
+  FP8Q_REQUIRE((int64_t)(T + 63) / 64 * B * Hq < ((int64_t)1 << 31) && S < ((int64_t)1 << 31), FP8Q_ESHAPE,
+               "ceil(T/64)*B*Hq and S must be below 2^31");
   FP8Q_REQUIRE(q_q && q_s && k_cache && k_scale && v_cache && v_scale && start && out, FP8Q_EINVAL,
                "null pointer");
   FP8Q_REQUIRE(aligned16(q_q) && aligned16(q_s) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&

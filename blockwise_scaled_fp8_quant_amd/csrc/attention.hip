@@ -507,18 +507,22 @@ hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, c
 // first).  Queries are token-major, q [B][T][Hq][128] E4M3 with one scale per
 // row, as the QKV projection's quantized output holds them.
 //
-// One workgroup per (sequence, query head, 64 query tokens); its four waves
+// One workgroup per (sequence, query head, 128 query tokens); its eight waves
 // own 16 query tokens each.  Workgroups are ordered longest first (the last
 // query tiles of every head start first).  Per 64-key tile:
 //  - the workgroup stages the tile in LDS: the E4M3 key rows as they are, the
 //    value rows decoded exactly to bf16 (every E4M3 value is a bf16 value) and
-//    transposed to [dim][key], and the 64 key and value scales;
+//    transposed to [dim][key], and the 64 key and value scales; the global
+//    loads of the next tile go out before the math of this one;
 //  - scores S^T = K Q^T on the matrix cores in FP8: one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 keys (the whole head dimension
 //    in one instruction), key rows as A and the wave's query rows as B, so
 //    lane l holds keys 4(l/16)..+3 of query l%16 and every per-query quantity
 //    (running maximum, sum, output column) lives in one lane column;
-//  - online softmax in base 2, one rescale per tile; the weights p * v_scale
+//  - online softmax in base 2; a query's maximum is raised only when a tile
+//    exceeds it by more than 8 (a factor 2^8 in the weights), so the output
+//    rescale is rare; masks only
+//    on tiles that reach past some query's position; the weights p * v_scale
 //    are rounded to bf16 (relative error at most 2^-8 each) and go straight
 //    from the score registers into the B operand of the value product;
 //  - O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, eight per 32 keys (16 dims
@@ -529,9 +533,14 @@ hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, c
 // LDS rows are XOR-swizzled in 16-byte chunks by row so that the 16 lanes
 // reading one chunk of 16 different rows hit different banks.
 // ---------------------------------------------------------------------------
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfQ = 16 * kPfWaves;  // query tokens per workgroup
 constexpr int kPfKeys = 64;          // keys per staged tile
+constexpr int kPfThreads = 64 * kPfWaves;
+// A query's running maximum moves only when a tile's maximum exceeds it by
+// more than this (base 2): weights stay below 2^8 and the rescale of the
+// output, a wave-uniform branch, is rare once the maximum has settled.
+constexpr float kPfLazy = 8.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -545,14 +554,14 @@ struct PrefillArgs {
   const int32_t *start;
   uint16_t *out;
   int32_t B, T, Hq, Hkv;
-  int64_t S;
+  int32_t S;       // below 2^31 (checked by the entry point)
   int32_t qtiles;  // ceil(T / kPfQ)
 };
 
 struct PrefillLds {
   uint8_t k[kPfKeys * kHeadDim];        // key rows, chunk c of row r at c ^ (r & 7)
   uint16_t vt[kHeadDim * kPfKeys];      // V^T bf16: row d, key slot j at chunk (j / 8) ^ (d & 7)
-  float ks[kPfKeys], vs[kPfKeys];
+  float ks[kPfKeys], vs[kPfKeys];       // ks times log2(e) / sqrt(128)
 };
 
 // Slot of key j (0..63) in a V^T row: inside each 32-key half, keys 4q..4q+3
@@ -569,7 +578,11 @@ __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));  // RNE
 }
 
-__global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ int clamp_pos(int64_t p, int32_t S) {  // last key a position may see, -1 for none
+  return p < 0 ? -1 : (p < S ? (int)p : S - 1);
+}
+
+__global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) PrefillLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -582,88 +595,101 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs
   const int64_t st = a.start[b];
   const int t0 = qt * kPfQ;
   const int tlast = (t0 + kPfQ < a.T ? t0 + kPfQ : a.T) - 1;  // last query token of the workgroup
-  // keys [0, kend) can enter any of the workgroup's outputs
-  int64_t kend = st + tlast + 1;
-  kend = kend < a.S ? kend : a.S;
-  const int ntiles = kend > 0 ? (int)((kend + kPfKeys - 1) / kPfKeys) : 0;
+  const int kend = clamp_pos(st + tlast, a.S) + 1;            // keys [0, kend) reach some output
+  const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
 
-  // This lane's query (column l%16 of the wave's 16) and its key limit.
+  // This lane's query (column l%16 of the wave's 16) and the last key it sees.
   const int tq = t0 + 16 * wave + (lane & 15);
   const bool qvalid = tq < a.T;
-  int64_t lim = st + tq;  // last key position it may see
-  lim = lim < a.S - 1 ? lim : a.S - 1;
-  if (!qvalid) lim = -1;
-  // the wave's own last key (uniform): tiles past it hold nothing for the wave
+  const int lim = qvalid ? clamp_pos(st + tq, a.S) : -1;
+  // the wave's last key (uniform): tiles past it hold nothing for the wave
   const int twl = t0 + 16 * wave + 15 < a.T ? t0 + 16 * wave + 15 : a.T - 1;
-  int64_t wlim = st + twl;
-  wlim = wlim < a.S - 1 ? wlim : a.S - 1;
-  if (t0 + 16 * wave >= a.T) wlim = -1;
+  const int wlim = t0 + 16 * wave < a.T ? clamp_pos(st + twl, a.S) : -1;
 
   // Query rows as the B operand: lane l gives query l%16, bytes 32(l/16)..+31.
   v8i_t qf = {0, 0, 0, 0, 0, 0, 0, 0};
-  float qmul = 0.0f;
-  constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
+  float qsc = 0.0f;
   if (qvalid) {
     const int64_t qrow = (b * a.T + tq) * a.Hq + h;
     const uint4 *qp = reinterpret_cast<const uint4 *>(a.qq + qrow * kHeadDim + 32 * (lane >> 4));
     const uint4 x = qp[0], y = qp[1];
     qf[0] = x.x; qf[1] = x.y; qf[2] = x.z; qf[3] = x.w;
     qf[4] = y.x; qf[5] = y.y; qf[6] = y.z; qf[7] = y.w;
-    qmul = a.qs[qrow] * kL2eRsqrtD;
+    qsc = a.qs[qrow];
   }
 
-  const int64_t base = (b * a.Hkv + g) * a.S;  // (b, g, token 0) in the cache
-  const uint8_t *kc = a.kc + base * kHeadDim;
-  const uint8_t *vc = a.vc + base * kHeadDim;
+  const int64_t base = (b * a.Hkv + g) * (int64_t)a.S;  // (b, g, token 0) in the cache
+  // staging roles: key chunk tid (row tid/8, chunk tid%8); values: keys
+  // 4kg..4kg+3 x dims 4d4..4d4+3; scales: thread tid < 128
+  const int kg = tid >> 5, d4 = tid & 31;
+  const uint8_t *kp = a.kc + (base + (tid >> 3)) * kHeadDim + 16 * (tid & 7);
+  const uint8_t *vp = a.vc + (base + 4 * kg) * kHeadDim + 4 * d4;
+  const float *sp = (tid < 64 ? a.ks : a.vs) + base + (tid & 63);
+  constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
+  const float smul = tid < 64 ? kL2eRsqrtD : 1.0f;
+
+  uint4 kreg;
+  uint32_t vreg[4];
+  float sreg = 0.0f;
+  auto fetch = [&](int kt) {
+    const int k0 = kt * kPfKeys;
+    if (k0 + kPfKeys <= a.S) {  // whole tile inside the cache (uniform)
+      kreg = *reinterpret_cast<const uint4 *>(kp + (int64_t)k0 * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vreg[j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)(k0 + j) * kHeadDim);
+      if (tid < 128) sreg = sp[k0];
+    } else {  // last tile: rows past the cache read its last row (masked later)
+      const int r = tid >> 3;
+      const int kk = k0 + r < a.S ? k0 : a.S - 1 - r;
+      kreg = *reinterpret_cast<const uint4 *>(kp + (int64_t)kk * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 4 * kg + j < a.S ? k0 + j : a.S - 1 - 4 * kg;
+        vreg[j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)key * kHeadDim);
+      }
+      if (tid < 128) sreg = sp[k0 + (tid & 63) < a.S ? k0 : a.S - 1 - (tid & 63)];
+    }
+  };
+  auto stage = [&]() {
+    {
+      const int r = tid >> 3, cc = tid & 7;
+      *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = kreg;
+    }
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    float f[4][4];  // [key][dim]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[j], false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[j], true);
+      f[j][0] = lo.x; f[j][1] = lo.y; f[j][2] = hi.x; f[j][3] = hi.y;
+    }
+    const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 4 * d4 + e;
+      uint2 w;
+      w.x = bf16x2_of(f[0][e], f[1][e]);
+      w.y = bf16x2_of(f[2][e], f[3][e]);
+      *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
+    }
+    if (tid < 128) (tid < 64 ? L.ks : L.vs)[tid & 63] = sreg * smul;
+  };
 
   float m_run = -__builtin_inff(), l_run = 0.0f;  // per query (lane column); l_run per lane
   v4f_t acc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
 
+  if (ntiles > 0) fetch(0);
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int64_t k0 = (int64_t)kt * kPfKeys;
+    const int k0 = kt * kPfKeys;
     __syncthreads();  // every wave is done with the previous tile
-    {
-      // key rows: 512 chunks of 16 bytes, two per thread
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i;
-        const int r = c >> 3, cc = c & 7;
-        int64_t key = k0 + r;
-        key = key < a.S ? key : a.S - 1;
-        const uint4 v = *reinterpret_cast<const uint4 *>(kc + key * kHeadDim + 16 * cc);
-        *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = v;
-      }
-      // value rows: thread = 4 keys x 8 dims, decoded to bf16 and transposed
-      const int kg = tid >> 4, d8 = tid & 15;
-      float f[4][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t key = k0 + 4 * kg + j;
-        key = key < a.S ? key : a.S - 1;
-        dec8(*reinterpret_cast<const uint2 *>(vc + key * kHeadDim + 8 * d8), f[j]);
-      }
-      const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * d8 + e;
-        uint2 w;
-        w.x = bf16x2_of(f[0][e], f[1][e]);
-        w.y = bf16x2_of(f[2][e], f[3][e]);
-        *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
-      }
-      if (tid < kPfKeys) {
-        int64_t key = k0 + tid;
-        key = key < a.S ? key : a.S - 1;
-        L.ks[tid] = a.ks[base + key];
-        L.vs[tid] = a.vs[base + key];
-      }
-    }
+    stage();
     __syncthreads();
-    if (k0 > wlim) continue;  // the whole tile lies after the wave's last query
+    if (kt + 1 < ntiles) fetch(kt + 1);  // in flight during this tile's math
+    if (k0 > wlim) continue;             // the whole tile lies after the wave's last query
 
-    // scores of the 64 keys: four MFMAs of 16 keys
+    // scores of the 64 keys (base 2): four MFMAs of 16 keys
     float sc[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -674,14 +700,20 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs
       const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, zero, 0, 0, 0, 127, 0, 127);
       const float4 ksc = *reinterpret_cast<const float4 *>(&L.ks[16 * j + 4 * (lane >> 4)]);
-      const float kv[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = k0 + 16 * j + 4 * (lane >> 4) + i;
-        sc[j][i] = key <= lim ? d[i] * (qmul * kv[i]) : -__builtin_inff();
-      }
+      sc[j][0] = d[0] * (qsc * ksc.x);
+      sc[j][1] = d[1] * (qsc * ksc.y);
+      sc[j][2] = d[2] * (qsc * ksc.z);
+      sc[j][3] = d[3] * (qsc * ksc.w);
     }
-    // online softmax over the tile (the four lanes l, l^16, l^32, l^48 share a query)
+    // keys past a query's position (the diagonal tiles and the cache end)
+    if (__builtin_amdgcn_ballot_w64(k0 + kPfKeys - 1 > lim) != 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * j + 4 * (lane >> 4) + i > lim) sc[j][i] = -__builtin_inff();
+    }
+    // online softmax (the four lanes l, l^16, l^32, l^48 share a query)
     float mt = sc[0][0];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -689,10 +721,16 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs
       for (int i = 0; i < 4; ++i) mt = __builtin_fmaxf(mt, sc[j][i]);
     mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
     mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = __builtin_fmaxf(m_run, mt);
-    const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;  // no key yet: keep everything at 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const bool raise = mt > m_run + kPfLazy;  // false for a tile with no key for this query
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mt : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
     float psum = 0.0f;
     uint32_t pw[2][4];  // bf16 pairs of p * v_scale: [32-key half][k-slot pair]
 #pragma unroll
@@ -713,9 +751,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(PrefillArgs
         pw[hf][2 + i] = bf16x2_of(p[4 + 2 * i] * vsb[2 * i], p[4 + 2 * i + 1] * vsb[2 * i + 1]);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    l_run += psum;
     // O^T += V^T P^T, 32 keys at a time
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -750,9 +786,9 @@ hipError_t launch_attention_prefill(const uint8_t *qq, const float *qs, const ui
                                     int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int64_t S,
                                     hipStream_t stream) {
   if ((int64_t)B * T * Hq == 0) return hipSuccess;
-  PrefillArgs a{qq, qs, kc, ks, vc, vs, start, out, B, T, Hq, Hkv, S, (T + kPfQ - 1) / kPfQ};
+  PrefillArgs a{qq, qs, kc, ks, vc, vs, start, out, B, T, Hq, Hkv, (int32_t)S, (T + kPfQ - 1) / kPfQ};
   const int64_t grid = (int64_t)a.qtiles * B * Hq;
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, a);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -451,7 +451,8 @@ fp8q_status fp8_kv_cache_append_tokens(const uint16_t *k_new, const uint16_t *v_
  * values on the bf16 matrix cores (fp32 accumulation); out is rounded once to
  * bf16.  Against the exact result the error is at most about
  * 2^-8 (sum_j p_j |v_j| / sum_j p_j + |out|).
- * Any Hq that is a multiple of Hkv.  Sizes: ceil(T/64) * B * Hq < 2^31.
+ * Any Hq that is a multiple of Hkv.  Sizes: ceil(T/64) * B * Hq < 2^31 and
+ * S < 2^31 (FP8Q_ESHAPE otherwise).
  */
 fp8q_status fp8_attention_prefill(const uint8_t *q_q, const float *q_s,
                                   const uint8_t *k_cache, const float *k_scale,
