@@ -537,6 +537,7 @@ constexpr int kPfWaves = 8;
 constexpr int kPfQ = 16 * kPfWaves;  // query tokens per workgroup
 constexpr int kPfKeys = 64;          // keys per staged tile
 constexpr int kPfThreads = 64 * kPfWaves;
+static_assert(kPfThreads >= 128 && 512 % kPfThreads == 0, "staging roles");
 // A query's running maximum moves only when a tile's maximum exceeds it by
 // more than this (base 2): weights stay below 2^8 and the rescale of the
 // output, a wave-uniform branch, is rare once the maximum has settled.
@@ -582,7 +583,12 @@ __device__ __forceinline__ int clamp_pos(int64_t p, int32_t S) {  // last key a 
   return p < 0 ? -1 : (p < S ? (int)p : S - 1);
 }
 
-__global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a) {
+// Four waves per SIMD (two workgroups per CU): the register budget this asks
+// for (128) costs a few spills outside the MFMA sequences; measured 220 us at
+// 4096 tokens against 250 us at three waves per SIMD.  With four waves per
+// workgroup the staging work per query doubles (300 us).
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4))) void attn_prefill_kernel(
+    PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) PrefillLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
 
   // Query rows as the B operand: lane l gives query l%16, bytes 32(l/16)..+31.
   v8i_t qf = {0, 0, 0, 0, 0, 0, 0, 0};
-  float qsc = 0.0f;
+  float qsc = 1.0f;  // (a query past T sees no key: its weights are all 0)
   if (qvalid) {
     const int64_t qrow = (b * a.T + tq) * a.Hq + h;
     const uint4 *qp = reinterpret_cast<const uint4 *>(a.qq + qrow * kHeadDim + 32 * (lane >> 4));
@@ -619,58 +625,71 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
   }
 
   const int64_t base = (b * a.Hkv + g) * (int64_t)a.S;  // (b, g, token 0) in the cache
-  // staging roles: key chunk tid (row tid/8, chunk tid%8); values: keys
-  // 4kg..4kg+3 x dims 4d4..4d4+3; scales: thread tid < 128
-  const int kg = tid >> 5, d4 = tid & 31;
+  // Staging roles: the tile is 512 key chunks of 16 bytes (row c/8, chunk
+  // c%8) and 512 value pieces (keys 4kg..4kg+3 x dims 4d4..4d4+3, piece
+  // 32kg + d4), kParts of each per thread; scales: threads below 128.
+  constexpr int kParts = 512 / kPfThreads;
   const uint8_t *kp = a.kc + (base + (tid >> 3)) * kHeadDim + 16 * (tid & 7);
-  const uint8_t *vp = a.vc + (base + 4 * kg) * kHeadDim + 4 * d4;
+  const uint8_t *vp = a.vc + (base + 4 * (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+  constexpr int kStepRows = kPfThreads / 8;  // key rows between a thread's parts (both kinds)
   const float *sp = (tid < 64 ? a.ks : a.vs) + base + (tid & 63);
   constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
   const float smul = tid < 64 ? kL2eRsqrtD : 1.0f;
 
-  uint4 kreg;
-  uint32_t vreg[4];
+  uint4 kreg[kParts];
+  uint32_t vreg[kParts][4];
   float sreg = 0.0f;
   auto fetch = [&](int kt) {
     const int k0 = kt * kPfKeys;
     if (k0 + kPfKeys <= a.S) {  // whole tile inside the cache (uniform)
-      kreg = *reinterpret_cast<const uint4 *>(kp + (int64_t)k0 * kHeadDim);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)(k0 + j) * kHeadDim);
+      for (int u = 0; u < kParts; ++u) {
+        kreg[u] = *reinterpret_cast<const uint4 *>(kp + (int64_t)(k0 + u * kStepRows) * kHeadDim);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vreg[u][j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)(k0 + 4 * u * (kPfThreads / 32) + j) * kHeadDim);
+      }
       if (tid < 128) sreg = sp[k0];
     } else {  // last tile: rows past the cache read its last row (masked later)
-      const int r = tid >> 3;
-      const int kk = k0 + r < a.S ? k0 : a.S - 1 - r;
-      kreg = *reinterpret_cast<const uint4 *>(kp + (int64_t)kk * kHeadDim);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * kg + j < a.S ? k0 + j : a.S - 1 - 4 * kg;
-        vreg[j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)key * kHeadDim);
+      for (int u = 0; u < kParts; ++u) {
+        const int r = (tid >> 3) + u * kStepRows;
+        kreg[u] = *reinterpret_cast<const uint4 *>(kp + (int64_t)(k0 + r < a.S ? k0 + u * kStepRows : a.S - 1 - (tid >> 3)) * kHeadDim);
+        const int kr = 4 * ((tid >> 5) + u * (kPfThreads / 32));  // first key of the piece
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int off = k0 + kr + j < a.S ? k0 + 4 * u * (kPfThreads / 32) + j : a.S - 1 - 4 * (tid >> 5);
+          vreg[u][j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)off * kHeadDim);
+        }
       }
       if (tid < 128) sreg = sp[k0 + (tid & 63) < a.S ? k0 : a.S - 1 - (tid & 63)];
     }
   };
   auto stage = [&]() {
-    {
-      const int r = tid >> 3, cc = tid & 7;
-      *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = kreg;
-    }
     typedef float f2 __attribute__((ext_vector_type(2)));
-    float f[4][4];  // [key][dim]
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[j], false);
-      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[j], true);
-      f[j][0] = lo.x; f[j][1] = lo.y; f[j][2] = hi.x; f[j][3] = hi.y;
-    }
-    const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
+    for (int u = 0; u < kParts; ++u) {
+      {
+        const int r = (tid >> 3) + u * kStepRows, cc = tid & 7;
+        *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = kreg[u];
+      }
+      float f[4][4];  // [key][dim]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 4 * d4 + e;
-      uint2 w;
-      w.x = bf16x2_of(f[0][e], f[1][e]);
-      w.y = bf16x2_of(f[2][e], f[3][e]);
-      *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
+      for (int j = 0; j < 4; ++j) {
+        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[u][j], false);
+        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[u][j], true);
+        f[j][0] = lo.x; f[j][1] = lo.y; f[j][2] = hi.x; f[j][3] = hi.y;
+      }
+      const int kg = (tid >> 5) + u * (kPfThreads / 32), d4 = tid & 31;
+      const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * d4 + e;
+        uint2 w;
+        w.x = bf16x2_of(f[0][e], f[1][e]);
+        w.y = bf16x2_of(f[2][e], f[3][e]);
+        *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
+      }
     }
     if (tid < 128) (tid < 64 ? L.ks : L.vs)[tid & 63] = sreg * smul;
   };
@@ -689,21 +708,36 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
     if (kt + 1 < ntiles) fetch(kt + 1);  // in flight during this tile's math
     if (k0 > wlim) continue;             // the whole tile lies after the wave's last query
 
-    // scores of the 64 keys (base 2): four MFMAs of 16 keys
+    // scores of the 64 keys (base 2): four MFMAs of 16 keys, in two pairs
+    // whose operands are read together, the scaling of one pair after the
+    // MFMAs of the next
     float sc[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * j + (lane & 15);
-      const uint4 x = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4)) ^ (r & 7))]);
-      const uint4 y = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4) + 1) ^ (r & 7))]);
-      const v8i_t kf = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    {
+      auto kread = [&](int j, v8i_t &kf, float4 &ksc) {
+        const int r = 16 * j + (lane & 15);
+        const uint4 x = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4)) ^ (r & 7))]);
+        const uint4 y = *reinterpret_cast<const uint4 *>(&L.k[r * kHeadDim + 16 * ((2 * (lane >> 4) + 1) ^ (r & 7))]);
+        kf = (v8i_t){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        ksc = *reinterpret_cast<const float4 *>(&L.ks[16 * j + 4 * (lane >> 4)]);
+      };
       const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf, zero, 0, 0, 0, 127, 0, 127);
-      const float4 ksc = *reinterpret_cast<const float4 *>(&L.ks[16 * j + 4 * (lane >> 4)]);
-      sc[j][0] = d[0] * (qsc * ksc.x);
-      sc[j][1] = d[1] * (qsc * ksc.y);
-      sc[j][2] = d[2] * (qsc * ksc.z);
-      sc[j][3] = d[3] * (qsc * ksc.w);
+      v8i_t kf[2];
+      float4 ksc[4];
+      v4f_t d[4];
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        kread(2 * pr, kf[0], ksc[2 * pr]);
+        kread(2 * pr + 1, kf[1], ksc[2 * pr + 1]);
+        d[2 * pr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[0], qf, zero, 0, 0, 0, 127, 0, 127);
+        d[2 * pr + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[1], qf, zero, 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[j][0] = d[j][0] * ksc[j].x;  // the query scale (> 0) is applied in the exponent
+        sc[j][1] = d[j][1] * ksc[j].y;
+        sc[j][2] = d[j][2] * ksc[j].z;
+        sc[j][3] = d[j][3] * ksc[j].w;
+      }
     }
     // keys past a query's position (the diagonal tiles and the cache end)
     if (__builtin_amdgcn_ballot_w64(k0 + kPfKeys - 1 > lim) != 0) {
@@ -713,7 +747,8 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
         for (int i = 0; i < 4; ++i)
           if (k0 + 16 * j + 4 * (lane >> 4) + i > lim) sc[j][i] = -__builtin_inff();
     }
-    // online softmax (the four lanes l, l^16, l^32, l^48 share a query)
+    // online softmax (the four lanes l, l^16, l^32, l^48 share a query); the
+    // score is qsc * sc, and qsc > 0, so its maximum is qsc * max(sc)
     float mt = sc[0][0];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -721,6 +756,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
       for (int i = 0; i < 4; ++i) mt = __builtin_fmaxf(mt, sc[j][i]);
     mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
     mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    mt *= qsc;
     const bool raise = mt > m_run + kPfLazy;  // false for a tile with no key for this query
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float m_new = raise ? mt : m_run;
@@ -741,8 +777,8 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
       float p[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(sc[2 * hf][i] - m_use);
-        p[4 + i] = __builtin_amdgcn_exp2f(sc[2 * hf + 1][i] - m_use);
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(qsc, sc[2 * hf][i], -m_use));
+        p[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(qsc, sc[2 * hf + 1][i], -m_use));
         psum += p[i] + p[4 + i];
       }
 #pragma unroll
@@ -752,16 +788,24 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_kernel(PrefillArgs a)
       }
     }
     l_run += psum;
-    // O^T += V^T P^T, 32 keys at a time
+    // O^T += V^T P^T, 32 keys at a time; each value fragment is read two
+    // MFMAs ahead of its use
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, (uint4){pw[hf][0], pw[hf][1], pw[hf][2], pw[hf][3]});
+      const int chunk = 4 * hf + (lane >> 4);
+      auto vread = [&](int db) {
+        const int d = 16 * db + (lane & 15);
+        return *reinterpret_cast<const uint4 *>(&L.vt[d * kPfKeys + 8 * (chunk ^ (d & 7))]);
+      };
+      uint4 vf[3];
+      vf[0] = vread(0);
+      vf[1] = vread(1);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int d = 16 * db + (lane & 15);
-        const int chunk = 4 * hf + (lane >> 4);
-        const uint4 v = *reinterpret_cast<const uint4 *>(&L.vt[d * kPfKeys + 8 * (chunk ^ (d & 7))]);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v), pb, acc[db], 0, 0, 0);
+        if (db + 2 < 8) vf[(db + 2) % 3] = vread(db + 2);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[db % 3]), pb, acc[db], 0, 0,
+                                                          0);
       }
     }
   }

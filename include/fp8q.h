@@ -441,7 +441,8 @@ fp8q_status fp8_kv_cache_append_tokens(const uint16_t *k_new, const uint16_t *v_
  * no such token gives zeros.  The queries' own keys and values are in the
  * cache already (fp8_kv_cache_append_tokens first).
  *   q_q [B][T][Hq][128] E4M3, q_s [B][T][Hq] fp32: query rows in 1x128 blocks
- *       (fp8_quant_act_1x128 of the projection's [B*T][Hq*128] output)
+ *       (fp8_quant_act_1x128 of the projection's [B*T][Hq*128] output); the
+ *       query scales must be positive and finite, as the quantizer makes them
  *   k_cache, k_scale, v_cache, v_scale as for fp8_kv_cache_append
  *   start [B] int32, DEVICE memory
  *   out [B][T][Hq][128] bf16 bits (out)
