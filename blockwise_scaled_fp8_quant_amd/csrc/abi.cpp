@@ -66,8 +66,8 @@ fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t
   FP8Q_REQUIRE(M >= 0 && K >= 0, FP8Q_EINVAL, "negative size");
   FP8Q_REQUIRE(mode == FP8Q_SCALE_AMAX || mode == FP8Q_SCALE_POW2, FP8Q_EINVAL, "unknown scale mode");
   FP8Q_REQUIRE(K > 0 && K % 128 == 0, FP8Q_ESHAPE, "K must be a positive multiple of 128");
-  // four lanes per block: M*K/128 blocks give 4*M*K/128 work-items, below 2^32
-  FP8Q_REQUIRE(M <= (((int64_t)1 << 30) - 1) / (K / 128), FP8Q_ESHAPE, "M*K/128 must be below 2^30");
+  // eight lanes per block: M*K/128 blocks give 8*M*K/128 work-items, below 2^32
+  FP8Q_REQUIRE(M <= (((int64_t)1 << 29) - 1) / (K / 128), FP8Q_ESHAPE, "M*K/128 must be below 2^29");
   if (M == 0) return FP8Q_OK;
   FP8Q_REQUIRE(x && q && scales, FP8Q_EINVAL, "null pointer");
   FP8Q_REQUIRE(aligned16(x) && aligned16(q) && aligned16(scales), FP8Q_EALIGN,

@@ -77,7 +77,7 @@ typedef enum fp8q_scale_mode {
  * Every element: q = E4M3(RN_fp32(x / s)), rounded to nearest with ties to an
  * even mantissa and saturated to +-448; a zero keeps its sign.
  * The result is bit-identical to that rule for every finite input.
- * Sizes: M*K/128 < 2^30 (FP8Q_ESHAPE otherwise; the launch's work-items stay
+ * Sizes: M*K/128 < 2^29 (FP8Q_ESHAPE otherwise; the launch's work-items stay
  * below 2^32).
  */
 fp8q_status fp8_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K,

@@ -137,8 +137,8 @@ def test_launch_size_bounds(lib):
     """Sizes whose launch would exceed a dispatch's 2^32 work-items are refused
     on the host with FP8Q_ESHAPE (checked before any pointer or device)."""
     f = lib.fp8_quant_act_1x128
-    assert f(GOOD, 1 << 23, 1 << 14, GOOD, GOOD, 0, None) == 2                     # M*K/128 = 2^30
-    assert "2^30" in _err(lib)
+    assert f(GOOD, 1 << 22, 1 << 14, GOOD, GOOD, 0, None) == 2                     # M*K/128 = 2^29
+    assert "2^29" in _err(lib)
     a = lib.fp8_attention_decode
     assert a(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 21, 64, 8, 1, None, 0, None) == 2   # B*Hkv = 2^24
     assert "2^24" in _err(lib)
