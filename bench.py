@@ -357,9 +357,10 @@ def small_m(fp8q, layers, torch, dev, reps, M=2048):
             fp8q.fp8_blockscaled_gemm(aq, as_, l["bq"], l["bs"], out=y)
         g()
         t = time_loop(g, reps, torch, label=f"small_m/{l['name']}")
-        big, small = fp8q.fp8_blockscaled_gemm_tile_plan(M, l["N"])  # the library's own choice
+        rows, panels = fp8q.fp8_blockscaled_gemm_tile_plan(M, l["N"])  # the library's own choice
         out[l["name"]] = {"gemm_us": round(t * 1e6, 2), "tflops": round(2.0 * M * l["N"] * l["K"] / t / 1e12, 1),
-                          "panels_on_256_token_tiles": big, "panels_on_128_token_tiles": small}
+                          "tile_plan": {"rows_on_256_token_tiles": rows, "panels_on_256_token_tiles": panels,
+                                        "panels": -(-l["N"] // 256), "tokens": M}}
         log(f"M={M} {l['name']}: {out[l['name']]}")
     return {"tokens": M, "per_layer": out}
 

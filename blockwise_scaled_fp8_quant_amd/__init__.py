@@ -620,11 +620,12 @@ def fp8_moe_permute(expert_ids, E, n_shared=0, out=None, workspace=None):
 
 
 def fp8_blockscaled_gemm_tile_plan(M, N, swiglu=False):
-    """(panels on 256-token tiles, panels on 128-token tiles) of a dense
-    M x N GEMM: how the library splits its output's 256-row weight panels
-    between its two tile shapes (swiglu: for fp8_blockscaled_gemm_swiglu_quant,
-    else for the other dense GEMMs)."""
-    n1 = _lib.load().fp8_blockscaled_gemm_tile_plan(M, N, 1 if swiglu else 0)
+    """(R, P): the tiles of token rows [0, R) and 256-row weight panels [0, P)
+    of a dense M x N GEMM run as 256-token tiles, all others as 128-token tiles
+    (swiglu: for fp8_blockscaled_gemm_swiglu_quant, else for the other dense
+    GEMMs)."""
+    rows = ctypes.c_int64(0)
+    n1 = _lib.load().fp8_blockscaled_gemm_tile_plan(M, N, 1 if swiglu else 0, ctypes.byref(rows))
     if n1 < 0:
         raise ValueError("invalid GEMM size")
-    return n1, -(-N // 256) - n1
+    return rows.value, n1

@@ -75,7 +75,7 @@ def load():
     lib.fp8_attention_prefill.restype = ci
     lib.fp8_attention_decode.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i64, p, i64, p]
     lib.fp8_attention_decode.restype = ci
-    lib.fp8_blockscaled_gemm_tile_plan.argtypes = [i64, i64, ci]
+    lib.fp8_blockscaled_gemm_tile_plan.argtypes = [i64, i64, ci, ctypes.POINTER(ctypes.c_int64)]
     lib.fp8_blockscaled_gemm_tile_plan.restype = i32
     lib.fp8_moe_permute.argtypes = [p, i64, i32, i32, i32, p, p, p, p, i64, p]
     lib.fp8_moe_permute.restype = ci

@@ -459,9 +459,12 @@ fp8q_status fp8_attention_decode(const uint8_t *q_q, const float *q_s, const uin
                   __func__);
 }
 
-int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int swiglu) {
+int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int swiglu, int64_t *rows_large) {
   if (M < 1 || N < 128 || N % 128 != 0 || M > ((int64_t)1 << 31) || N > ((int64_t)1 << 31)) return -1;
-  return (int32_t)fp8q::dense_large_panels(M, N, swiglu == 0);
+  int64_t rows, panels;
+  fp8q::dense_tile_plan(M, N, swiglu == 0, rows, panels);
+  if (rows_large) *rows_large = rows;
+  return (int32_t)panels;
 }
 
 int64_t fp8_moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {

@@ -42,7 +42,9 @@ hipError_t launch_blockscaled_gemm_quant(const uint8_t *a_q, const float *a_s,
 // Weight panels (256 rows each) of a dense M x N GEMM output that run on
 // 256-row tiles; the others run on 128-row tiles (bf16_out: a bf16 output,
 // which may be split between the two shapes).
-int64_t dense_large_panels(int64_t M, int64_t N, bool may_split);
+// Tile plan of a dense M x N output: rows [0, rows_large) x panels
+// [0, panels_large) on 256-token tiles, the rest on 128-token tiles.
+void dense_tile_plan(int64_t M, int64_t N, bool may_split, int64_t &rows_large, int64_t &panels_large);
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const float *a_s,
                                const uint8_t *b_q, const float *b_s,

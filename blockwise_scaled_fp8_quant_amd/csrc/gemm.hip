@@ -1506,31 +1506,56 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Weight panels (256 rows each) of an M x N output that go on 256-row tiles;
-// the rest go on 128-row tiles.  The shape with the shortest estimated time:
-// rounds of tiles over the 256 CUs times a tile's time, a 128-row tile taking
-// about 0.7 of a 256-row one (measured on the Llama shapes).  The output of
-// all but the SwiGLU GEMM may also be split by weight panels: the first n1
-// panels on 256-row tiles, the rest on 128-row tiles, as two launches into
-// column slices of the output (bf16 Y, or the E4M3 codes and their scales).
-// At 4096 tokens QKV's 24 panels make 384 large tiles (two rounds, the second
-// half empty); 16 panels on large tiles (one round) and 8 on small ones (one
-// round) cost 1.7 instead of 2 (measured on the quantized output: 1.09x).  At 2048 tokens QKV's 192 large tiles (one round) beat 384 small
-// ones (+37%), while O and down (128 large tiles, half the CUs idle) take
-// small tiles.
-int64_t dense_large_panels(int64_t M, int64_t N, bool may_split) {
+// Tile plan of an M x N output: the tiles of token rows [0, R) and weight
+// panels (256 rows each) [0, P) run as 256-token tiles, the rest as 128-token
+// tiles.  The plan with the shortest estimated time: rounds of tiles over the
+// 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a 256-row one
+// (measured on the Llama shapes).  Besides all-large (R = M, P = all) and
+// all-small (R = 0), the output of every GEMM but the SwiGLU one may be split
+// in two launches into slices of the output (bf16 Y, or the E4M3 codes and
+// their scales): by weight panels (R = M, P < all) or by token rows (R < M,
+// P = all).  At 4096 tokens QKV's 24 panels make 384 large tiles (two rounds,
+// the second half empty); 16 panels on large tiles (one round) and 8 on small
+// ones (one round) cost 1.7 instead of 2 (measured on the quantized output:
+// 1.09x).  The weight gradient of QKV (6144 rows of dW, 16 panels) splits by
+// rows the same way: 4096 rows on large tiles, 2048 on small ones.  At 2048
+// tokens QKV's 192 large tiles (one round) beat 384 small ones (+37%), while O
+// and down (128 large tiles, half the CUs idle) take small tiles.
+void dense_tile_plan(int64_t M, int64_t N, bool may_split, int64_t &rows_large, int64_t &panels_large) {
   const int64_t tiles_n = (N + kBN - 1) / kBN;
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  auto cost = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
-    return (mt_large * n1 + 255) / 256 * 10 + (mt_small * (tiles_n - n1) + 255) / 256 * 7;
+  auto rounds = [](int64_t tiles) { return (tiles + 255) / 256; };
+  auto cost_n = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
+    return rounds(mt_large * n1) * 10 + rounds(mt_small * (tiles_n - n1)) * 7;
   };
-  int64_t n1 = cost(tiles_n) <= cost(0) ? tiles_n : 0;
+  auto cost_m = [&](int64_t m1) {  // m1 large row tiles (256 rows each), the rest on small ones
+    return rounds(m1 * tiles_n) * 10 + rounds((M - m1 * CfgLarge::kBM + CfgSmall::kBM - 1) / CfgSmall::kBM * tiles_n) * 7;
+  };
+  int64_t best = cost_n(tiles_n), n1 = tiles_n, m1 = -1;
+  if (cost_n(0) < best) {
+    best = cost_n(0);
+    n1 = 0;
+  }
   if (may_split) {
     for (int64_t c = 1; c < tiles_n; ++c)
-      if (cost(c) < cost(n1)) n1 = c;
+      if (cost_n(c) < best) {
+        best = cost_n(c);
+        n1 = c;
+      }
+    for (int64_t r = 1; r * CfgLarge::kBM < M; ++r)
+      if (cost_m(r) < best) {
+        best = cost_m(r);
+        m1 = r;
+      }
   }
-  return n1;
+  if (m1 > 0) {
+    rows_large = m1 * CfgLarge::kBM;
+    panels_large = tiles_n;
+  } else {
+    rows_large = n1 > 0 ? M : 0;
+    panels_large = n1;
+  }
 }
 
 template <bool kPow2, int kOut = kOutBf16, bool kBRow = false, bool kSwiGLU = false>
@@ -1543,10 +1568,30 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N};
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
-  const int64_t n1 = dense_large_panels(M, N, !kSwiGLU);
-  if (n1 == tiles_n) {
+  int64_t rows_large, n1;
+  dense_tile_plan(M, N, !kSwiGLU, rows_large, n1);
+  if (rows_large == M && n1 == tiles_n) {
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
+  }
+  if (rows_large > 0 && rows_large < M) {
+    // token rows [0, rows_large) on 256-row tiles, then the rest on 128-row tiles
+    GemmParams q = p;
+    q.M = rows_large;
+    q.slots_m = rows_large / CfgLarge::kBM;
+    hipError_t e = launch<LargeCfg<V>, V>(q, stream);
+    if (e != hipSuccess) return e;
+    p.a_q = a_q + rows_large * K;
+    p.a_s = a_s + rows_large * (K / kBK);
+    if constexpr (kOut == kOutBf16) {
+      p.y = y + rows_large * p.ldy;
+    } else {
+      p.yq = yq + rows_large * p.ldy;
+      p.ys = ys + rows_large * (p.ldy >> 7);
+    }
+    p.M = M - rows_large;
+    p.slots_m = (p.M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+    return launch<SmallCfg<V>, V>(p, stream);
   }
   if (n1 > 0) {
     // panels [0, n1) on 256-row tiles, then the rest on 128-row tiles

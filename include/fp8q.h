@@ -551,13 +551,17 @@ fp8q_status fp8_attention_decode_noalloc(const uint8_t *q_q, const float *q_s,
                                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
                                          void *stream);
 
-/* Informational: how many 256-row weight panels of an M x N dense GEMM
- * output run on 256-token x 256 tiles; the other ceil(N/256) - that many run
- * on 128-token tiles.  swiglu = 0 for fp8_blockscaled_gemm and its pow2,
- * weight-gradient and quantized-output variants (their output may be split
- * between the two tile heights), 1 for fp8_blockscaled_gemm_swiglu_quant (all
- * panels on one height).  -1 for invalid sizes.  No device access. */
-int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int swiglu);
+/* Informational: the tile plan of an M x N dense GEMM output.  The tiles of
+ * token rows [0, R) and 256-row weight panels [0, P) run as 256-token x 256
+ * tiles, every other tile as a 128-token x 256 tile.  Returns P and, when
+ * rows_large is not NULL, stores R there: R = M and P = ceil(N/256) for all
+ * large tiles, R = 0 and P = 0 for all small ones, R = M with a smaller P for a
+ * split by weight panels, R < M with all panels for a split by token rows.
+ * swiglu = 0 for fp8_blockscaled_gemm and its pow2, weight-gradient and
+ * quantized-output variants (their output may be split), 1 for
+ * fp8_blockscaled_gemm_swiglu_quant (one tile height).  -1 for invalid sizes.
+ * No device access. */
+int32_t fp8_blockscaled_gemm_tile_plan(int64_t M, int64_t N, int swiglu, int64_t *rows_large);
 
 /* Static English text of a status code (never NULL). */
 const char *fp8q_status_string(int status);

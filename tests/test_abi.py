@@ -261,14 +261,24 @@ def test_noalloc_scratch_covers_every_split():
 
 
 def test_gemm_tile_plan(lib):
-    """Weight panels on 256-token tiles: all of them for gate+up and down at 4096
-    tokens, 16 of QKV's 24 (one round on each shape), none for O at 2048
-    tokens; the SwiGLU GEMM's output is not split."""
+    """Tile plans: all 256-token tiles for gate+up and down at 4096 tokens; QKV
+    split by weight panels (16 of 24 large, one round on each shape); the
+    weight gradient of QKV (dW 6144 x 4096) split by rows (4096 large); all
+    small tiles for O at 2048 tokens; the SwiGLU GEMM's output is not split."""
+    import ctypes
     f = lib.fp8_blockscaled_gemm_tile_plan
-    assert f(4096, 28672, 0) == 112 and f(4096, 4096, 0) == 16
-    assert f(4096, 6144, 0) == 16 and f(4096, 6144, 1) in (0, 24)
-    assert f(2048, 4096, 0) == 0
-    assert f(0, 128, 0) == -1 and f(64, 100, 0) == -1
+
+    def plan(M, N, swiglu=0):
+        r = ctypes.c_int64(-7)
+        p = f(M, N, swiglu, ctypes.byref(r))
+        return r.value, p
+    assert plan(4096, 28672) == (4096, 112) and plan(4096, 4096) == (4096, 16)
+    assert plan(4096, 6144) == (4096, 16)
+    assert plan(4096, 6144, 1) in ((0, 0), (4096, 24))
+    assert plan(6144, 4096) == (4096, 16)
+    assert plan(2048, 4096) == (0, 0)
+    assert f(4096, 6144, 0, None) == 16
+    assert f(0, 128, 0, None) == -1 and f(64, 100, 0, None) == -1
 
 
 def test_moe_permute_argument_errors(lib):

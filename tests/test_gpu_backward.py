@@ -206,12 +206,14 @@ def test_wgrad_exact_integer_products(pow2_scales):
     assert np.array_equal(host_bf16_as_f64(y), ref)
 
 
-@pytest.mark.parametrize("layer", [1, 3])
+@pytest.mark.parametrize("layer", [0, 1, 3])
 def test_llama_backward_full_size_sampled(layer):
-    """Full-size Llama-3.1-8B-shaped O (4096x4096) and down (4096x14336)
-    layers at 4096 tokens: dY ~ N(0, 1e-3), quantized on the GPU in both
-    layouts (checked bit for bit on sampled rows against the oracle), then
-    dgrad and wgrad checked on sampled outputs against the fp64 oracle."""
+    """Full-size Llama-3.1-8B-shaped QKV (6144x4096), O (4096x4096) and down
+    (4096x14336) layers at 4096 tokens: dY ~ N(0, 1e-3), quantized on the GPU
+    in both layouts (checked bit for bit on sampled rows against the oracle),
+    then dgrad and wgrad checked on sampled outputs against the fp64 oracle,
+    with rows on both sides of a split tile plan (QKV's weight gradient runs
+    rows 0..4095 on 256-row tiles and 4096..6143 on 128-row tiles)."""
     require_gpu()
     fp8q = lib()
     name, N, K = synth.LLAMA_LAYERS[layer]
@@ -236,7 +238,9 @@ def test_llama_backward_full_size_sampled(layer):
     ms, ks = rng.integers(0, M, 400), rng.integers(0, K, 400)
     ref = oracle.gemm_dgrad_sampled_f64(hgq, hgs, hwq, hws, ms, ks)
     gemm_tolerance_check(dx.float().cpu().numpy().astype(np.float64)[ms, ks], ref, f"{name} dgrad sampled")
-    ns, ks = rng.integers(0, N, 400), rng.integers(0, K, 400)
+    edge = np.array([0, 4095, 4096, N - 1])
+    ns = np.concatenate([rng.integers(0, N, 400), np.repeat(edge[edge < N], 8)])
+    ks = rng.integers(0, K, ns.size)
     ref = oracle.gemm_wgrad_sampled_f64(host_u8(gtq), host_f32(gts), host_u8(xtq), host_f32(xts), ns, ks)
     gemm_tolerance_check(dw.float().cpu().numpy().astype(np.float64)[ns, ks], ref, f"{name} wgrad sampled")
 

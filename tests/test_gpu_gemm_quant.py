@@ -109,10 +109,10 @@ def test_fused_llama_qkv_panel_split(mode):
     # scales.  Whole output, bit for bit against quantizing the bf16 output.
     require_gpu()
     M, N, K = 4096, 6144, 4096
-    big, small = lib().fp8_blockscaled_gemm_tile_plan(M, N)
-    assert big > 0 and small > 0, (big, small)
+    rows, big = lib().fp8_blockscaled_gemm_tile_plan(M, N)
+    assert rows == M and 0 < big < N // 256, (rows, big)
     aq, as_, bq, bs = _operands(M, N, K, seed=43 + mode)
-    say("gemm_quant qkv split", M, N, K, MODES[mode], big, small)
+    say("gemm_quant qkv split", M, N, K, MODES[mode], rows, big)
     q, s, ybits = _run(aq, as_, bq, bs, mode)
     q_ref, s_ref = oracle.quant_act_1x128(ybits, mode)
     assert_bytes_equal(q, q_ref, "qkv bytes")
