@@ -147,9 +147,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=64,
                     help="tokens per layer in the oracle's single-thread CPU-baseline sample")
-    ap.add_argument("--sections", default="pow2,fused,norm,backward,recal,moe,dispatch,attention,smallm,bf16,cpu",
+    ap.add_argument("--sections",
+                    default="pow2,fused,norm,backward,recal,moe,dispatch,attention,smallm,bf16,power,cpu",
                     help="extra measurements after the step (comma list of pow2, fused, norm, backward, recal, "
-                         "moe, dispatch, attention, smallm, bf16, cpu)")
+                         "moe, dispatch, attention, smallm, bf16, power, cpu)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the step (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -338,6 +339,8 @@ def main():
         result["small_m"] = small_m(fp8q, layers, torch, dev, reps)
     if "bf16" in sections:
         result["bf16_reference"] = bf16_compare(layers, torch, M, reps, gemm_tflops)
+    if "power" in sections:
+        result["power"] = power_under_load(fp8q, layers, torch, step_flops)
     if "cpu" in sections:
         result["cpu_baseline"] = cpu_baseline(layers, synth, M, args.cpu_rows)
     result["timing_stats"] = STATS
@@ -952,6 +955,106 @@ def _cpu_model():
     except (OSError, ValueError):
         pass
     return None
+
+
+def power_under_load(fp8q, layers, torch, step_flops, seconds=2.0, period=0.02):
+    """GPU socket power while the step runs back to back for about two
+    seconds, sampled every 20 ms through amdsmi (read-only queries) on the
+    device the step runs on (matched by PCI bus), beside the idle power just
+    before.  Reported unavailable, with the reason, when amdsmi cannot read
+    it.  The step rate of this loop (50 steps between synchronizations, after
+    20 more warm-up steps) is reported with it; it is not the headline
+    figure."""
+    import threading
+    try:
+        import amdsmi
+    except ImportError as e:
+        return {"available": False, "reason": f"amdsmi not importable: {e}"}
+    try:
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+    except Exception as e:  # noqa: BLE001 - any failure means no reading
+        return {"available": False, "reason": f"amdsmi_init: {e}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = (getattr(props, "pci_domain_id", None), getattr(props, "pci_bus_id", None))
+        handle = None
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+            dom, bus = int(bdf.split(":")[0], 16), int(bdf.split(":")[1], 16)
+            if (dom, bus) == want:
+                handle = h
+        if handle is None and len(handles) == 1:
+            handle = handles[0]
+        if handle is None:
+            return {"available": False, "reason": f"no amdsmi device matches PCI {want} among {len(handles)}"}
+
+        def read():
+            info = amdsmi.amdsmi_get_power_info(handle)
+            for key in ("current_socket_power", "average_socket_power", "socket_power"):
+                v = info.get(key)
+                if isinstance(v, (int, float)) and v > 0:
+                    return float(v), key
+            return None, None
+
+        first, key = read()
+        if first is None:
+            return {"available": False, "reason": "amdsmi reports no socket power for this device"}
+        idle = []
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            idle.append(read()[0])
+            time.sleep(period)
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                samples.append(read()[0])
+                time.sleep(period)
+
+        def step():
+            for l in layers:
+                fp8q.fp8_quant_act_1x128(l["x"], out=(l["aq"], l["as_"]))
+                fp8q.fp8_blockscaled_gemm(l["aq"], l["as_"], l["bq"], l["bs"], out=l["y"])
+        for _ in range(20):  # reach the loaded clock and power state first
+            step()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll, daemon=True)
+        Ev = torch.cuda.Event
+        start, end = Ev(enable_timing=True), Ev(enable_timing=True)
+        n, t0 = 0, time.perf_counter()
+        th.start()
+        start.record()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                step()
+            n += 50
+            torch.cuda.synchronize()
+        end.record()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        samples = [v for v in samples if v is not None]
+        idle = [v for v in idle if v is not None]
+        t_step = start.elapsed_time(end) / 1e3 / n
+        avg = sum(samples) / len(samples) if samples else None
+        tflops = step_flops / t_step / 1e12
+        res = {"available": True, "quantity": key, "unit": "W",
+               "workload": "the step (act quant + GEMM, 4 Llama layers) back to back, 50 steps per sync",
+               "seconds": round(time.perf_counter() - t0, 2), "steps": n, "samples": len(samples),
+               "avg_w": round(avg, 1) if avg else None, "max_w": round(max(samples), 1) if samples else None,
+               "idle_w": round(sum(idle) / len(idle), 1) if idle else None,
+               "loop_tflops": round(tflops, 1), "tflops_per_w": round(tflops / avg, 3) if avg else None}
+        log(f"power under load: {res['avg_w']} W average ({res['max_w']} max, {res['idle_w']} idle), "
+            f"{tflops:.1f} TFLOP/s in this loop, {res['tflops_per_w']} TFLOP/s per W")
+        return res
+    except Exception as e:  # noqa: BLE001 - a failed reading must not stop the benchmark
+        return {"available": False, "reason": f"{type(e).__name__}: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
 
 
 def cpu_baseline(layers, synth, M, one_thread_rows):
