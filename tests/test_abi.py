@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
               "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
-              "fp8_kv_cache_append",
+              "fp8_kv_cache_append", "fp8_kv_cache_append_tokens", "fp8_attention_prefill",
+              "fp8_moe_permute", "fp8_blockscaled_gemm_tile_plan",
               "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
         assert n in names
 
@@ -208,6 +209,30 @@ def test_kv_cache_append_argument_errors(lib):
     assert f(GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, 2, 8, 64, 0, None) == 1     # null positions
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, GOOD, GOOD, 2, 8, 64, 1, None) == 3      # misaligned
     assert f(None, None, None, None, None, None, None, 0, 8, 64, 0, None) == 0     # empty call
+
+
+def test_kv_cache_append_tokens_argument_errors(lib):
+    f = lib.fp8_kv_cache_append_tokens
+    #        k_new v_new start kc    ks    vc    vs    B  T   H  S   mode
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 16, 8, 64, 3, None) == 1     # unknown mode
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, -1, 8, 64, 0, None) == 1     # negative T
+    assert f(GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, 2, 16, 8, 64, 0, None) == 1     # null start
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, ODD, GOOD, 2, 16, 8, 64, 1, None) == 3      # misaligned
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 20, 1 << 12, 8, 64, 0, None) == 2   # B*T*H = 2^35
+    assert f(None, None, None, None, None, None, None, 2, 0, 8, 64, 0, None) == 0     # no tokens
+
+
+def test_attention_prefill_argument_errors(lib):
+    f = lib.fp8_attention_prefill
+    #        qq    qs    kc    ks    vc    vs    start out   B  T   Hq  Hkv S
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 32, 6, 128, None) == 2     # Hq % Hkv
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 32, 0, 128, None) == 2     # Hkv = 0
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, -1, 32, 8, 128, None) == 1     # negative T
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 32, 8, 1 << 31, None) == 2  # S = 2^31
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 20, 1 << 16, 32, 8, 128, None) == 2  # grid
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 2, 64, 32, 8, 128, None) == 1     # null start
+    assert f(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 32, 8, 128, None) == 3      # misaligned out
+    assert f(None, None, None, None, None, None, None, None, 2, 0, 32, 8, 128, None) == 0      # no queries
 
 
 def test_attention_decode_argument_errors(lib):
