@@ -117,12 +117,20 @@ struct TileCfg {
   static constexpr int kOffSB = kOffSA + kBytesSA;
   static constexpr int kStageBytes = (kOffSB + kBytesSB + 1023) / 1024 * 1024;
   static constexpr int kLdsBytes = kStageBytes * kStages;
+  // Scale chunks of the per-row-scale variant (issue_chunk_quarter): the
+  // activation scales and the per-row weight-side scales of four K blocks,
+  // double-buffered after the stages.
+  static constexpr int kChunkSA = kBM * 16;
+  static constexpr int kChunkBytes = kChunkSA + kBN * 16;
+  static constexpr int kOffChunk = kStageBytes * kStages;
+  static constexpr int kLdsBytesChunked = kOffChunk + 2 * kChunkBytes;
   static constexpr int kPiecesB = kBytesB / 1024 / kLoaders;  // 1 KB DMA pieces per loader wave
   static constexpr int kPiecesA = kBytesA / 1024 / kLoaders;
   static constexpr int kPieces = kPiecesB + kPiecesA;         // operand pieces per loader wave
   static constexpr int kScaleLoaders = kBM / 64;              // loaders 0.. each fetch 64 activation scales
   static_assert(kScaleLoaders <= kLoaders && kBM % 64 == 0, "activation scales: one per lane");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kStages == 2, "the DMA wait before a block's barrier is vmcnt(0): two stages");
+  static_assert(kLdsBytesChunked <= 160 * 1024, "LDS budget");
 };
 
 // 256 x 256 tiles: on the ping-pong schedule (gemm_main_pp) when the
@@ -158,6 +166,107 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ sw
 __device__ __forceinline__ int sa_row_of_pos(int p) {
   const int wm = p >> 6, j = (p & 63) >> 2, mi = p & 3;
   return wm * 64 + mi * 16 + j;
+}
+
+// Scale chunks (the per-row-scale variant, 1x128 blocks on both operands).
+// Both scale vectors are stored one row per token or weight-side row with the
+// K blocks contiguous, so a 64-lane 4-byte load of one K block (one row per
+// lane) touches 64 cache lines, and a CU's memory path pays per line.  With
+// two such vectors per stage that cost the weight-gradient GEMM 10-28% of
+// its time (measured against the same loads made contiguous, wrong values).
+// Instead a chunk holds the scales of K blocks 4c .. 4c+3 and a load
+// instruction covers 16 rows x 4 blocks (lane l: row slot t = l % 16, block
+// l / 16), 16 cache lines: Llama weight gradients 8-11% faster with
+// VALU-folded scales, 10-23% with power-of-two ones.  In LDS the 64 words of instruction i sit
+// at [i][block][t].  Chunk c lives in buffer c % 2; the stage of block 0
+// loads chunk 0 whole, and the stage of block kn >= 1 loads quarter
+// (kn - 1) % 4 of chunk (kn - 1) / 4 + 1, so chunk c is complete with the
+// stage of block 4c, and the previous chunk in its buffer (c - 2) was last
+// read in block 4c - 5, before the stage of block 4c - 3 is issued.  (For
+// the other variants, with one such vector and a scale per weight tile,
+// chunks measured 1-2% slower than one load per block, and 5-8% slower with
+// gathered rows, whose row offsets per chunk quarter take registers.)
+constexpr int kScChunk = 4;
+
+// Row of slot t in instruction i of a chunk, per scale vector.  Activation
+// (token-side) scales: lane j of a wave reads its four token rows wm*64 +
+// mi*16 + j (mi = 0..3) of one block as four consecutive words.
+__host__ __device__ constexpr int sa_chunk_row(int i, int t) {
+  return (i >> 2) * 64 + (t & 3) * 16 + 4 * (i & 3) + (t >> 2);
+}
+// Per-row weight-side scales folded by the VALU: row order, so the four rows
+// of a lane's outputs (16ni + 4(l/16) + r) are consecutive.
+__host__ __device__ constexpr int sbf_chunk_row(int i, int t) { return 16 * i + t; }
+// Per-row power-of-two weight-side scales: the eight rows a lane supplies to
+// the eight A sub-tiles of its wave (128w + 16s + c, c = l % 16) are
+// consecutive.
+__host__ __device__ constexpr int sbp_chunk_row(int i, int t) {
+  return 128 * (i >> 3) + 16 * (t & 7) + 2 * (i & 7) + (t >> 3);
+}
+// Every row of the tile exactly once per chunk.
+template <int (*kRow)(int, int)>
+constexpr bool chunk_covers(int rows) {
+  int seen[256] = {};
+  for (int i = 0; i < rows / 16; ++i)
+    for (int t = 0; t < 16; ++t) {
+      const int r = kRow(i, t);
+      if (r < 0 || r >= rows || seen[r]) return false;
+      seen[r] = 1;
+    }
+  return true;
+}
+static_assert(chunk_covers<sa_chunk_row>(256) && chunk_covers<sa_chunk_row>(128) &&
+                  chunk_covers<sbf_chunk_row>(256) && chunk_covers<sbp_chunk_row>(256),
+              "scale chunk rows");
+
+// The chunk and quarter that the stage of block kn >= 1 loads.
+__device__ __forceinline__ int chunk_of_stage(int kn) { return ((kn - 1) >> 2) + 1; }
+__device__ __forceinline__ int quarter_of_stage(int kn) { return (kn - 1) & 3; }
+
+// LDS byte offset of block k's scales in its chunk buffer ((k/4) % 2, block
+// k % 4), and the words a lane reads there: its four token rows (16 bytes);
+// the four rows of weight sub-tile row ni of its outputs (VALU fold, 16
+// bytes); the eight rows it supplies to the A sub-tiles (power-of-two, 32
+// bytes).
+template <class C>
+__device__ __forceinline__ int chunk_base(int k) {
+  return C::kOffChunk + ((k >> 2) & 1) * C::kChunkBytes + (k & 3) * 64;
+}
+template <class C>
+__device__ __forceinline__ const float4 *sa_chunk_ptr(const uint8_t *lds, int k, int wm, int lane) {
+  const int j = lane & 15;
+  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + (wm * 4 + (j >> 2)) * 256 + 16 * (j & 3));
+}
+template <class C>
+__device__ __forceinline__ const float4 *sbf_chunk_ptr(const uint8_t *lds, int k, int wn, int ni, int lane) {
+  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 8 + ni) * 256 +
+                                          16 * (lane >> 4));
+}
+template <class C>
+__device__ __forceinline__ const float4 *sbp_chunk_ptr(const uint8_t *lds, int k, int wn, int lane) {
+  const int c = lane & 15;
+  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 8 + (c >> 1)) * 256 +
+                                          32 * (c & 1));
+}
+
+// This lane's index, computed where it is used.  The asm statement cannot be
+// hoisted out of a loop, so the chunk-load offsets derived from it are
+// recomputed at each stage (a few VALU operations) instead of being held
+// through the main loop, where the register allocator spilled them (and the
+// wait for a spill reload, vmcnt(0), also waits for the DMA already issued).
+__device__ __forceinline__ uint32_t lane_id_now() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Byte offset of this lane's word in chunk 0 of a scale vector whose
+// instruction i (uniform) maps row slots by kRow: row slot lane % 16, K block
+// lane / 16.
+template <int (*kRow)(int, int)>
+__device__ __forceinline__ uint32_t chunk_lane_off(int i, int KB) {
+  const uint32_t ln = lane_id_now();
+  return (uint32_t)(kRow(i, (int)(ln & 15u)) * KB + (int)(ln >> 4)) * 4u;
 }
 
 struct TileJob {
@@ -202,16 +311,25 @@ __device__ __forceinline__ TileRsrc make_rsrc(const TileJob &t) {
 // lane's offset is only (row in piece)*K + chunk.  (The raw-buffer bound does
 // not cover the scalar offset operand, which is why the row offset goes into
 // the base rather than there.)
+//
+// kScalar: write the clamp so that it stays in scalar instructions.  As
+// min(max(.)), the compiler folds it into one v_med3_i32 and keeps the
+// per-piece bounds in vector registers; in the per-row-scale variant these
+// were spilled (its in-loop reloads then wait for all vector-memory
+// operations, the DMA included).  The other variants keep the fold: with the
+// scalar form their register allocation spilled more.
+template <bool kScalar = false>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t piece_rsrc(const uint8_t *rows, int valid_rows, int64_t K,
                                                               int piece, uint32_t kbyte) {
   int nr = valid_rows - 8 * piece;
-  nr = nr < 0 ? 0 : (nr > 8 ? 8 : nr);
+  if (!kScalar) nr = nr < 0 ? 0 : nr;
+  nr = nr > 8 ? 8 : nr;
   const uint64_t base = (uint64_t)(uintptr_t)(rows + (int64_t)(8 * piece) * K + kbyte);
   // Uniform by construction; readfirstlane tells the compiler so (it would
   // otherwise wrap each load in a loop over distinct resource values).
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(nr * (int)K);
+  const int n = __builtin_amdgcn_readfirstlane(kScalar ? (nr > 0 ? nr * (int)K : 0) : nr * (int)K);
   return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, kRsrcWord3);
 }
 
@@ -238,8 +356,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gather_rsrc(const uint8_t *a, 
 // which holds logical chunk c = (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (p%2).
 struct DmaLane {
   uint32_t rc[2];  // (row in piece)*K + chunk offset, even / odd pieces
-  uint32_t sa;     // activation-scale row of this lane (lanes 0..31)
-  uint32_t sb;     // weight-scale row (lanes 0..1; per-row scales: row lane of each 64)
+  // Scale rows (not the per-row variant, whose chunk loads recompute theirs):
+  uint32_t sa;     // activation-scale row of this lane
+  uint32_t sb;     // weight tile's 128-row block of this lane (lanes 0..1)
   // Gathered token rows: this lane's byte offset in the token matrix for each
   // of its loader's token pieces, and of its scale row; kGatherOOB for a row
   // past the tile or an index outside [0, T), which then reads zeros.
@@ -258,12 +377,7 @@ __device__ __forceinline__ DmaLane dma_lane(const TileJob &t, int wave, int lane
   for (int par = 0; par < 2; ++par) d.rc[par] = row * K + ((c0 ^ par) << 4);
   const int l = wave - C::kFirstLoader;  // meaningful for loader waves only
   d.sa = (uint32_t)sa_row_of_pos((l % C::kScaleLoaders) * 64 + lane) * (uint32_t)t.KB * 4u;
-  // Weight-side scales.  Tile scales: rows of the two 128-row blocks (lanes
-  // 0..1).  Per-row scales, VALU fold: row order (lane of each 64).  Per-row
-  // power-of-two scales: LDS slot 128w + 8c + i holds row 128w + 16i + c, so
-  // that a lane reads the rows it supplies to the eight MFMA sub-tiles with
-  // two 16-byte reads; loader j fills slots 64j .. 64j+63.
-  d.sb = (uint32_t)(!V::kBRow ? (lane & 1) : (V::kPow2 ? (lane & 7) * 16 + (lane >> 3) : lane)) * (uint32_t)t.KB * 4u;
+  d.sb = (uint32_t)(lane & 1) * (uint32_t)t.KB * 4u;
   if constexpr (kGather) {
     static_assert(C::kPiecesA <= kMaxPiecesA, "gather offsets per lane");
     auto src = [&](int r) -> int64_t {  // source token row of tile row r, or -1
@@ -297,7 +411,7 @@ __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, 
   const int l = wave - C::kFirstLoader;  // loader index
   if (q < C::kPiecesB) {
     const int piece = l * C::kPiecesB + q;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.b_q, t.n_valid, t.K, piece, kbyte),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc<V::kBRow>(t.b_q, t.n_valid, t.K, piece, kbyte),
                                              (lds_void_t *)(buf + piece * 1024), 16, d.rc[piece & 1], 0, 0, 0);
   } else {
     const int piece = l * C::kPiecesA + (q - C::kPiecesB);
@@ -306,55 +420,68 @@ __device__ __forceinline__ void issue_piece(const TileJob &t, const DmaLane &d, 
                                                (lds_void_t *)(buf + C::kOffA + piece * 1024), 16,
                                                d.ga[q - C::kPiecesB], 0, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc(t.a_q, t.m_valid, t.K, piece, kbyte),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(piece_rsrc<V::kBRow>(t.a_q, t.m_valid, t.K, piece, kbyte),
                                                (lds_void_t *)(buf + C::kOffA + piece * 1024), 16, d.rc[piece & 1],
                                                0, 0, 0);
   }
 }
 
-// Number of vector-memory instructions a wave issues for one stage.
-// Weight-side scale loads of loader l: with tile scales one 2-lane load on
-// the first loader; with per-row scales kBN/64 loads of 64 rows, load j on
-// loader (kScaleLoaders + j) % kLoaders.
+// Quarter q of scale chunk c (per-row variant): loader l's activation-scale
+// instruction (loaders 0 .. kScaleLoaders-1, instruction q*kScaleLoaders + l)
+// and its per-row weight-side one (instruction 4q + j on loader
+// (kScaleLoaders + j) % kLoaders), into chunk buffer c % 2 after lds.
 template <class C, class V>
-__host__ __device__ constexpr int sb_loads(int l) {
-  if (!V::kBRow) return l == 0 ? 1 : 0;
-  int n = 0;
-  for (int j = 0; j < kBN / 64; ++j) n += ((C::kScaleLoaders + j) % C::kLoaders == l) ? 1 : 0;
-  return n;
+__device__ __forceinline__ void issue_chunk_quarter(const TileRsrc &rs, int KB, uint8_t *lds, int c, int q, int l) {
+  static_assert(kBN / 64 <= C::kLoaders, "one weight-side chunk load per loader and stage");
+  uint8_t *cb = lds + C::kOffChunk + (c & 1) * C::kChunkBytes;
+  const uint32_t kb = (uint32_t)c * 16u;  // bytes of blocks 0 .. 4c-1 in a scale row
+  if (l < C::kScaleLoaders) {
+    const int i = q * C::kScaleLoaders + l;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(cb + i * 256), 4,
+                                             chunk_lane_off<sa_chunk_row>(i, KB) + kb, 0, 0, 0);
+  }
+  const int j = (l - C::kScaleLoaders + C::kLoaders) % C::kLoaders;
+  if (j < kBN / 64) {
+    const int i = q * 4 + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(cb + C::kChunkSA + i * 256), 4,
+                                             chunk_lane_off<V::kPow2 ? sbp_chunk_row : sbf_chunk_row>(i, KB) + kb,
+                                             0, 0, 0);
+  }
 }
 
-template <class C, class V>
-__host__ __device__ constexpr int loads_per_stage(int l) {
-  return C::kPieces + (l < C::kScaleLoaders ? 1 : 0) + sb_loads<C, V>(l);
-}
-
+// The scale loads of the stage of block k (buf: its stage buffer): one
+// 64-lane activation-scale load on each of the first kScaleLoaders loaders
+// and the weight tile's two block scales (lanes 0..1 of loader 0); with
+// per-row weight-side scales, the chunk quarter the stage carries (first:
+// block 0's stage, all of chunk 0; a literal at every call, so the branch
+// folds away once inlined).
 template <class C, class V>
 __device__ __forceinline__ void issue_scales(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
-                                             uint8_t *buf, int wave, int lane) {
+                                             uint8_t *buf, int wave, int lane, bool first) {
   const int l = wave - C::kFirstLoader;
-  if (l < C::kScaleLoaders)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
-                                             (V::kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
   if constexpr (V::kBRow) {
-    // LDS slots 64j .. 64j+63 of the weight-side scales (row order, or the
-    // power-of-two layout described at dma_lane)
+    uint8_t *lds = buf - (k & 1) * C::kStageBytes;  // block k's stage is buffer k % 2
+    if (first) {
 #pragma unroll
-    for (int j = 0; j < kBN / 64; ++j) {
-      const int row0 = V::kPow2 ? (j >> 1) * 128 + (j & 1) * 8 : j * 64;
-      if ((C::kScaleLoaders + j) % C::kLoaders == l)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB + j * 256), 4,
-                                                 d.sb + (uint32_t)(row0 * t.KB * 4) + (uint32_t)k * 4u, 0, 0, 0);
+      for (int q = 0; q < kScChunk; ++q) issue_chunk_quarter<C, V>(rs, t.KB, lds, 0, q, l);
+    } else {
+      issue_chunk_quarter<C, V>(rs, t.KB, lds, chunk_of_stage(k), quarter_of_stage(k), l);
     }
-  } else if (l == 0 && lane < 2)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
-                                             0, 0, 0);
+  } else {
+    if (l < C::kScaleLoaders)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void_t *)(buf + C::kOffSA + l * 256), 4,
+                                               (V::kGather ? d.gsa : d.sa) + (uint32_t)k * 4u, 0, 0, 0);
+    if (l == 0 && lane < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(buf + C::kOffSB), 4, d.sb + (uint32_t)k * 4u,
+                                               0, 0, 0);
+  }
 }
 
+// The DMA of block k's stage (first: block 0's, issued before the main loop).
 template <class C, class V>
 __device__ __forceinline__ void issue_stage(const TileJob &t, const TileRsrc &rs, const DmaLane &d, int k,
-                                            uint8_t *buf, int wave, int lane) {
-  issue_scales<C, V>(t, rs, d, k, buf, wave, lane);
+                                            uint8_t *buf, int wave, int lane, bool first) {
+  issue_scales<C, V>(t, rs, d, k, buf, wave, lane, first);
 #pragma unroll
   for (int q = 0; q < C::kPieces; ++q) issue_piece<C, V>(t, d, k, buf, wave, q);
 }
@@ -435,17 +562,23 @@ struct HeadRaw {
 // steps: the LDS reads (first weight sub-tile, scale words), then the scale
 // arithmetic (combined per-lane scales, or E8M0 bytes), which can wait until
 // the reads have landed without holding up other work.
+// buf: block k's stage buffer; lds, k: where the per-row variant finds the
+// block's scales (its chunk buffer).
 template <class C, class V>
-__device__ __forceinline__ void read_head(const uint8_t *buf, int wn, int wm, int lane, BlockFrags &f, HeadRaw &h) {
+__device__ __forceinline__ void read_head(const uint8_t *buf, const uint8_t *lds, int k, int wn, int wm, int lane,
+                                          BlockFrags &f, HeadRaw &h) {
 #pragma unroll
   for (int a = 0; a < C::kWAhead; ++a) f.wf[a] = frag(buf, wn * C::kWaveN + a * 16, lane);
-  h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
+  if constexpr (V::kBRow)
+    h.sa4 = *sa_chunk_ptr<C>(lds, k, wm, lane);
+  else
+    h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   if constexpr (V::kPow2 && V::kBRow) {
     static_assert(C::kWaveN == 128, "per-row power-of-two weight scales: 128 weight rows per wave");
-    const float4 *rp = reinterpret_cast<const float4 *>(buf + C::kOffSB + (wn * 128 + (lane & 15) * 8) * 4);
+    const float4 *rp = sbp_chunk_ptr<C>(lds, k, wn, lane);
     h.lo = rp[0];
     h.hi = rp[1];
-  } else {
+  } else if constexpr (!V::kBRow) {
     h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + ((wn * C::kWaveN) >> 7) * 4);  // the wave's 128-row block
   }
 }
@@ -479,11 +612,12 @@ __device__ __forceinline__ void finish_head(const HeadRaw &h, BlockFrags &f) {
   }
 }
 
+// Block 0's fragments and scales (its stage is buffer 0, at the LDS base).
 template <class C, class V>
 __device__ __forceinline__ void load_block(const uint8_t *buf, int wave, int wn, int wm, int lane,
                                            BlockFrags &f) {
   HeadRaw h;
-  read_head<C, V>(buf, wn, wm, lane, f, h);
+  read_head<C, V>(buf, buf, 0, wn, wm, lane, f, h);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) f.xf[mi] = frag(buf + C::kOffA, wm * 64 + mi * 16, lane);
   finish_head<V>(h, f);
@@ -570,9 +704,9 @@ __device__ __forceinline__ void pin(v4f &v) { asm volatile("" : "+v"(v)); }
 // which issues them after the barrier, between the LDS reads of the next
 // block's token fragments.
 template <class C, class V, int kJEnd>
-__device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, const BlockFrags &f,
-                                          v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], float4 (&sbq)[2],
-                                          const StageDma &dma, v8i &wlast) {
+__device__ __forceinline__ void mma_steps(const uint8_t *tb, const uint8_t *lds, int k, int wn, int lane,
+                                          const BlockFrags &f, v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing],
+                                          float4 (&sbq)[2], const StageDma &dma, v8i &wlast) {
   constexpr bool kPow2 = V::kPow2;
   // per-row weight scales with VALU folds hold the most registers; issuing
   // their DMA mid-block made the compiler spill inside the loop
@@ -593,9 +727,9 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
       __builtin_amdgcn_sched_barrier(0);
       if (ni + kWAhead < C::kSubN) wf[(ni + kWAhead) % R] = frag(tb, wn * C::kWaveN + (ni + kWAhead) * 16, lane);
       if constexpr (V::kBRow)
-        sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
+        sbq[ni & 1] = *sbf_chunk_ptr<C>(lds, k, wn, ni, lane);
       if (ni == kDmaStep && dma.on && dma.wave >= C::kFirstLoader)
-        issue_stage<C, V>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane);
+        issue_stage<C, V>(*dma.t, *dma.rs, *dma.d, dma.k, dma.buf, dma.wave, dma.lane, false);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kPow2) {
@@ -630,7 +764,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, int wn, int lane, c
     // the row scales of the deferred last row (its slot's previous row has
     // had all its folds by now)
     constexpr int ni = kJEnd / kSubM;
-    sbq[ni & 1] = *reinterpret_cast<const float4 *>(tb + C::kOffSB + (wn * 128 + ni * 16 + 4 * (lane >> 4)) * 4);
+    sbq[ni & 1] = *sbf_chunk_ptr<C>(lds, k, wn, ni, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -694,38 +828,11 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
-// Wait until the DMA of block kk has landed in every wave's view: at most the
-// later blocks already issued (kk+1 .. kk+kStages-2) may still be in flight.
-// vmcnt wait for loader l (each loader's own count of loads per stage).
-template <class C, class V, int L = 0>
-__device__ __forceinline__ void wait_loader(int l) {
-  constexpr int n = C::kStages - 2;
-  if constexpr (L + 1 < C::kLoaders) {
-    if (l == L)
-      wait_vmcnt<loads_per_stage<C, V>(L) * n>();
-    else
-      wait_loader<C, V, L + 1>(l);
-  } else {
-    wait_vmcnt<loads_per_stage<C, V>(L) * n>();
-  }
-}
-
-template <class C, class V>
-__device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
-  constexpr int n = C::kStages - 2;  // stages issued after block kk's
-  const int l = wave - C::kFirstLoader;
-  if (n > 0 && kk + n < KB && l >= 0) {
-    if constexpr (V::kBRow)
-      wait_loader<C, V>(l);
-    else if (l == 0)
-      wait_vmcnt<loads_per_stage<C, V>(0) * n>();
-    else if (l < C::kScaleLoaders)
-      wait_vmcnt<loads_per_stage<C, V>(1) * n>();
-    else
-      wait_vmcnt<loads_per_stage<C, V>(C::kScaleLoaders) * n>();
-  } else {
-    wait_vmcnt<0>();
-  }
+// Wait until the DMA of block kk has landed in every wave's view, then meet
+// at the barrier.  With two stages nothing later than block kk has been
+// issued when a wave arrives here, so the wait is for all of its loads.
+__device__ __forceinline__ void wait_block() {
+  wait_vmcnt<0>();
   barrier_nofence();
 }
 
@@ -737,18 +844,18 @@ __device__ __forceinline__ void wait_block(int kk, int KB, int wave) {
 // read of block k has landed before this wave arrives at the barrier (after
 // which the DMA of block k+2 may overwrite block k's buffer).
 template <class C, class V>
-__device__ __forceinline__ void block_boundary(const uint8_t *nbuf, int knext, int KB, int wave, int wn, int wm,
-                                               int lane, BlockFrags &f, const v8i &wlast,
+__device__ __forceinline__ void block_boundary(const uint8_t *nbuf, const uint8_t *lds, int knext, int KB, int wave,
+                                               int wn, int wm, int lane, BlockFrags &f, const v8i &wlast,
                                                v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing], const float4 (&sbq)[2]) {
   constexpr bool kPow2 = V::kPow2;
   constexpr int ni = C::kSubN - 1;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  wait_block<C, V>(knext, KB, wave);
+  wait_block();
   __builtin_amdgcn_sched_barrier(0);
   BlockFrags g;
   g.bad = f.bad;
   HeadRaw h;
-  read_head<C, V>(nbuf, wn, wm, lane, g, h);
+  read_head<C, V>(nbuf, lds, knext, wn, wm, lane, g, h);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) {
@@ -1294,9 +1401,9 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s)
     if (s < KB && wave >= C::kFirstLoader)
-      issue_stage<C, V>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane);
+      issue_stage<C, V>(t, rs, dl, s, lds + s * C::kStageBytes, wave, lane, true);
 
-  wait_block<C, V>(0, KB, wave);
+  wait_block();
   BlockFrags f;
   f.bad = 0;
   load_block<C, V>(lds, wave, wn, wm, lane, f);
@@ -1308,17 +1415,18 @@ __device__ __forceinline__ void gemm_tile(const TileJob &t, const TileOut &o, in
                C::kStages - 1 < KB};
   v8i wlast;
   for (int k = 0; k + 1 < KB; ++k) {
-    mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+    mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, lds, k, wn, lane, f, acc, p, sbq, dma, wlast);
     // Block k's buffer is free once every wave is past the barrier in
     // block_boundary; block k + kStages goes into it during the next block.
     dma.k = k + C::kStages;
     dma.buf = lds + cur * C::kStageBytes;
     dma.on = k + C::kStages < KB;
     cur = (cur + 1 == C::kStages) ? 0 : cur + 1;
-    block_boundary<C, V>(lds + cur * C::kStageBytes, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
+    block_boundary<C, V>(lds + cur * C::kStageBytes, lds, k + 1, KB, wave, wn, wm, lane, f, wlast, acc, p, sbq);
   }
   // the last block: its last row's MFMAs and the trailing folds, no barrier
-  mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, wn, lane, f, acc, p, sbq, dma, wlast);
+  mma_steps<C, V, C::kMfma - kSubM>(lds + cur * C::kStageBytes, lds, KB - 1, wn, lane, f, acc, p, sbq, dma,
+                                    wlast);
 #pragma unroll
   for (int mi = 0; mi < kSubM; ++mi) {
     const int j = C::kMfma - kSubM + mi;
@@ -1485,24 +1593,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 }
 
 template <class C, class V>
+constexpr int lds_bytes() {
+  return V::kBRow ? C::kLdsBytesChunked : C::kLdsBytes;
+}
+
+template <class C, class V>
 static hipError_t launch(GemmParams p, hipStream_t stream) {
   // The LDS size above the default limit is an attribute of the kernel on the
   // current device: set once per device (std::call_once, so concurrent first
   // calls from several host threads are safe), and the outcome kept.
   static std::once_flag once[kMaxDevices];
   static hipError_t attr_err[kMaxDevices];
+  constexpr int kLds = lds_bytes<C, V>();
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(once[dev], [dev]() {
     attr_err[dev] = hipFuncSetAttribute((const void *)gemm_kernel<C, V>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   });
   if (attr_err[dev] != hipSuccess) return attr_err[dev];
   const int64_t grid = p.slots_m * p.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<C, V>), dim3((unsigned)grid), dim3(C::kThreads),
-                     C::kLdsBytes, stream, p);
+                     kLds, stream, p);
   return hipGetLastError();
 }
 
