@@ -87,9 +87,12 @@ struct TileCfg {
   static constexpr int kStages = kStages_;
   // The n step of a K block at which the waves issue the DMA of the next
   // block.  Issuing it mid-block keeps its LDS writes away from the fragment
-  // reads that start each block.  256-row tiles (8 waves): step 4, +8% (amax)
-  // and +12% (power-of-two) on the dense Llama shapes against step 0; at step
-  // 5 and later the DMA is not finished when the block ends.  128-row tiles
+  // reads that start each block.  256-row tiles (8 waves, lockstep loop):
+  // step 3.  Against step 0 steps 2-4 gain 5-8% on the dense Llama shapes; at
+  // step 5 and later the DMA is not finished when the block ends.  Step 3
+  // against 4: dense +1-2%, grouped MoE GEMMs +1-10% (Qwen3 down +10%, gathered
+  // rows +4-6%), whose tiles' operands miss in L2 more often, so the DMA needs
+  // the extra step to land.  128-row tiles
   // (4 waves, one per SIMD, so each K block takes longer per wave): step 5
   // with two stages, +22% against three stages and step 0.
   // The last kLoaders waves issue the stage DMA.
@@ -143,7 +146,7 @@ struct TileCfg {
 // such a stall; in ping-pong it is reading LDS, so the folds cost 10% more
 // (Llama gate+up and down).  Without folds the ping-pong loop is 3-6% ahead.
 using CfgLarge = TileCfg<256, 8, 2, 8, 0, 1, 2, true>;
-using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 4>;
+using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 3>;
 using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
 // 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD) for
 // bf16 outputs without per-row weight scales, whose epilogues do not need a
@@ -708,9 +711,8 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, const uint8_t *lds,
                                           const BlockFrags &f, v4f (&acc)[kSubN][kSubM], v4f (&p)[kRing],
                                           float4 (&sbq)[2], const StageDma &dma, v8i &wlast) {
   constexpr bool kPow2 = V::kPow2;
-  // per-row weight scales with VALU folds hold the most registers; issuing
-  // their DMA mid-block made the compiler spill inside the loop
-  constexpr int kDmaStep = (V::kBRow && !kPow2) ? 0 : C::kDmaStep;
+  // per-row power-of-two weight-side scales: step 4 measured 2% ahead of 3
+  constexpr int kDmaStep = (V::kBRow && kPow2 && C::kBM == 256) ? 4 : C::kDmaStep;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int kWAhead = C::kWAhead;
   static_assert(kWAhead >= 1 && kWAhead <= kMaxWAhead, "weight read-ahead");
