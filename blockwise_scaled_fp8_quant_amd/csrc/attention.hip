@@ -559,9 +559,9 @@ hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, c
 // own 16 query tokens each.  Workgroups are ordered longest first (the last
 // query tiles of every head start first).  Per 64-key tile:
 //  - the workgroup stages the tile in LDS: the E4M3 key rows as they are, the
-//    value rows decoded exactly to bf16 (every E4M3 value is a bf16 value) and
-//    transposed to [dim][key], and the 64 key and value scales; the global
-//    loads of the next tile go out before the math of this one;
+//    value rows decoded exactly to bf16 (every E4M3 value is a bf16 value),
+//    row-major, and the 64 key and value scales; the global loads of the next
+//    tile go out before the math of this one;
 //  - scores S^T = K Q^T on the matrix cores in FP8: one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16 keys (the whole head dimension
 //    in one instruction), key rows as A and the wave's query rows as B, so
@@ -577,9 +577,13 @@ hipError_t launch_attention_decode_noalloc(const uint8_t *qq, const float *qs, c
 //    each), fp32 accumulation: lane l holds dims 4(l/16)..+3 of each 16-dim
 //    block for query l%16.  The MFMA's k slots of lane group q are keys
 //    4q..4q+3 and 16+4q..16+4q+3 of the 32 (the keys whose scores that lane
-//    group holds); V^T is stored with its keys in that order.
-// LDS rows are XOR-swizzled in 16-byte chunks by row so that the 16 lanes
-// reading one chunk of 16 different rows hit different banks.
+//    group holds).  The V^T operand comes from the row-major value tile by
+//    LDS transpose loads (ds_read_b64_tr_b16, two per MFMA), so the staging
+//    writes whole rows instead of scattering a transpose.
+// Key rows in LDS are XOR-swizzled in 16-byte chunks by row so that the 16
+// lanes reading one chunk of 16 different rows hit different banks; value
+// rows are padded by 32 bytes so that the eight rows a half-wave's transpose
+// load touches start in different banks.
 // ---------------------------------------------------------------------------
 constexpr int kPfWaves = 8;
 constexpr int kPfQ = 16 * kPfWaves;  // query tokens per workgroup
@@ -607,17 +611,25 @@ struct PrefillArgs {
   int32_t qtiles;  // ceil(T / kPfQ)
 };
 
+constexpr int kPfVRow = kHeadDim + 16;  // bf16 per value row in LDS (32 bytes of padding)
+
 struct PrefillLds {
   uint8_t k[kPfKeys * kHeadDim];        // key rows, chunk c of row r at c ^ (r & 7)
-  uint16_t vt[kHeadDim * kPfKeys];      // V^T bf16: row d, key slot j at chunk (j / 8) ^ (d & 7)
+  uint16_t v[kPfKeys * kPfVRow];        // value rows, bf16, row-major
   float ks[kPfKeys], vs[kPfKeys];       // ks times log2(e) / sqrt(128)
 };
 
-// Slot of key j (0..63) in a V^T row: inside each 32-key half, keys 4q..4q+3
-// go to slots 8q..8q+3 and keys 16+4q..16+4q+3 to slots 8q+4..8q+7.
-__device__ __forceinline__ int vt_slot(int j) {
-  const int half = j & 32, k = j & 31;
-  return half + (k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// Transpose load of 16-bit elements (ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane 4j + (i / 4) names an 8-byte window of four elements and
+// lane i receives, as its element j, element i % 4 of that window (checked on
+// gfx950 with distinct values).  So if lane r of a group names row key(r / 4),
+// columns c0 + 4 (r % 4) .. +3 of a row-major tile, lane i receives column
+// c0 + i of rows key(0) .. key(3).
+__device__ __forceinline__ v4s_t lds_read_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t *)(__attribute__((address_space(3))) void *)p);
 }
 
 __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
@@ -673,19 +685,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
   }
 
   const int64_t base = (b * a.Hkv + g) * (int64_t)a.S;  // (b, g, token 0) in the cache
-  // Staging roles: the tile is 512 key chunks of 16 bytes (row c/8, chunk
-  // c%8) and 512 value pieces (keys 4kg..4kg+3 x dims 4d4..4d4+3, piece
-  // 32kg + d4), kParts of each per thread; scales: threads below 128.
+  // Staging roles: the key and the value tile are 512 chunks of 16 bytes each
+  // (row c/8, chunk c%8), kParts of each per thread; scales: threads below 128.
   constexpr int kParts = 512 / kPfThreads;
   const uint8_t *kp = a.kc + (base + (tid >> 3)) * kHeadDim + 16 * (tid & 7);
-  const uint8_t *vp = a.vc + (base + 4 * (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+  const uint8_t *vp = a.vc + (base + (tid >> 3)) * kHeadDim + 16 * (tid & 7);
   constexpr int kStepRows = kPfThreads / 8;  // key rows between a thread's parts (both kinds)
   const float *sp = (tid < 64 ? a.ks : a.vs) + base + (tid & 63);
   constexpr float kL2eRsqrtD = 1.4426950408889634f * 0.08838834764831845f;
   const float smul = tid < 64 ? kL2eRsqrtD : 1.0f;
 
-  uint4 kreg[kParts];
-  uint32_t vreg[kParts][4];
+  uint4 kreg[kParts], vreg[kParts];
   float sreg = 0.0f;
   auto fetch = [&](int kt) {
     const int k0 = kt * kPfKeys;
@@ -693,22 +703,16 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int u = 0; u < kParts; ++u) {
         kreg[u] = *reinterpret_cast<const uint4 *>(kp + (int64_t)(k0 + u * kStepRows) * kHeadDim);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[u][j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)(k0 + 4 * u * (kPfThreads / 32) + j) * kHeadDim);
+        vreg[u] = *reinterpret_cast<const uint4 *>(vp + (int64_t)(k0 + u * kStepRows) * kHeadDim);
       }
       if (tid < 128) sreg = sp[k0];
     } else {  // last tile: rows past the cache read its last row (masked later)
 #pragma unroll
       for (int u = 0; u < kParts; ++u) {
         const int r = (tid >> 3) + u * kStepRows;
-        kreg[u] = *reinterpret_cast<const uint4 *>(kp + (int64_t)(k0 + r < a.S ? k0 + u * kStepRows : a.S - 1 - (tid >> 3)) * kHeadDim);
-        const int kr = 4 * ((tid >> 5) + u * (kPfThreads / 32));  // first key of the piece
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int off = k0 + kr + j < a.S ? k0 + 4 * u * (kPfThreads / 32) + j : a.S - 1 - 4 * (tid >> 5);
-          vreg[u][j] = *reinterpret_cast<const uint32_t *>(vp + (int64_t)off * kHeadDim);
-        }
+        const int64_t off = (int64_t)(k0 + r < a.S ? k0 + u * kStepRows : a.S - 1 - (tid >> 3)) * kHeadDim;
+        kreg[u] = *reinterpret_cast<const uint4 *>(kp + off);
+        vreg[u] = *reinterpret_cast<const uint4 *>(vp + off);
       }
       if (tid < 128) sreg = sp[k0 + (tid & 63) < a.S ? k0 : a.S - 1 - (tid & 63)];
     }
@@ -717,27 +721,21 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int u = 0; u < kParts; ++u) {
-      {
-        const int r = (tid >> 3) + u * kStepRows, cc = tid & 7;
-        *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = kreg[u];
-      }
-      float f[4][4];  // [key][dim]
+      const int r = (tid >> 3) + u * kStepRows, cc = tid & 7;
+      *reinterpret_cast<uint4 *>(&L.k[r * kHeadDim + 16 * (cc ^ (r & 7))]) = kreg[u];
+      // value dims 16cc .. 16cc+15 of key r, decoded exactly to bf16
+      uint32_t w[8];
+      const uint32_t x[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[u][j], false);
-        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vreg[u][j], true);
-        f[j][0] = lo.x; f[j][1] = lo.y; f[j][2] = hi.x; f[j][3] = hi.y;
+        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[j], false);
+        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[j], true);
+        w[2 * j] = bf16x2_of(lo.x, lo.y);
+        w[2 * j + 1] = bf16x2_of(hi.x, hi.y);
       }
-      const int kg = (tid >> 5) + u * (kPfThreads / 32), d4 = tid & 31;
-      const int slot = vt_slot(4 * kg);  // keys 4kg..4kg+3 take 4 consecutive slots
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 4 * d4 + e;
-        uint2 w;
-        w.x = bf16x2_of(f[0][e], f[1][e]);
-        w.y = bf16x2_of(f[2][e], f[3][e]);
-        *reinterpret_cast<uint2 *>(&L.vt[d * kPfKeys + 8 * ((slot >> 3) ^ (d & 7)) + (slot & 7)]) = w;
-      }
+      uint4 *vd = reinterpret_cast<uint4 *>(&L.v[r * kPfVRow + 16 * cc]);
+      vd[0] = (uint4){w[0], w[1], w[2], w[3]};
+      vd[1] = (uint4){w[4], w[5], w[6], w[7]};
     }
     if (tid < 128) (tid < 64 ? L.ks : L.vs)[tid & 63] = sreg * smul;
   };
@@ -837,14 +835,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
     l_run += psum;
     // O^T += V^T P^T, 32 keys at a time; each value fragment is read two
-    // MFMAs ahead of its use
+    // MFMAs ahead of its use.  Fragment (hf, db): lane (q = l/16, i = l%16)
+    // needs dim 16db + i of keys 32hf + 4q + j and 32hf + 16 + 4q + j
+    // (j = 0..3), two transpose loads in which lane r of group q names key
+    // 32hf + 4q + r/4 (+16), dims 16db + 4(r%4) .. +3.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, (uint4){pw[hf][0], pw[hf][1], pw[hf][2], pw[hf][3]});
-      const int chunk = 4 * hf + (lane >> 4);
+      const uint16_t *vrow = &L.v[(32 * hf + 4 * (lane >> 4) + ((lane >> 2) & 3)) * kPfVRow + 4 * (lane & 3)];
       auto vread = [&](int db) {
-        const int d = 16 * db + (lane & 15);
-        return *reinterpret_cast<const uint4 *>(&L.vt[d * kPfKeys + 8 * (chunk ^ (d & 7))]);
+        const v4s_t lo = lds_read_tr16(vrow + 16 * db);
+        const v4s_t hi = lds_read_tr16(vrow + 16 * kPfVRow + 16 * db);
+        return (uint4){__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
       };
       uint4 vf[3];
       vf[0] = vread(0);
