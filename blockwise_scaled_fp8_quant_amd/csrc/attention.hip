@@ -256,14 +256,33 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
 
   const int tg = lane >> 4;  // token group of the value pass
   const int dq = lane & 15;  // 8-dim slice of the value pass
-  for (int tile = tile_begin + wave; tile < tile_end; tile += kAttnWaves) {
+  // A tile's key rows (this lane's part of the four 16-token MFMA operands)
+  // and its 64 key and value scales (one per lane: one load instruction each;
+  // a vector-memory instruction costs the same whatever its width).  They are
+  // loaded one tile ahead: the next tile's go out as soon as this tile's score
+  // MFMAs have read theirs, and land during the softmax and the value pass.
+  // Rows past len read row len-1 (masked in the scores).
+  uint4 kx[4], ky[4];
+  float ks_l = 0.0f, vs_l = 0.0f;
+  auto load_keys = [&](int tile) {
     const int64_t t0 = (int64_t)tile * kTileTok;
-    // the tile's 64 key and value scales, one per lane (one load instruction
-    // each; a vector-memory instruction costs the same whatever its width)
     int64_t ts = t0 + lane;
     ts = ts < len ? ts : len - 1;
-    const float ks_l = ksc[ts], vs_l = vsc[ts];
-    // value rows of this lane (issued first: not needed until after the softmax)
+    ks_l = ksc[ts];
+    vs_l = vsc[ts];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t t = t0 + 16 * j + (lane & 15);
+      t = t < len ? t : len - 1;
+      const uint4 *kp = reinterpret_cast<const uint4 *>(kc + t * kHeadDim + 32 * (lane >> 4));
+      kx[j] = kp[0];
+      ky[j] = kp[1];
+    }
+  };
+  if (tile_begin + wave < tile_end) load_keys(tile_begin + wave);
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kAttnWaves) {
+    const int64_t t0 = (int64_t)tile * kTileTok;
+    // value rows of this lane (not needed until after the softmax)
     uint2 vb[16];
     float vsl[4];
 #pragma unroll
@@ -276,11 +295,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
     float sc[4][kRowsPerLane];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int64_t t = t0 + 16 * j + (lane & 15);
-      const bool valid = t < len;
-      t = valid ? t : len - 1;
-      const uint4 *kp = reinterpret_cast<const uint4 *>(kc + t * kHeadDim + 32 * (lane >> 4));
-      const uint4 x = kp[0], y = kp[1];
+      const bool valid = t0 + 16 * j + (lane & 15) < len;
+      const uint4 x = kx[j], y = ky[j];
       const v8i_t kf = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
       const float kscale = __shfl(ks_l, 16 * j + (lane & 15));
       vsl[j] = __shfl(vs_l, 16 * j + (lane & 15));
@@ -289,6 +305,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_decode_kernel(AttnArgs a
 #pragma unroll
       for (int r = 0; r < kRowsPerLane; ++r) sc[j][r] = valid ? d[r] * (qmul[r] * kscale) : -__builtin_inff();
     }
+    // the next tile's keys and scales (their registers are free once the
+    // MFMAs above have read them); the asm statements keep the loads here.
+    // After the wave's last tile they reload this tile's rows (cache hits):
+    // under a branch, the wait counts after it would have to assume the loads
+    // absent and wait for them in the value pass.
+    asm volatile("" ::: "memory");
+    load_keys(tile + kAttnWaves < tile_end ? tile + kAttnWaves : tile);
+    asm volatile("" ::: "memory");
     // online softmax per head
     float alpha[GRP];
 #pragma unroll
