@@ -1580,12 +1580,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     o.yq = p.yq + m0 * p.ldy + n0;
     o.ys = p.ys + m0 * (p.ldy >> 7) + (n0 >> 7);
   }
-  if constexpr (kGrouped && C::kBM == 256 && kOut == kOutBf16 && V::kPow2 && !V::kBRow) {
+  if constexpr (kGrouped && C::kBM == 256 && kOut == kOutBf16 && !V::kBRow) {
     // A group's last slot with at most 128 rows runs as a 128-row tile (same
     // eight waves): about half the padding of a 256-row tile, at ~0.7 of its
-    // time (Qwen3 routing: padding rows 23% -> 12% of the rows; +2% on its
-    // gate+up GEMM).  Power-of-two scales only: in the amax kernel the second
-    // tile body raises the lockstep loop's spills and costs 1.5-2.5%.
+    // time (Qwen3 routing: padding rows 23% -> 12% of the rows).  Measured:
+    // Qwen3 gate+up +2% (pow2), amax grouped GEMMs +1-6% (Moonlight down
+    // -1.5%), gathered rows +1.5-3%.
     if (t.m_valid <= CfgSmall8::kBM) {
       gemm_tile<CfgSmall8, V>(t, o, p.ldy, lds);
       return;
