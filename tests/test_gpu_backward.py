@@ -147,11 +147,14 @@ def test_dgrad(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,rows", [(1, 128, 128, None), (300, 256, 384, None), (128, 640, 256, None),
-                                        (1000, 384, 512, None), (700, 256, 128, 200)])
+                                        (1000, 384, 512, None), (700, 256, 128, 200), (1200, 256, 384, None)])
 def test_wgrad(M, N, K, rows):
     """dW [N, K] = dY^T X over Mp = 128*ceil(M/128) tokens (the ragged tail's
     padding codes are zeros); rows = 200 keeps the first 200 dY^T rows, which
-    leaves a partial tile of dW rows."""
+    leaves a partial tile of dW rows.  The kernel loads both scale vectors in
+    chunks of four 128-token blocks, two chunk buffers in turn: 1, 3, 6, 8 and
+    10 blocks cover a lone partial chunk, a partial second one, two whole ones
+    and a third chunk that reuses the first one's buffer."""
     require_gpu()
     fp8q = lib()
     ops = _grad_operands(M, N, K, 3 * M + N + K)
@@ -245,7 +248,8 @@ def test_llama_backward_full_size_sampled(layer):
     gemm_tolerance_check(dw.float().cpu().numpy().astype(np.float64)[ns, ks], ref, f"{name} wgrad sampled")
 
 
-@pytest.mark.parametrize("M,N,K,rows", [(300, 256, 384, None), (128, 640, 256, None), (700, 256, 128, 200)])
+@pytest.mark.parametrize("M,N,K,rows", [(300, 256, 384, None), (128, 640, 256, None), (700, 256, 128, 200),
+                                        (1200, 256, 384, None)])
 def test_wgrad_pow2(M, N, K, rows):
     """Power-of-two scales applied by the matrix cores (per-row E8M0 on both
     operands) against the oracle."""
