@@ -114,14 +114,18 @@ def _stat(label, mean_s, durs_us):
                     "n": n}
 
 
-def time_loop(fn, reps, torch, label=None):
+def time_loop(fn, reps, torch, label=None, warmup=2):
     """Average duration (s) of fn() over reps back-to-back launches, HIP events
-    on the current stream (the stream the library enqueues on).  With a label,
-    a second loop brackets every launch with its own events and its median and
-    minimum go to STATS beside this mean (the per-launch event records add
-    gaps between launches, so the mean comes from the first loop only)."""
+    on the current stream (the stream the library enqueues on), after warmup
+    untimed calls (a kernel's first launch in the process also loads its code
+    and sets its attributes).  With a label, a second loop brackets every
+    launch with its own events and its median and minimum go to STATS beside
+    this mean (the per-launch event records add gaps between launches, so the
+    mean comes from the first loop only)."""
     Ev = torch.cuda.Event
     start, end = Ev(enable_timing=True), Ev(enable_timing=True)
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     start.record()
     for _ in range(reps):
