@@ -1485,6 +1485,20 @@ __device__ __forceinline__ void raster(int64_t L, int64_t slots_m, int64_t tiles
   tn = n0 + (r - tm * gw);
 }
 
+// The second region of a dense launch with two tile shapes: an M x N block of
+// the output (a column slice or a band of rows) on 128-row tiles, with its
+// operands' and output's origins.
+struct GemmRegion {
+  const uint8_t *a_q;
+  const float *a_s;
+  const uint8_t *b_q;
+  const float *b_s;
+  uint16_t *y;
+  int64_t M, N;
+  int64_t slots_m;
+  int32_t tiles_n;
+};
+
 struct GemmParams {
   const uint8_t *a_q;
   const float *a_s;
@@ -1502,6 +1516,11 @@ struct GemmParams {
   int32_t G;
   int32_t tiles_n;
   int64_t ldy;  // row stride of y (bf16 output): N, or the full width for a column slice
+  // Dense bf16 output with two tile shapes in one launch: workgroups
+  // [0, wgs_large) take the 256-row tiles described above, the rest the
+  // 128-row tiles of `small`.  0: one shape.
+  int64_t wgs_large;
+  GemmRegion small;
 };
 
 __device__ __forceinline__ int64_t clamp_off(const int32_t *off, int32_t g, int64_t M) {
@@ -1550,7 +1569,34 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   constexpr bool kGather = V::kGather;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  if constexpr (!kGrouped && C::kBM == 256 && kOut == kOutBf16 && !V::kBRow && !V::kSwiGLU) {
+    if (p.wgs_large > 0 && (int64_t)blockIdx.x >= p.wgs_large) {
+      // The workgroups are dispatched in order, so the 128-row tiles fill
+      // the CUs as the 256-row ones finish (no launch boundary between the
+      // two shapes).
+      const GemmRegion &r = p.small;
+      const int64_t Ls = xcd_remap(blockIdx.x - p.wgs_large, gridDim.x - p.wgs_large);
+      int64_t sm, sn;
+      raster(Ls, r.slots_m, r.tiles_n, sm, sn);
+      const int64_t m0 = sm * CfgSmall8::kBM, n0 = sn * kBN;
+      if (m0 >= r.M) return;
+      TileJob t;
+      t.KB = (int)(p.K / kBK);
+      t.K = p.K;
+      t.a_q = r.a_q + m0 * p.K;
+      t.a_s = r.a_s + m0 * t.KB;
+      t.gidx = nullptr;
+      t.T = 0;
+      t.b_q = r.b_q + n0 * p.K;
+      t.b_s = r.b_s + (n0 >> 7) * t.KB;
+      t.m_valid = (int)((r.M - m0) < CfgSmall8::kBM ? (r.M - m0) : CfgSmall8::kBM);
+      t.n_valid = (int)((r.N - n0) < kBN ? (r.N - n0) : kBN);
+      const TileOut o{r.y + m0 * p.ldy + n0, nullptr, nullptr};
+      gemm_tile<CfgSmall8, V>(t, o, p.ldy, lds);
+      return;
+    }
+  }
+  const int64_t L = xcd_remap(blockIdx.x, p.wgs_large > 0 ? p.wgs_large : (int64_t)gridDim.x);
   int64_t tm, tn;
   raster(L, p.slots_m, p.tiles_n, tm, tn);
   const int64_t n0 = tn * kBN;
@@ -1637,7 +1683,7 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   });
   if (attr_err[dev] != hipSuccess) return attr_err[dev];
-  const int64_t grid = p.slots_m * p.tiles_n;
+  const int64_t grid = p.slots_m * p.tiles_n + (p.wgs_large > 0 ? p.small.slots_m * p.small.tiles_n : 0);
   hipLaunchKernelGGL((gemm_kernel<C, V>), dim3((unsigned)grid), dim3(C::kThreads),
                      kLds, stream, p);
   return hipGetLastError();
@@ -1702,7 +1748,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   using V = Variant<false, kPow2, kOut, false, kBRow, kSwiGLU>;
   if (M == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N};
+  GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N, 0, {}};
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
   const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
   int64_t rows_large, n1;
@@ -1710,6 +1756,33 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   if (rows_large == M && n1 == tiles_n) {
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
+  }
+  if constexpr (kOut == kOutBf16 && !kBRow && !kSwiGLU) {
+    // Both shapes in one launch (the 128-row tiles run 8 waves too): rows
+    // [0, rows_large) x panels [0, n1) on 256-row tiles, the rest (the other
+    // rows, or the other panels) on 128-row tiles.
+    static_assert(SmallCfg<V>::kThreads == LargeCfg<V>::kThreads, "one workgroup size");
+    const bool by_rows = rows_large > 0 && rows_large < M;
+    if (by_rows || n1 > 0) {
+      GemmRegion r;
+      if (by_rows) {
+        p.M = rows_large;
+        p.slots_m = rows_large / CfgLarge::kBM;
+        r = GemmRegion{a_q + rows_large * K, a_s + rows_large * (K / kBK), b_q, b_s, y + rows_large * p.ldy,
+                       M - rows_large, N, 0, tiles_n};
+      } else {
+        const int64_t n_off = n1 * kBN;
+        p.N = n_off;
+        p.tiles_n = (int32_t)n1;
+        p.slots_m = mt_large;
+        r = GemmRegion{a_q, a_s, b_q + n_off * K, b_s + (n_off / 128) * (K / kBK), y + n_off, M, N - n_off, 0,
+                       (int32_t)(tiles_n - n1)};
+      }
+      r.slots_m = (r.M + CfgSmall8::kBM - 1) / CfgSmall8::kBM;
+      p.wgs_large = p.slots_m * p.tiles_n;
+      p.small = r;
+      return launch<LargeCfg<V>, V>(p, stream);
+    }
   }
   if (rows_large > 0 && rows_large < M) {
     // token rows [0, rows_large) on 256-row tiles, then the rest on 128-row tiles
@@ -1761,7 +1834,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
   using V = Variant<true, kPow2, kOutBf16, kGather>;
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n, N};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n, N, 0, {}};
   // 256-row tiles once the average group fills one; their ragged last tile
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
