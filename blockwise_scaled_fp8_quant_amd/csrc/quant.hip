@@ -513,6 +513,9 @@ hipError_t launch_quant_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *q
 // and passes them to the others through DPP row_share.  The block |max| is
 // taken over the fp32 values before their bf16 rounding and rounded once:
 // the rounding is monotonic, so this is the |max| of the rounded values.
+// Between the |max| and the codes, y is held as packed bf16 pairs (half the
+// registers of fp32 values: 93 VGPRs at K = 4096, 157 at K = 8192, which
+// lets three waves share a SIMD there).
 // With one row per wave the chip keeps 16 rows per CU in flight; giving a
 // wave several rows, with the next row's loads overlapping the current row's
 // math, measured slower, and so did two to eight waves per row.  The kernel
@@ -565,35 +568,19 @@ __device__ __forceinline__ void share_params(const BlockQ &mine, const float (&a
   }
 }
 
+// One row of the norm: w holds the lane's kChunks chunks of the row, gam the
+// same chunks of gamma.
 template <int kMode, int kChunks>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma, int64_t M, int K, float eps,
-    uint8_t *__restrict__ q, float *__restrict__ scales) {
-  static_assert(kChunks >= 1 && kChunks <= 16 && (kChunks & (kChunks - 1)) == 0, "chunks per lane");
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
-  const uint16_t *xr = x + (row < M ? row : M - 1) * K;
-  uint4 gam[kChunks], w[kChunks];
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {  // the row first: its data decides when the math can start
-    const int col = 512 * i + 8 * lane;
-    w[i] = load_stream16(xr + (col < K ? col : K - 8));
-  }
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int col = 512 * i + 8 * lane;
-    gam[i] = *reinterpret_cast<const uint4 *>(gamma + (col < K ? col : K - 8));
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
-
+__device__ __forceinline__ void norm_row(const uint4 (&w)[kChunks], const uint4 (&gam)[kChunks], int K, float eps,
+                                         int lane, uint8_t *__restrict__ qr, float *__restrict__ sr) {
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    const bool in = 512 * i + 8 * lane < K;  // a chunk past the row (clamped load) adds nothing
-    ss = dot2_sq(in ? w[i].x : 0u, ss);
-    ss = dot2_sq(in ? w[i].y : 0u, ss);
-    ss = dot2_sq(in ? w[i].z : 0u, ss);
-    ss = dot2_sq(in ? w[i].w : 0u, ss);
+    float t = dot2_sq(w[i].x, ss);
+    t = dot2_sq(w[i].y, t);
+    t = dot2_sq(w[i].z, t);
+    t = dot2_sq(w[i].w, t);
+    ss = 512 * i + 8 * lane < K ? t : ss;  // a chunk past the row (clamped load) adds nothing
   }
   // butterfly: every lane ends with the same sum (each step adds a pair in
   // either order, and fp32 addition is commutative)
@@ -601,26 +588,22 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   const float r = 1.0f / __builtin_sqrtf(ss * (1.0f / (float)K) + eps);
 
-  float f[kChunks][8];
+  uint32_t yb[kChunks][4];  // y rounded to bf16, two per word
   float amax[kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
     const uint32_t xw[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
     const uint32_t gw[4] = {gam[i].x, gam[i].y, gam[i].z, gam[i].w};
-    float yf[8];
     float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      yf[2 * k] = (bf16_lo(xw[k]) * r) * bf16_lo(gw[k]);
-      yf[2 * k + 1] = (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]);
-      m = max3_abs(m, yf[2 * k], yf[2 * k + 1]);
+      const float lo = (bf16_lo(xw[k]) * r) * bf16_lo(gw[k]);
+      const float hi = (bf16_hi(xw[k]) * r) * bf16_hi(gw[k]);
+      m = max3_abs(m, lo, hi);
+      yb[i][k] = to_bf16x2(lo, hi);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t b = to_bf16x2(yf[2 * k], yf[2 * k + 1]);
-      f[i][2 * k] = bf16_lo(b);
-      f[i][2 * k + 1] = bf16_hi(b);
-    }
+    // y is held as packed bf16 until the block scales are known
+    asm volatile("" : "+v"(yb[i][0]), "+v"(yb[i][1]), "+v"(yb[i][2]), "+v"(yb[i][3]));
     amax[i] = bf16_lo(to_bf16x2(group16_max(m), 0.0f));
   }
   BlockQ p[kChunks];
@@ -634,16 +617,49 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
     share_params<kMode, kChunks>(block_params<kMode>(a), amax, p);
   }
 
-  const int nb = K >> 7;
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
     const int col = 512 * i + 8 * lane;
-    const uint2 o = quant8<kMode>(p[i], f[i]);
-    if (col < K && row < M) {  // (col < K is uniform over each 16-lane block)
-      if ((lane & 15) == 0) scales[row * nb + (col >> 7)] = p[i].s;
-      *reinterpret_cast<uint2 *>(q + row * K + col) = o;
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = bf16_lo(yb[i][k]);
+      f[2 * k + 1] = bf16_hi(yb[i][k]);
+    }
+    const uint2 o = quant8<kMode>(p[i], f);
+    if (col < K) {  // (uniform over each 16-lane block)
+      if ((lane & 15) == 0) sr[col >> 7] = p[i].s;
+      *reinterpret_cast<uint2 *>(qr + col) = o;
     }
   }
+}
+
+// The lane's chunks of one row of x (columns 512 i + 8 lane, clamped into the row).
+template <int kChunks>
+__device__ __forceinline__ void load_row(const uint16_t *__restrict__ xr, int K, int lane, uint4 (&w)[kChunks]) {
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    w[i] = load_stream16(xr + (col < K ? col : K - 8));
+  }
+}
+
+template <int kMode, int kChunks>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma, int64_t M, int K, float eps,
+    uint8_t *__restrict__ q, float *__restrict__ scales) {
+  static_assert(kChunks >= 1 && kChunks <= 16 && (kChunks & (kChunks - 1)) == 0, "chunks per lane");
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
+  uint4 gam[kChunks], w[kChunks];
+  load_row<kChunks>(x + (row < M ? row : M - 1) * K, K, lane, w);  // the row first: its data decides when the math can start
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int col = 512 * i + 8 * lane;
+    gam[i] = *reinterpret_cast<const uint4 *>(gamma + (col < K ? col : K - 8));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the math
+  if (row < M) norm_row<kMode, kChunks>(w, gam, K, eps, lane, q + row * K, scales + row * (K >> 7));
 }
 
 template <int kMode, int kChunks>
