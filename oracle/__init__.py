@@ -33,6 +33,8 @@ from .oracle import (  # noqa: F401
     bf16_to_f64,
     swiglu_h_f64,
     gemm_swiglu_quant,
+    grouped_gemm_swiglu_quant,
+    grouped_gemm_swiglu_quant_rows,
     rmsnorm_f64,
     rmsnorm_quant_1x128,
     moe_permute,

@@ -461,6 +461,62 @@ def gemm_swiglu_quant(aq, as_, bq, bs, mode=MODE_AMAX):
     return quant_act_1x128(round_bf16(swiglu_h_f64(aq, as_, bq, bs)), mode)
 
 
+# The same fused gate+up projection for the experts of a SwiGLU
+# mixture-of-experts layer (the recipe's MoE models, page 1, "Leistungsgewinne
+# in der Praxis" and "Warum dies fuer die KI-Oekonomie wichtig ist"): routed
+# row r of group g goes through expert g's fused gate+up weight, then the
+# SwiGLU and row quantization above.  Reading: the grouping is that of the
+# grouped GEMM (rows [offsets[g], offsets[g+1]) to expert g), and routed rows
+# may be gathered from the token matrix by index, an index outside the tokens
+# standing for a zero row (zero codes, zero scale), as for the gathering
+# grouped GEMM.
+# ---------------------------------------------------------------------------
+
+def _gather_rows(aq, as_, row_index):
+    """(a_q, a_s) of the routed rows: token row row_index[r], or a zero row."""
+    aq = np.asarray(aq, dtype=np.uint8)
+    as_ = np.asarray(as_, dtype=np.float32)
+    idx = np.asarray(row_index, dtype=np.int64)
+    ok = (idx >= 0) & (idx < aq.shape[0])
+    gq = np.zeros((idx.size, aq.shape[1]), dtype=np.uint8)
+    gs = np.zeros((idx.size, as_.shape[1]), dtype=np.float32)
+    gq[ok] = aq[idx[ok]]
+    gs[ok] = as_[idx[ok]]
+    return gq, gs
+
+
+def _swiglu_quant_of_y(y, mode):
+    """Fused gate|up GEMM output y [rows, 2F] (fp64, before its bf16 rounding)
+    -> the row quantization of bf16(silu(bf16(g)) * bf16(u))."""
+    yb = bf16_to_f64(round_bf16(y))
+    g, u = swiglu_split(yb)
+    return quant_act_1x128(round_bf16(g / (1.0 + np.exp(-g)) * u), mode)
+
+
+def grouped_gemm_swiglu_quant(aq, as_, bq, bs, offsets, mode=MODE_AMAX, row_index=None):
+    """(h_q uint8 [M_total, F], h_s f32 [M_total, F/128]).  bq [G, 2F, K],
+    bs [G, 2F/128, K/128] (gate/up interleaved per expert as for
+    gemm_swiglu_quant), offsets int32 [G+1] covering all M_total rows.
+    row_index None: aq [M_total, K] are the routed rows; else aq [T, K] the
+    tokens and routed row r is token row_index[r]."""
+    if row_index is not None:
+        aq, as_ = _gather_rows(aq, as_, row_index)
+    return _swiglu_quant_of_y(grouped_gemm_f64(aq, as_, bq, bs, offsets), mode)
+
+
+def grouped_gemm_swiglu_quant_rows(aq, as_, bq, bs, groups, rows, mode=MODE_AMAX):
+    """The rows `rows` of grouped_gemm_swiglu_quant's output, row rows[i] of aq
+    (already gathered, or the token row it reads) going through the expert
+    groups[i]: (h_q uint8 [len(rows), F], h_s f32 [len(rows), F/128])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    N = np.asarray(bq).shape[1]
+    ms = np.repeat(rows, N)
+    ns = np.tile(np.arange(N, dtype=np.int64), rows.size)
+    grp = np.repeat(np.asarray(groups, dtype=np.int32), N)
+    y = grouped_gemm_sampled_f64(aq, as_, bq, bs, grp, ms, ns).reshape(rows.size, N)
+    return _swiglu_quant_of_y(y, mode)
+
+
 # ---------------------------------------------------------------------------
 # RMS normalization with the next layer's quantization fused: the third
 # producer of FP8 activations in a Llama/Qwen3 block (its norms feed the QKV

@@ -8,7 +8,9 @@ Praxis").  Pins, independent of the functions under test:
   - h against torch's silu in float64 on the bf16-rounded gate and up taken
     from the plain GEMM by that index arithmetic;
   - closed forms: g = 0 gives 0, exact-integer products give h from math.exp;
-  - the quantized output against the pinned row quantizer of bf16(h).
+  - the quantized output against the pinned row quantizer of bf16(h);
+  - the grouped (mixture-of-experts) form against the dense form on each
+    group's rows, explicit gathering by index, and a zero row's closed form.
 """
 import math
 
@@ -76,3 +78,68 @@ def test_quantized_output_is_the_row_quantizer_of_bf16_h(oracle_lib):
         q2, s2 = oracle_lib.quant_act_1x128(oracle_lib.round_bf16(oracle_lib.swiglu_h_f64(aq, as_, bq, bs)), mode)
         assert q.shape == (M, F) and s.shape == (M, F // 128)
         assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# The grouped (mixture-of-experts) form.  Pins, independent of the code under
+# test: the dense oracle above on each group's rows alone (its C GEMM loop is
+# a different routine from the grouped one), explicit gathering by index, and
+# the closed form of a zero row.
+# ---------------------------------------------------------------------------
+
+def _expert_operands(rng, G, F, K, M):
+    aq = _codes(rng, (M, K))
+    as_ = rng.uniform(1e-3, 1e-2, size=(M, K // 128)).astype(np.float32)
+    bq = _codes(rng, (G, 2 * F, K))
+    bs = rng.uniform(1e-3, 1e-2, size=(G, 2 * F // 128, K // 128)).astype(np.float32)
+    return aq, as_, bq, bs
+
+
+def test_grouped_equals_dense_per_group(oracle_lib):
+    """Ragged groups, one of them empty: every group's rows equal the dense
+    fused oracle on those rows with that expert's weight."""
+    rng = np.random.default_rng(11)
+    G, F, K = 4, 256, 256
+    offsets = np.array([0, 37, 37, 140, 205], dtype=np.int32)
+    aq, as_, bq, bs = _expert_operands(rng, G, F, K, int(offsets[-1]))
+    for mode in (0, 1):
+        hq, hs = oracle_lib.grouped_gemm_swiglu_quant(aq, as_, bq, bs, offsets, mode)
+        assert hq.shape == (205, F) and hs.shape == (205, F // 128)
+        for g in range(G):
+            a, b = offsets[g], offsets[g + 1]
+            if a == b:
+                continue
+            dq, ds = oracle_lib.gemm_swiglu_quant(aq[a:b], as_[a:b], bq[g], bs[g], mode)
+            assert np.array_equal(hq[a:b], dq) and np.array_equal(hs[a:b], ds), (mode, g)
+
+
+def test_grouped_gather_by_index(oracle_lib):
+    """Routed rows read token rows by index: the result equals the grouped
+    oracle on the explicitly gathered rows; an index outside the tokens is a
+    zero row, whose h is 0 (codes 0, the all-zero block's scale 1)."""
+    rng = np.random.default_rng(12)
+    G, F, K, T = 3, 128, 384, 50
+    aq, as_, bq, bs = _expert_operands(rng, G, F, K, T)
+    idx = rng.integers(0, T, size=90).astype(np.int32)
+    idx[[5, 61]] = [-1, T]                                  # outside the token matrix
+    offsets = np.array([0, 30, 31, 90], dtype=np.int32)
+    hq, hs = oracle_lib.grouped_gemm_swiglu_quant(aq, as_, bq, bs, offsets, 0, row_index=idx)
+    gq = np.stack([aq[i] if 0 <= i < T else np.zeros(K, np.uint8) for i in idx])
+    gs = np.stack([as_[i] if 0 <= i < T else np.zeros(K // 128, np.float32) for i in idx])
+    rq, rs = oracle_lib.grouped_gemm_swiglu_quant(gq, gs, bq, bs, offsets, 0)
+    assert np.array_equal(hq, rq) and np.array_equal(hs, rs)
+    for r in (5, 61):
+        assert (hq[r] == 0).all() and (hs[r] == 1.0).all()
+
+
+def test_grouped_rows_equal_full(oracle_lib):
+    """The sampled-rows form gives the full form's rows."""
+    rng = np.random.default_rng(13)
+    G, F, K = 3, 128, 256
+    offsets = np.array([0, 20, 64, 100], dtype=np.int32)
+    aq, as_, bq, bs = _expert_operands(rng, G, F, K, 100)
+    hq, hs = oracle_lib.grouped_gemm_swiglu_quant(aq, as_, bq, bs, offsets, 1)
+    rows = np.array([0, 19, 20, 63, 64, 99])
+    groups = np.searchsorted(offsets, rows, side="right") - 1
+    sq, ss = oracle_lib.grouped_gemm_swiglu_quant_rows(aq, as_, bq, bs, groups, rows, 1)
+    assert np.array_equal(sq, hq[rows]) and np.array_equal(ss, hs[rows])
