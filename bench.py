@@ -609,11 +609,47 @@ def moe(fp8q, synth, torch, dev, reps):
                 "fp8_over_bf16_dense_proxy": round(tb / t, 3)}
             log(f"moe {shape.name} {layer}: {tf:.1f} TFLOP/s ({t * 1e6:.1f} us), roof {roof:.0f}; "
                 f"bf16 dense proxy {flops / tb / 1e12:.1f}")
+            if layer == "gate_up":
+                out[f"{shape.name}/gate_up_swiglu_quant"] = moe_swiglu(fp8q, torch, aq, as_, bq, bs, offd, y,
+                                                                       reps, shape.name, t)
             del x, w, w0, bq, bs, aq, as_, y
             torch.cuda.empty_cache()
     out["bf16_dense_proxy"] = ("torch.matmul in bf16 of all M_total rows against one expert's weight: the same "
                                "flops as the grouped GEMM in one dense call, standing in for a bf16 grouped GEMM")
     return out
+
+
+def moe_swiglu(fp8q, torch, aq, as_, bq, bs, offd, y, reps, name, t_gemm):
+    """The experts' gate+up GEMM with SwiGLU and the down projection's 1x128
+    quantization in its epilogue (weight rows read as alternating 128-row
+    gate/up blocks per expert), against the unfused sequence: the bf16 grouped
+    GEMM, silu(gate) * up as torch elementwise ops on the bf16 halves, then
+    the 1x128 quantizer.  t_gemm: the bf16 grouped GEMM alone (timed above)."""
+    Mt, N = y.shape
+    F = N // 2
+    hq = torch.empty((Mt, F), dtype=torch.uint8, device=y.device)
+    hs = torch.empty((Mt, F // 128), dtype=torch.float32, device=y.device)
+    h = torch.empty((Mt, F), dtype=torch.bfloat16, device=y.device)
+    yv, hv = y.view(Mt, F // 128, 2, 128), h.view(Mt, F // 128, 128)
+
+    def separate():
+        fp8q.fp8_grouped_gemm(aq, as_, bq, bs, offd, out=y)
+        torch.mul(torch.nn.functional.silu(yv[:, :, 0]), yv[:, :, 1], out=hv)
+        fp8q.fp8_quant_act_1x128(h, "amax", out=(hq, hs))
+
+    def fused():
+        fp8q.fp8_grouped_gemm_swiglu_quant(aq, as_, bq, bs, offd, out=(hq, hs))
+    separate()
+    fused()
+    ts = time_loop(separate, reps, torch, label=f"moe/{name}/swiglu/separate")
+    tf = time_loop(fused, reps, torch, label=f"moe/{name}/swiglu/fused")
+    f = 2.0 * Mt * N * bq.shape[2]
+    log(f"moe {name} gate_up + swiglu + quant fused: {tf * 1e6:.1f} us ({f / tf / 1e12:.1f} TFLOP/s) vs "
+        f"{ts * 1e6:.1f} us separate, {t_gemm * 1e6:.1f} us bf16 grouped GEMM alone")
+    del hq, hs, h
+    return {"F": F, "fused_us": round(tf * 1e6, 2), "fused_tflops": round(f / tf / 1e12, 1),
+            "separate_us": round(ts * 1e6, 2), "gemm_alone_us": round(t_gemm * 1e6, 2),
+            "speedup": round(ts / tf, 3), "over_gemm_alone": round(t_gemm / tf, 3)}
 
 
 def backward(fp8q, synth, layers, torch, dev, M, reps):

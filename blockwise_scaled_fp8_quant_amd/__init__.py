@@ -27,7 +27,7 @@ __all__ = ["SCALE_AMAX", "SCALE_POW2", "fp8_quant_act_1x128", "fp8_rmsnorm_quant
            "fp8_quant_weight_128x128", "WeightBatch", "fp8_quant_weight_128x128_batched",
            "fp8_blockscaled_gemm", "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2",
            "fp8_grouped_gemm_pow2", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant",
-           "fp8_grouped_gemm_gather",
+           "fp8_grouped_gemm_gather", "fp8_grouped_gemm_swiglu_quant",
            "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad",
            "fp8_blockscaled_gemm_wgrad_pow2",
            "fp8_kv_cache_append", "fp8_attention_decode", "fp8_attention_decode_workspace_size",
@@ -342,6 +342,52 @@ def fp8_grouped_gemm_gather(a_q, a_s, b_q, b_s, group_offsets, row_index, mode="
                _lib.load().fp8_grouped_gemm_gather(pa, pas, T, pb, pbs, poff, pidx, G, M, N, K, py,
                                                    _mode(mode), _stream(a_q)))
     return y
+
+
+def fp8_grouped_gemm_swiglu_quant(a_q, a_s, b_q, b_s, group_offsets, row_index=None, mode="amax", out=None):
+    """Experts' fused gate+up projection with SwiGLU and the down projection's
+    quantization in the epilogue.
+
+    b_q [G, 2F, K], b_s [G, 2F/128, K/128] (gate and up rows in alternating
+    128-row blocks per expert), group_offsets int32 [G+1] in device memory.
+    row_index None: a_q [M_total, K], a_s [M_total, K/128], routed row r is row
+    r; else int32 [M_total] in device memory and a_q [T, K] the tokens, routed
+    row r reading token row_index[r].  Returns (h_q uint8 [M_total, F],
+    h_s fp32 [M_total, F/128]): per row, fp8_blockscaled_gemm_swiglu_quant
+    with the row's expert weight.
+    """
+    a_q, pa = _as_bytes(a_q, "a_q", 2)
+    b_q, pb = _as_bytes(b_q, "b_q", 3)
+    pas = _dev(a_s, "a_s", torch.float32, 2)
+    pbs = _dev(b_s, "b_s", torch.float32, 3)
+    poff = _dev(group_offsets, "group_offsets", torch.int32, 1)
+    T, K = a_q.shape
+    G, N, Kb = b_q.shape
+    if N % 256 != 0:
+        raise ValueError("b_q must have 2F rows per expert, F a multiple of 128")
+    F = N // 2
+    if Kb != K or tuple(a_s.shape) != (T, K // 128) or tuple(b_s.shape) != (G, N // 128, K // 128):
+        raise ValueError("operand shapes do not match")
+    if group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must have G+1 entries")
+    if row_index is None:
+        M, pidx = T, None
+    else:
+        pidx = _dev(row_index, "row_index", torch.int32, 1)
+        M = row_index.numel()
+    if out is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=a_q.device)
+        hs = torch.empty((M, F // 128), dtype=torch.float32, device=a_q.device)
+    else:
+        hq, hs = out
+    hq, phq = _as_bytes(hq, "h_q", 2)
+    phs = _dev(hs, "h_s", torch.float32, 2)
+    if tuple(hq.shape) != (M, F) or tuple(hs.shape) != (M, F // 128):
+        raise ValueError("output shapes do not match")
+    _lib.check("fp8_grouped_gemm_swiglu_quant",
+               _lib.load().fp8_grouped_gemm_swiglu_quant(pa, pas, T, pb, pbs, poff, pidx, G, M, F, K, phq, phs,
+                                                         _mode(mode), _stream(a_q)))
+    return hq, hs
 
 
 def _dual(fn, x, rows_mult, mode, rowwise, out):

@@ -16,7 +16,8 @@ ENTRY_POINTS = ("fp8_quant_act_1x128", "fp8_rmsnorm_quant_1x128", "fp8_quant_wei
                 "fp8_quant_weight_128x128_batched",
                 "fp8_blockscaled_gemm",
                 "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
-                "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather", "fp8_quant_act_dual",
+                "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
+                "fp8_grouped_gemm_swiglu_quant", "fp8_quant_act_dual",
                 "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
                 "fp8_kv_cache_append", "fp8_kv_cache_append_tokens", "fp8_attention_prefill",
                 "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8_attention_decode_noalloc",
@@ -67,6 +68,8 @@ def load():
         getattr(lib, name).restype = ci
     lib.fp8_grouped_gemm_gather.argtypes = [p, p, i64, p, p, p, p, i32, i64, i64, i64, p, ci, p]
     lib.fp8_grouped_gemm_gather.restype = ci
+    lib.fp8_grouped_gemm_swiglu_quant.argtypes = [p, p, i64, p, p, p, p, i32, i64, i64, i64, p, p, ci, p]
+    lib.fp8_grouped_gemm_swiglu_quant.restype = ci
     lib.fp8_kv_cache_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i64, ci, p]
     lib.fp8_kv_cache_append.restype = ci
     lib.fp8_kv_cache_append_tokens.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i64, ci, p]

@@ -306,6 +306,35 @@ fp8q_status gather_entry(const char *fn, const uint8_t *a_q, const float *a_s, i
                   fn);
 }
 
+fp8q_status grouped_swiglu_entry(const char *fn, const uint8_t *a_q, const float *a_s, int64_t T,
+                                 const uint8_t *b_q, const float *b_s, const int32_t *group_offsets,
+                                 const int32_t *row_index, int32_t G, int64_t M_total, int64_t F, int64_t K,
+                                 uint8_t *h_q, float *h_s, int mode, void *stream) {
+  g_last_error.clear();
+  if (mode != FP8Q_SCALE_AMAX && mode != FP8Q_SCALE_POW2) return fail(FP8Q_EINVAL, fn, "unknown mode");
+  if (G < 1) return fail(FP8Q_EINVAL, fn, "G must be >= 1");
+  if (!(T >= 0 && M_total >= 0 && F >= 0 && K >= 0)) return fail(FP8Q_EINVAL, fn, "negative size");
+  if (!(K > 0 && K % 128 == 0)) return fail(FP8Q_ESHAPE, fn, "K must be a positive multiple of 128");
+  if (F % 128 != 0) return fail(FP8Q_ESHAPE, fn, "F must be a multiple of 128");
+  if (K > kMaxGemmK) return fail(FP8Q_ESHAPE, fn, "K larger than 4194304");
+  if (!(M_total < ((int64_t)1 << 31) && F <= ((int64_t)1 << 30)))
+    return fail(FP8Q_EINVAL, fn, "M_total or F too large");
+  // Gathered rows are addressed by 32-bit byte offsets into the token matrix.
+  if (row_index && T >= ((int64_t)1 << 31) / K)
+    return fail(FP8Q_ESHAPE, fn, "token matrix T*K must be below 2^31 bytes");
+  if (M_total == 0 || F == 0) return FP8Q_OK;
+  if (row_index && T == 0) return fail(FP8Q_EINVAL, fn, "T must be positive when there are routed rows");
+  if (!(a_q && a_s && b_q && b_s && h_q && h_s && group_offsets)) return fail(FP8Q_EINVAL, fn, "null pointer");
+  if (!(aligned16(a_q) && aligned16(a_s) && aligned16(b_q) && aligned16(b_s) && aligned16(h_q) && aligned16(h_s) &&
+        aligned16(group_offsets) && aligned16(row_index)))
+    return fail(FP8Q_EALIGN, fn, "pointers must be 16-byte aligned");
+  fp8q_status st = check_device(fn);
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_grouped_gemm_swiglu_quant(a_q, a_s, T, b_q, b_s, group_offsets, row_index, G,
+                                                         M_total, F, K, h_q, h_s, mode, (hipStream_t)stream),
+                  fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,6 +393,14 @@ fp8q_status fp8_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_
                                     void *stream) {
   return gather_entry(__func__, a_q, a_s, T, b_q, b_s, group_offsets, row_index, G, M_total, N, K, y, mode,
                       stream);
+}
+
+fp8q_status fp8_grouped_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s, int64_t T, const uint8_t *b_q,
+                                          const float *b_s, const int32_t *group_offsets, const int32_t *row_index,
+                                          int32_t G, int64_t M_total, int64_t F, int64_t K, uint8_t *h_q,
+                                          float *h_s, int mode, void *stream) {
+  return grouped_swiglu_entry(__func__, a_q, a_s, T, b_q, b_s, group_offsets, row_index, G, M_total, F, K, h_q, h_s,
+                              mode, stream);
 }
 
 fp8q_status fp8_kv_cache_append(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,

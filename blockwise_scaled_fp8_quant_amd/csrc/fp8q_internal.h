@@ -87,6 +87,13 @@ hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int6
                                       const int32_t *group_offsets, const int32_t *row_index, int32_t G,
                                       int64_t M_total, int64_t N, int64_t K, uint16_t *y, bool pow2,
                                       hipStream_t stream);
+// Grouped gate+up GEMM with the SwiGLU epilogue (row_index may be null: rows
+// of a_q in order).
+hipError_t launch_grouped_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s, int64_t T,
+                                            const uint8_t *b_q, const float *b_s,
+                                            const int32_t *group_offsets, const int32_t *row_index, int32_t G,
+                                            int64_t M_total, int64_t F, int64_t K, uint8_t *hq, float *hs,
+                                            int mode, hipStream_t stream);
 
 // MoE dispatch order: routing table ids [T][k] -> offsets [E+n_shared+1],
 // row_index [T*(k+n_shared)], entry_row [T*k] (may be null), through a

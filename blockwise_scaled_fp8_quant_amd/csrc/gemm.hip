@@ -72,7 +72,7 @@ struct Variant {
   static constexpr bool kGather = kGather_;
   static constexpr bool kBRow = kBRow_;
   static constexpr bool kSwiGLU = kSwiGLU_;
-  static_assert(!(kSwiGLU && (kOut == kOutBf16 || kGrouped || kBRow)), "SwiGLU: dense, quantized output");
+  static_assert(!(kSwiGLU && (kOut == kOutBf16 || kBRow || kPow2)), "SwiGLU: quantized output, amax arithmetic");
   static_assert(!(kGather && !kGrouped), "gathered rows belong to groups");
   static_assert(!(kBRow && kGrouped), "per-row weight-side scales: dense only");
 };
@@ -1274,76 +1274,102 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
     }
   } else if constexpr (V::kSwiGLU) {
     static_assert(C::kWaveN == 128, "SwiGLU epilogue: a wave holds 128 gate or up rows");
+    static_assert(kSubM == 4, "SwiGLU epilogue: 64 rows per wave, split in two halves");
     // SwiGLU epilogue of a fused gate+up projection: the tile's weight rows
     // are 128 gate rows (waves wn = 0) and the 128 up rows of the same output
     // columns (waves wn = 1).  gate and up are rounded to bf16 as the bf16
-    // epilogue rounds them; the up waves pass theirs through LDS (the stage
-    // buffers are free once every wave is past the barrier), and the gate
-    // waves form h = silu(g) * u = g / (1 + e^-g) * u in fp32, round it to
-    // bf16 and quantize each row's 128 values as one 1x128 block (the
-    // activation rule), writing row r's block at column 128*(n0/256).
-    constexpr int kUpStride = 66;  // 32-bit words per LDS row (64 + 2: rows fall in different banks)
-    uint32_t *upl = reinterpret_cast<uint32_t *>(lds);
-    __syncthreads();
-    if (wn == 1) {
+    // epilogue rounds them.  The two waves holding the same 64 token rows
+    // split them: the gate wave forms h for rows 0-31 (m sub-tiles 0, 1) and
+    // the up wave for rows 32-63 (sub-tiles 2, 3), each receiving the other
+    // half's up (or gate) values through LDS (the stage buffers are free once
+    // every wave is past the barrier), so all eight waves share the exponent
+    // and quantization work.  h = silu(g) * u = g / (1 + e^-g) * u in fp32 is
+    // rounded to bf16 and each row's 128 values quantized as one 1x128 block
+    // (the activation rule), row r's block written at column 128*(n0/256).
+    constexpr int kXStride = 66;  // 32-bit words per LDS row (64 + 2: rows fall in different banks)
+    uint32_t *xl = reinterpret_cast<uint32_t *>(lds);
+    const int64_t F = N >> 1;   // columns of h
+    const int64_t nbo = F >> 7;  // scale blocks per row of h
+    // gate waves hand over g of sub-tiles 2, 3; up waves u of sub-tiles 0, 1
+    auto hand_over = [&](auto MI) {
+      constexpr int mi = decltype(MI)::value;
+      const int r = wm * 64 + mi * 16 + (lane & 15);
 #pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int r = wm * 64 + mi * 16 + (lane & 15);
-#pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) {
-          const int nn = ni * 16 + 4 * (lane >> 4);
-          uint2 w;
-          w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
-          w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
-          *reinterpret_cast<uint2 *>(upl + r * kUpStride + (nn >> 1)) = w;
-        }
+      for (int ni = 0; ni < kSubN; ++ni) {
+        const int nn = ni * 16 + 4 * (lane >> 4);
+        uint2 w;
+        w.x = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+        w.y = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+        *reinterpret_cast<uint2 *>(xl + r * kXStride + (nn >> 1)) = w;
       }
+    };
+    // h, its block scale and codes for sub-tile mi (kGate: this wave holds g)
+    auto rows_out = [&](auto MI, auto GATE) {
+      constexpr int mi = decltype(MI)::value;
+      constexpr bool kGate = decltype(GATE)::value;
+      const int r = wm * 64 + mi * 16 + (lane & 15);
+      uint32_t h[kSubN][2];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < kSubN; ++ni) {
+        const int nn = ni * 16 + 4 * (lane >> 4);
+        const uint2 xw = *reinterpret_cast<const uint2 *>(xl + r * kXStride + (nn >> 1));
+        const uint32_t m01 = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+        const uint32_t m23 = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+        const float mine[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+        const float other[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = kGate ? mine[i] : other[i], u = kGate ? other[i] : mine[i];
+          hv[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        }
+        h[ni][0] = pack_bf16x2(hv[0], hv[1]);
+        h[ni][1] = pack_bf16x2(hv[2], hv[3]);
+        amax = max3_abs(amax, bf16_lo(h[ni][0]), bf16_hi(h[ni][0]));
+        amax = max3_abs(amax, bf16_lo(h[ni][1]), bf16_hi(h[ni][1]));
+      }
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+      const BlockQ bq = block_params<kOut>(amax);
+      uint32_t cw[kSubN];
+#pragma unroll
+      for (int ni = 0; ni < kSubN; ++ni) {
+        const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
+        float qv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+        cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+      }
+      if (r < t.m_valid && (lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
+#pragma unroll
+      for (int q = 0; q < kSubN / 4; ++q) {
+        const uint4 v = rows_to_subtiles(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+        if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * F + 16 * (4 * q + (lane >> 4)), v);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using Gate = std::true_type;
+    using Up = std::false_type;
+    __syncthreads();
+    if (wn == 0) {
+      hand_over(I2{});
+      hand_over(I3{});
+    } else {
+      hand_over(I0{});
+      hand_over(I1{});
     }
     __syncthreads();
     if (wn == 0) {
-      const int64_t F = N >> 1;   // columns of h
-      const int64_t nbo = F >> 7;  // scale blocks per row of h
-#pragma unroll
-      for (int mi = 0; mi < kSubM; ++mi) {
-        const int r = wm * 64 + mi * 16 + (lane & 15);
-        uint32_t h[kSubN][2];
-        float amax = 0.0f;
-#pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) {
-          const int nn = ni * 16 + 4 * (lane >> 4);
-          const uint2 uw = *reinterpret_cast<const uint2 *>(upl + r * kUpStride + (nn >> 1));
-          const uint32_t g01 = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
-          const uint32_t g23 = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
-          const float g[4] = {bf16_lo(g01), bf16_hi(g01), bf16_lo(g23), bf16_hi(g23)};
-          const float u[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-          float hv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = g[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i])) * u[i];
-          h[ni][0] = pack_bf16x2(hv[0], hv[1]);
-          h[ni][1] = pack_bf16x2(hv[2], hv[3]);
-          amax = max3_abs(amax, bf16_lo(h[ni][0]), bf16_hi(h[ni][0]));
-          amax = max3_abs(amax, bf16_lo(h[ni][1]), bf16_hi(h[ni][1]));
-        }
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-        const BlockQ bq = block_params<kOut>(amax);
-        uint32_t cw[kSubN];
-#pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) {
-          const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
-          float qv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
-          cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-        }
-        if (r < t.m_valid && (lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
-#pragma unroll
-        for (int q = 0; q < kSubN / 4; ++q) {
-          const uint4 v = rows_to_subtiles(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
-          if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * F + 16 * (4 * q + (lane >> 4)), v);
-        }
-      }
+      rows_out(I0{}, Gate{});
+      rows_out(I1{}, Gate{});
+    } else {
+      rows_out(I2{}, Up{});
+      rows_out(I3{}, Up{});
     }
   } else {
     // Quantized epilogue (the activation quantization of the next layer, done
@@ -1827,14 +1853,15 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   return launch<SmallCfg<V>, V>(p, stream);
 }
 
-template <bool kPow2, bool kGather = false>
+template <bool kPow2, bool kGather = false, int kOut = kOutBf16, bool kSwiGLU = false>
 static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b_q, const float *b_s,
                           const int32_t *group_offsets, int32_t G, int64_t M_total, int64_t N, int64_t K,
-                          uint16_t *y, const int32_t *gather, int64_t T, hipStream_t stream) {
-  using V = Variant<true, kPow2, kOutBf16, kGather>;
+                          uint16_t *y, const int32_t *gather, int64_t T, hipStream_t stream,
+                          uint8_t *yq = nullptr, float *ys = nullptr) {
+  using V = Variant<true, kPow2, kOut, kGather, false, kSwiGLU>;
   if (M_total == 0 || N == 0) return hipSuccess;
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
-  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, nullptr, nullptr, gather, T, M_total, N, K, 0, G, tiles_n, N, 0, {}};
+  GemmParams p{a_q, a_s, b_q, b_s, group_offsets, y, yq, ys, gather, T, M_total, N, K, 0, G, tiles_n, N, 0, {}};
   // 256-row tiles once the average group fills one; their ragged last tile
   // per group then wastes at most half of the work it would at 128 rows.
   if (M_total >= (int64_t)G * CfgLarge::kBM) {
@@ -1894,6 +1921,26 @@ hipError_t launch_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int6
                                       hipStream_t stream) {
   return pow2 ? grouped<true, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, row_index, T, stream)
               : grouped<false, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, y, row_index, T, stream);
+}
+
+hipError_t launch_grouped_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s, int64_t T,
+                                            const uint8_t *b_q, const float *b_s,
+                                            const int32_t *group_offsets, const int32_t *row_index, int32_t G,
+                                            int64_t M_total, int64_t F, int64_t K, uint8_t *hq, float *hs,
+                                            int mode, hipStream_t stream) {
+  const int64_t N = 2 * F;
+  if (row_index) {
+    return mode == kModePow2
+               ? grouped<false, true, kModePow2, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, nullptr,
+                                                      row_index, T, stream, hq, hs)
+               : grouped<false, true, kModeAmax, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, nullptr,
+                                                      row_index, T, stream, hq, hs);
+  }
+  return mode == kModePow2
+             ? grouped<false, false, kModePow2, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, nullptr,
+                                                     nullptr, 0, stream, hq, hs)
+             : grouped<false, false, kModeAmax, true>(a_q, a_s, b_q, b_s, group_offsets, G, M_total, N, K, nullptr,
+                                                     nullptr, 0, stream, hq, hs);
 }
 
 }  // namespace fp8q

@@ -394,6 +394,41 @@ fp8q_status fp8_grouped_gemm_gather(const uint8_t *a_q, const float *a_s, int64_
                                     uint16_t *y, int mode, void *stream);
 
 /*
+ * The gate+up projection of the experts of a SwiGLU mixture-of-experts layer
+ * with the activation and the down projection's 1x128 quantization in its
+ * epilogue: fp8_blockscaled_gemm_swiglu_quant per group (the recipe's MoE
+ * models, page 1, "Leistungsgewinne in der Praxis" and "Warum dies fuer die
+ * KI-Oekonomie wichtig ist"; the separate activation and quantization passes
+ * it replaces are the quantization-kernel overhead named in "Leistungsgewinne
+ * in der Praxis").  Routed row r of group g (group_offsets[g] <= r <
+ * group_offsets[g+1]) is multiplied by expert g's fused gate+up weight, and
+ * row r of h is written:
+ *   a_q, a_s   row_index != NULL: [T][K], [T][K/128], the tokens quantized
+ *              once before dispatch; routed row r reads token row_index[r]
+ *              (an index outside [0, T) reads zeros), as in
+ *              fp8_grouped_gemm_gather.  row_index == NULL: [M_total][K],
+ *              [M_total][K/128], routed row r is row r (T is ignored).
+ *   b_q [G][2F][K], b_s [G][2F/128][K/128]  each expert's weight with gate and
+ *              up rows in alternating 128-row blocks, the layout of
+ *              fp8_blockscaled_gemm_swiglu_quant
+ *   group_offsets [G+1] int32, DEVICE memory, as for fp8_grouped_gemm (rows
+ *              no group covers are left unwritten)
+ *   row_index  [M_total] int32, DEVICE memory, or NULL
+ *   h_q [M_total][F] E4M3 bytes (out), h_s [M_total][F/128] fp32 (out)
+ *   F  output features per expert, a multiple of 128
+ *   mode fp8q_scale_mode of h's blocks; the GEMM applies the operands' scales
+ *        as fp8_grouped_gemm does (any finite values)
+ * Each row of h equals, bit for bit, what fp8_blockscaled_gemm_swiglu_quant
+ * gives for that row with its group's weight.  Errors as for
+ * fp8_grouped_gemm_gather (T*K below 2^31 bytes when row_index is given).
+ */
+fp8q_status fp8_grouped_gemm_swiglu_quant(const uint8_t *a_q, const float *a_s, int64_t T,
+                                          const uint8_t *b_q, const float *b_s,
+                                          const int32_t *group_offsets, const int32_t *row_index,
+                                          int32_t G, int64_t M_total, int64_t F, int64_t K,
+                                          uint8_t *h_q, float *h_s, int mode, void *stream);
+
+/*
  * FP8 KV cache (page 1, "Leistungsgewinne in der Praxis": FP8 for the KV cache
  * and attention takes the end-to-end gain to about 48%).  The cache holds
  * every key and value row of one token and one key/value head (head

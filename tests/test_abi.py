@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
               "fp8_quant_weight_128x128_batched", "fp8_blockscaled_gemm",
               "fp8_grouped_gemm", "fp8_blockscaled_gemm_pow2", "fp8_grouped_gemm_pow2",
               "fp8_blockscaled_gemm_quant", "fp8_blockscaled_gemm_swiglu_quant", "fp8_grouped_gemm_gather",
-              "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
+              "fp8_grouped_gemm_swiglu_quant", "fp8_quant_act_dual", "fp8_quant_weight_128x128_dual", "fp8_blockscaled_gemm_wgrad", "fp8_blockscaled_gemm_wgrad_pow2",
               "fp8_kv_cache_append", "fp8_kv_cache_append_tokens", "fp8_attention_prefill",
               "fp8_moe_permute", "fp8_blockscaled_gemm_tile_plan",
               "fp8_attention_decode", "fp8_attention_decode_workspace_size", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version"):
@@ -170,6 +170,26 @@ def test_grouped_argument_errors(lib, fn):
     assert f(GOOD, GOOD, GOOD, GOOD, ODD, 2, 64, 128, 128, GOOD, None) == 3
     assert f(None, None, None, None, None, 3, 0, 128, 128, None, None) == 0
     assert f(GOOD, GOOD, GOOD, GOOD, GOOD, 2, 64, 128, (1 << 22) + 128, GOOD, None) == 2
+
+
+def test_grouped_swiglu_quant_argument_errors(lib):
+    f = lib.fp8_grouped_gemm_swiglu_quant
+    #        aq    as    T   bq    bs    off   idx   G  M    F    K    hq    hs    mode
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, 128, GOOD, GOOD, 2, None) == 1   # unknown mode
+    assert "mode" in _err(lib)
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 0, 100, 128, 128, GOOD, GOOD, 0, None) == 1   # G < 1
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, 100, 64, 128, GOOD, GOOD, 0, None) == 2    # F % 128
+    assert "F" in _err(lib)
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, 200, GOOD, GOOD, 0, None) == 2   # K % 128
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, -1, 128, 128, GOOD, GOOD, 0, None) == 1    # negative size
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, None, GOOD, 2, 100, 128, 128, GOOD, GOOD, 0, None) == 1   # null offsets
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, 128, None, GOOD, 0, None) == 1   # null h_q
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, ODD, 2, 100, 128, 128, GOOD, GOOD, 0, None) == 3    # misaligned index
+    assert f(GOOD, GOOD, 0, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, 128, GOOD, GOOD, 0, None) == 1    # T = 0, rows routed
+    assert f(GOOD, GOOD, 1 << 20, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, 4096, GOOD, GOOD, 0, None) == 2  # T*K = 2^32
+    assert "2^31" in _err(lib)
+    assert f(None, None, 0, None, None, None, None, 2, 0, 128, 128, None, None, 0, None) == 0      # no routed rows
+    assert f(GOOD, GOOD, 64, GOOD, GOOD, GOOD, GOOD, 2, 100, 128, (1 << 22) + 128, GOOD, GOOD, 0, None) == 2
 
 
 @pytest.mark.parametrize("fn", ["fp8_quant_act_dual", "fp8_quant_weight_128x128_dual"])
