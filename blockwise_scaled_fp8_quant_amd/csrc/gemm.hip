@@ -1176,6 +1176,106 @@ __device__ __forceinline__ uint4 rows_to_subtiles(uint32_t w0, uint32_t w1, uint
   return (uint4){t01[0], t01[1], t23[0], t23[1]};
 }
 
+// SwiGLU epilogue of the 128-row, 8-wave tile (a group's ragged last slot in
+// the grouped GEMM): four waves along n with 64 weight rows each, wn = 0, 1
+// holding gate columns 0-63 and 64-127 of the tile's 128 features and
+// wn = 2, 3 the up columns of the same features.  Gate wave wn (< 2) and up
+// wave wn + 2 split their 64 token rows as the 256-row tile's epilogue does
+// (gate rows 0-31, up rows 32-63, the other half's values through LDS); a
+// row's 1x128 block is then held by two waves, one per 64-column half, which
+// exchange their partial |max| through LDS before quantizing.  Each value of
+// h, each block |max| and so each code equal the 256-row tile's.
+template <class C, class V>
+__device__ __forceinline__ void swiglu_epilogue_half(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds,
+                                                     v4f (&acc)[kSubN][kSubM], int wn, int wm, int lane) {
+  static_assert(C::kWaveN == 64 && C::kSubN == 4 && kSubM == 4 && C::kWavesN == 4, "128-row SwiGLU tile layout");
+  constexpr int kOut = V::kOut;
+  constexpr int kXStride = 66;  // 32-bit words per LDS row (64 + 2: rows fall in different banks)
+  uint32_t *xl = reinterpret_cast<uint32_t *>(lds);
+  float *ml = reinterpret_cast<float *>(lds + C::kBM * kXStride * 4);  // [2 halves][kBM rows] partial maxima
+  __syncthreads();  // the stage buffers are free once every wave is past the main loop
+  const int half = wn & 1;     // which 64 columns of each row's block
+  const bool gate = wn < 2;
+  const int64_t F = N >> 1;
+  const int64_t nbo = F >> 7;
+  // Branch-free on gate / up: the sub-tiles a wave hands over or keeps are
+  // picked by value (v_cndmask between two register values), never by an
+  // index computed from the wave kind, which would put the accumulators in
+  // scratch memory.
+  // Gate waves hand over g of sub-tiles 2, 3; up waves u of sub-tiles 0, 1.
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) {
+    const int r = wm * 64 + (gate ? 2 + mh : mh) * 16 + (lane & 15);
+#pragma unroll
+    for (int ni = 0; ni < C::kSubN; ++ni) {
+      const int nn = half * 64 + ni * 16 + 4 * (lane >> 4);
+      v4f lo = acc[ni][mh], hi = acc[ni][2 + mh];
+      asm volatile("" : "+v"(lo), "+v"(hi));  // two values, then a select (not a computed index)
+      const v4f a = gate ? hi : lo;
+      uint2 w;
+      w.x = pack_bf16x2(a[0], a[1]);
+      w.y = pack_bf16x2(a[2], a[3]);
+      *reinterpret_cast<uint2 *>(xl + r * kXStride + (nn >> 1)) = w;
+    }
+  }
+  __syncthreads();
+  // h of the kept sub-tiles (gate: 0, 1; up: 2, 3) for this wave's 64 columns
+  uint32_t h[2][C::kSubN][2];
+  float amax[2];
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) {
+    const int r = wm * 64 + (gate ? mh : 2 + mh) * 16 + (lane & 15);
+    float m = 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < C::kSubN; ++ni) {
+      const int nn = half * 64 + ni * 16 + 4 * (lane >> 4);
+      const uint2 xw = *reinterpret_cast<const uint2 *>(xl + r * kXStride + (nn >> 1));
+      v4f lo = acc[ni][mh], hi = acc[ni][2 + mh];
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      const v4f a = gate ? lo : hi;
+      const uint32_t m01 = pack_bf16x2(a[0], a[1]);
+      const uint32_t m23 = pack_bf16x2(a[2], a[3]);
+      const float mine[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+      const float other[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
+      float hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = gate ? mine[i] : other[i], u = gate ? other[i] : mine[i];
+        hv[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+      }
+      h[mh][ni][0] = pack_bf16x2(hv[0], hv[1]);
+      h[mh][ni][1] = pack_bf16x2(hv[2], hv[3]);
+      m = max3_abs(m, bf16_lo(h[mh][ni][0]), bf16_hi(h[mh][ni][0]));
+      m = max3_abs(m, bf16_lo(h[mh][ni][1]), bf16_hi(h[mh][ni][1]));
+    }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    amax[mh] = m;
+    if ((lane >> 4) == 0) ml[half * C::kBM + r] = m;
+  }
+  __syncthreads();
+  // the block's |max| from both halves, then this half's codes
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) {
+    const int r = wm * 64 + (gate ? mh : 2 + mh) * 16 + (lane & 15);
+    const BlockQ bq = block_params<kOut>(__builtin_fmaxf(amax[mh], ml[(half ^ 1) * C::kBM + r]));
+    uint32_t cw[C::kSubN];
+#pragma unroll
+    for (int ni = 0; ni < C::kSubN; ++ni) {
+      const float x[4] = {bf16_lo(h[mh][ni][0]), bf16_hi(h[mh][ni][0]), bf16_lo(h[mh][ni][1]),
+                          bf16_hi(h[mh][ni][1])};
+      float qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+      cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+    }
+    if (r < t.m_valid && half == 0 && (lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
+    const uint4 v = rows_to_subtiles(cw[0], cw[1], cw[2], cw[3]);
+    if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * F + half * 64 + 16 * (lane >> 4), v);
+  }
+}
+
 // After the main loop: the power-of-two NaN rule, zero rows of invalid
 // gathered indices, then the epilogue of the variant (bf16, quantized or
 // SwiGLU output).  bad: the pow2 scale-check bits of this lane.
@@ -1272,6 +1372,8 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
       const int rr = wm * 64 + r, nn = wn * C::kWaveN + c * 8;
       if (rr < t.m_valid && nn < t.n_valid) store_stream16(y + (int64_t)rr * N + nn, v);
     }
+  } else if constexpr (V::kSwiGLU && C::kWaveN == 64) {
+    swiglu_epilogue_half<C, V>(t, o, N, lds, acc, wn, wm, lane);
   } else if constexpr (V::kSwiGLU) {
     static_assert(C::kWaveN == 128, "SwiGLU epilogue: a wave holds 128 gate or up rows");
     static_assert(kSubM == 4, "SwiGLU epilogue: 64 rows per wave, split in two halves");
@@ -1291,7 +1393,7 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
     const int64_t F = N >> 1;   // columns of h
     const int64_t nbo = F >> 7;  // scale blocks per row of h
     // gate waves hand over g of sub-tiles 2, 3; up waves u of sub-tiles 0, 1
-    auto hand_over = [&](auto MI) {
+    auto hand_over = [&](auto MI) __attribute__((always_inline)) {
       constexpr int mi = decltype(MI)::value;
       const int r = wm * 64 + mi * 16 + (lane & 15);
 #pragma unroll
@@ -1304,7 +1406,7 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
       }
     };
     // h, its block scale and codes for sub-tile mi (kGate: this wave holds g)
-    auto rows_out = [&](auto MI, auto GATE) {
+    auto rows_out = [&](auto MI, auto GATE) __attribute__((always_inline)) {
       constexpr int mi = decltype(MI)::value;
       constexpr bool kGate = decltype(GATE)::value;
       const int r = wm * 64 + mi * 16 + (lane & 15);
@@ -1673,14 +1775,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
     o.yq = p.yq + m0 * p.ldy + n0;
     o.ys = p.ys + m0 * (p.ldy >> 7) + (n0 >> 7);
   }
-  if constexpr (kGrouped && C::kBM == 256 && kOut == kOutBf16 && !V::kBRow) {
+  if constexpr (kGrouped && C::kBM == 256 && (kOut == kOutBf16 || V::kSwiGLU) && !V::kBRow) {
     // A group's last slot with at most 128 rows runs as a 128-row tile (same
     // eight waves): about half the padding of a 256-row tile, at ~0.7 of its
     // time (Qwen3 routing: padding rows 23% -> 12% of the rows).  Measured:
     // Qwen3 gate+up +2% (pow2), amax grouped GEMMs +1-6% (Moonlight down
     // -1.5%), gathered rows +1.5-3%.
     if (t.m_valid <= CfgSmall8::kBM) {
-      gemm_tile<CfgSmall8, V>(t, o, p.ldy, lds);
+      gemm_tile<CfgSmall8, V>(t, o, V::kSwiGLU ? p.N : p.ldy, lds);
       return;
     }
   }
