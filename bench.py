@@ -933,7 +933,53 @@ def dispatch(fp8q, synth, torch, dev, reps):
         }
         log(f"dispatch {shape.name}: route {t_route * 1e6:.1f} us; after {t_after * 1e6:.1f} us, "
             f"before {t_before * 1e6:.1f} us (gather GEMM {t_gg * 1e6:.1f} vs grouped {t_gr * 1e6:.1f} us)")
-        del xt, bq, bs, xr, aq_r, as_r, aq_t, as_t, y, ws, entry
+
+        # The experts' whole FFN (gate+up, SwiGLU, down) from the routing table,
+        # the expert outputs in dispatch order (the top-k weighted combine back
+        # to tokens is outside the FP8 path).  FP8 end to end: tokens quantized
+        # once, the gathering gate+up GEMM with SwiGLU and the down
+        # projection's quantization in its epilogue, the grouped down GEMM on
+        # its codes.  Against: bf16 gather, quantize the routed rows, bf16
+        # gate+up, torch SwiGLU, quantize h, grouped down GEMM.
+        wd = synth.moe_weights(shape, "down", device=dev)
+        Hd, F = wd.shape[1], wd.shape[2]
+        dq = torch.empty((G, Hd, F), dtype=torch.uint8, device=dev)
+        dsc = torch.empty((G, Hd // 128, F // 128), dtype=torch.float32, device=dev)
+        for g in range(G):
+            fp8q.fp8_quant_weight_128x128(wd[g], out=(dq[g], dsc[g]))
+        del wd
+        hq = torch.empty((Mt, F), dtype=torch.uint8, device=dev)
+        hs = torch.empty((Mt, F // 128), dtype=torch.float32, device=dev)
+        h = torch.empty((Mt, F), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((Mt, Hd), dtype=torch.bfloat16, device=dev)
+        yv, hv = y.view(Mt, F // 128, 2, 128), h.view(Mt, F // 128, 128)
+
+        def ffn_fp8():
+            route()
+            fp8q.fp8_quant_act_1x128(xt, out=(aq_t, as_t))
+            fp8q.fp8_grouped_gemm_swiglu_quant(aq_t, as_t, bq, bs, offd, row_index=idx, out=(hq, hs))
+            fp8q.fp8_grouped_gemm(hq, hs, dq, dsc, offd, out=yd)
+
+        def ffn_unfused():
+            after()
+            torch.mul(torch.nn.functional.silu(yv[:, :, 0]), yv[:, :, 1], out=hv)
+            fp8q.fp8_quant_act_1x128(h, out=(hq, hs))
+            fp8q.fp8_grouped_gemm(hq, hs, dq, dsc, offd, out=yd)
+
+        ffn_fp8()
+        ffn_unfused()
+        t_ffn = time_loop(ffn_fp8, reps, torch, label=lb + "/ffn_fp8")
+        t_ffn_u = time_loop(ffn_unfused, reps, torch, label=lb + "/ffn_unfused")
+        flops = 2.0 * Mt * K * N + 2.0 * Mt * F * Hd
+        out[shape.name]["expert_ffn"] = {
+            "fp8_us": us(t_ffn), "unfused_us": us(t_ffn_u), "speedup": round(t_ffn_u / t_ffn, 3),
+            "fp8_tflops": round(flops / t_ffn / 1e12, 1), "F": F, "hidden": Hd,
+            "chain": ("route, quantize T tokens, gathering gate+up GEMM with SwiGLU + quantization epilogue, "
+                      "grouped down GEMM; against route, bf16 gather, quantize routed rows, bf16 gate+up, "
+                      "torch SwiGLU, quantize h, grouped down GEMM")}
+        log(f"dispatch {shape.name} expert FFN: FP8 end to end {t_ffn * 1e6:.1f} us "
+            f"({flops / t_ffn / 1e12:.1f} TFLOP/s) vs {t_ffn_u * 1e6:.1f} us unfused")
+        del xt, bq, bs, xr, aq_r, as_r, aq_t, as_t, y, ws, entry, dq, dsc, hq, hs, h, yd
         torch.cuda.empty_cache()
     return out
 
