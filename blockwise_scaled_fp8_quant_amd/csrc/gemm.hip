@@ -155,7 +155,7 @@ using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
 template <class V>
 using LargeCfg = typename std::conditional<V::kPow2 && !V::kBRow, CfgLarge, CfgLargeLockstep>::type;
 template <class V>
-using SmallCfg = typename std::conditional<V::kOut == kOutBf16 && !V::kBRow && !V::kSwiGLU, CfgSmall8, CfgSmall>::type;
+using SmallCfg = typename std::conditional<!V::kBRow, CfgSmall8, CfgSmall>::type;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -1176,6 +1176,65 @@ __device__ __forceinline__ uint4 rows_to_subtiles(uint32_t w0, uint32_t w1, uint
   return (uint4){t01[0], t01[1], t23[0], t23[1]};
 }
 
+// Quantized epilogue of the 128-row, 8-wave tile (the 128-row part of a
+// single-launch tile plan): four waves along n with 64 weight rows each, so
+// the 1x128 block of a row's columns 128b .. 128b+127 is held by waves 2b
+// and 2b+1, one 64-column half each.  Each wave rounds its values to bf16
+// and takes their |max| over its half; the two waves exchange the partial
+// maxima through LDS, then quantize their halves with the block's scale.
+// The codes and scales equal those of the 256-row tile's epilogue (and so
+// of quantizing the bf16 output).
+template <class C, class V>
+__device__ __forceinline__ void quant_epilogue_half(const TileJob &t, const TileOut &o, int64_t N, uint8_t *lds,
+                                                    v4f (&acc)[kSubN][kSubM], int wn, int wm, int lane) {
+  static_assert(C::kWaveN == 64 && C::kSubN == 4 && C::kWavesN == 4, "128-row quantized tile layout");
+  constexpr int kOut = V::kOut;
+  float *ml = reinterpret_cast<float *>(lds);  // [4 waves along n][kBM rows] partial maxima
+  const int half = wn & 1;
+  const bool live = (wn >> 1) * 128 < t.n_valid;  // this block's columns exist (N is a multiple of 128)
+  const int64_t nbo = N >> 7;  // scale blocks per output row
+  uint32_t h[kSubM][C::kSubN][2];
+  float amax[kSubM];
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) {
+    float m = 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < C::kSubN; ++ni) {
+      h[mi][ni][0] = pack_bf16x2(acc[ni][mi][0], acc[ni][mi][1]);
+      h[mi][ni][1] = pack_bf16x2(acc[ni][mi][2], acc[ni][mi][3]);
+      m = max3_abs(m, bf16_lo(h[mi][ni][0]), bf16_hi(h[mi][ni][0]));
+      m = max3_abs(m, bf16_lo(h[mi][ni][1]), bf16_hi(h[mi][ni][1]));
+    }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    amax[mi] = __builtin_fmaxf(m, __shfl_xor(m, 32));
+  }
+  __syncthreads();  // the stage buffers are free once every wave is past the main loop
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi)
+    if ((lane >> 4) == 0) ml[wn * C::kBM + wm * 64 + mi * 16 + (lane & 15)] = amax[mi];
+  __syncthreads();
+  if (!live) return;
+#pragma unroll
+  for (int mi = 0; mi < kSubM; ++mi) {
+    const int r = wm * 64 + mi * 16 + (lane & 15);
+    const BlockQ bq = block_params<kOut>(__builtin_fmaxf(amax[mi], ml[(wn ^ 1) * C::kBM + r]));
+    uint32_t cw[C::kSubN];
+#pragma unroll
+    for (int ni = 0; ni < C::kSubN; ++ni) {
+      const float x[4] = {bf16_lo(h[mi][ni][0]), bf16_hi(h[mi][ni][0]), bf16_lo(h[mi][ni][1]),
+                          bf16_hi(h[mi][ni][1])};
+      float qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+      cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+    }
+    if (r < t.m_valid && half == 0 && (lane >> 4) == 0) o.ys[(int64_t)r * nbo + (wn >> 1)] = bq.s;
+    const uint4 v = rows_to_subtiles(cw[0], cw[1], cw[2], cw[3]);
+    if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * N + wn * 64 + 16 * (lane >> 4), v);
+  }
+}
+
 // SwiGLU epilogue of the 128-row, 8-wave tile (a group's ragged last slot in
 // the grouped GEMM): four waves along n with 64 weight rows each, wn = 0, 1
 // holding gate columns 0-63 and 64-127 of the tile's 128 features and
@@ -1484,8 +1543,10 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
     // quantizer, so the result equals quantizing the bf16 output bit for bit.
     // The codes go out as 16 bytes per lane (rows_to_subtiles): 64 bytes of a
     // row per instruction instead of 16, +1-5% on the Llama shapes.
-    static_assert(C::kWaveN == 128, "quantized epilogue: a wave's 128 columns are one 1x128 block");
-    if (wn * 128 < t.n_valid) {
+    if constexpr (C::kWaveN == 64) {
+      quant_epilogue_half<C, V>(t, o, N, lds, acc, wn, wm, lane);
+    } else if (wn * 128 < t.n_valid) {
+      static_assert(C::kWaveN == 128, "quantized epilogue: a wave's 128 columns are one 1x128 block");
       const int64_t nbo = N >> 7;  // scale blocks per output row
 #pragma unroll
       for (int mi = 0; mi < kSubM; ++mi) {
@@ -1622,6 +1683,8 @@ struct GemmRegion {
   const uint8_t *b_q;
   const float *b_s;
   uint16_t *y;
+  uint8_t *yq;
+  float *ys;
   int64_t M, N;
   int64_t slots_m;
   int32_t tiles_n;
@@ -1697,7 +1760,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   constexpr bool kGather = V::kGather;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
-  if constexpr (!kGrouped && C::kBM == 256 && kOut == kOutBf16 && !V::kBRow && !V::kSwiGLU) {
+  if constexpr (!kGrouped && C::kBM == 256 && !V::kBRow && !V::kSwiGLU) {
     if (p.wgs_large > 0 && (int64_t)blockIdx.x >= p.wgs_large) {
       // The workgroups are dispatched in order, so the 128-row tiles fill
       // the CUs as the 256-row ones finish (no launch boundary between the
@@ -1719,7 +1782,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
       t.b_s = r.b_s + (n0 >> 7) * t.KB;
       t.m_valid = (int)((r.M - m0) < CfgSmall8::kBM ? (r.M - m0) : CfgSmall8::kBM);
       t.n_valid = (int)((r.N - n0) < kBN ? (r.N - n0) : kBN);
-      const TileOut o{r.y + m0 * p.ldy + n0, nullptr, nullptr};
+      TileOut o{nullptr, nullptr, nullptr};
+      if constexpr (kOut == kOutBf16) {
+        o.y = r.y + m0 * p.ldy + n0;
+      } else {
+        o.yq = r.yq + m0 * p.ldy + n0;
+        o.ys = r.ys + m0 * (p.ldy >> 7) + (n0 >> 7);
+      }
       gemm_tile<CfgSmall8, V>(t, o, p.ldy, lds);
       return;
     }
@@ -1823,9 +1892,10 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
 // 256 CUs times a tile's time, a 128-row tile taking about 0.7 of a 256-row one
 // (measured on the Llama shapes).  Besides all-large (R = M, P = all) and
 // all-small (R = 0), the output of every GEMM but the SwiGLU one may be split
-// in two launches into slices of the output (bf16 Y, or the E4M3 codes and
-// their scales): by weight panels (R = M, P < all) or by token rows (R < M,
-// P = all).  At 4096 tokens QKV's 24 panels make 384 large tiles (two rounds,
+// into slices of the output (bf16 Y, or the E4M3 codes and their scales): by
+// weight panels (R = M, P < all) or by token rows (R < M, P = all), as one
+// launch holding both tile shapes (8 waves each) or, with per-row weight
+// scales, as two launches.  At 4096 tokens QKV's 24 panels make 384 large tiles (two rounds,
 // the second half empty); 16 panels on large tiles (one round) and 8 on small
 // ones (one round) cost 1.7 instead of 2 (measured on the quantized output:
 // 1.09x).  The weight gradient of QKV (6144 rows of dW, 16 panels) splits by
@@ -1885,25 +1955,27 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
   }
-  if constexpr (kOut == kOutBf16 && !kBRow && !kSwiGLU) {
+  if constexpr (!kBRow && !kSwiGLU) {
     // Both shapes in one launch (the 128-row tiles run 8 waves too): rows
     // [0, rows_large) x panels [0, n1) on 256-row tiles, the rest (the other
     // rows, or the other panels) on 128-row tiles.
-    static_assert(SmallCfg<V>::kThreads == LargeCfg<V>::kThreads, "one workgroup size");
+    static_assert(CfgSmall8::kThreads == LargeCfg<V>::kThreads, "one workgroup size");
     const bool by_rows = rows_large > 0 && rows_large < M;
     if (by_rows || n1 > 0) {
       GemmRegion r;
       if (by_rows) {
         p.M = rows_large;
         p.slots_m = rows_large / CfgLarge::kBM;
-        r = GemmRegion{a_q + rows_large * K, a_s + rows_large * (K / kBK), b_q, b_s, y + rows_large * p.ldy,
-                       M - rows_large, N, 0, tiles_n};
+        r = GemmRegion{a_q + rows_large * K, a_s + rows_large * (K / kBK), b_q, b_s,
+                       y ? y + rows_large * p.ldy : nullptr, yq ? yq + rows_large * p.ldy : nullptr,
+                       ys ? ys + rows_large * (p.ldy >> 7) : nullptr, M - rows_large, N, 0, tiles_n};
       } else {
         const int64_t n_off = n1 * kBN;
         p.N = n_off;
         p.tiles_n = (int32_t)n1;
         p.slots_m = mt_large;
-        r = GemmRegion{a_q, a_s, b_q + n_off * K, b_s + (n_off / 128) * (K / kBK), y + n_off, M, N - n_off, 0,
+        r = GemmRegion{a_q, a_s, b_q + n_off * K, b_s + (n_off / 128) * (K / kBK), y ? y + n_off : nullptr,
+                       yq ? yq + n_off : nullptr, ys ? ys + n_off / 128 : nullptr, M, N - n_off, 0,
                        (int32_t)(tiles_n - n1)};
       }
       r.slots_m = (r.M + CfgSmall8::kBM - 1) / CfgSmall8::kBM;

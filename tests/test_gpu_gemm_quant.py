@@ -105,8 +105,9 @@ def test_fused_exact_integer_products(mode):
 @pytest.mark.parametrize("mode", [0, 1])
 def test_fused_llama_qkv_panel_split(mode):
     # The QKV projection at 4096 tokens: 16 weight panels on 256-row tiles and
-    # 8 on 128-row tiles, two launches into column slices of the codes and
-    # scales.  Whole output, bit for bit against quantizing the bf16 output.
+    # 8 on 128-row tiles (8 waves, each holding half of a 1x128 block), one
+    # launch into column slices of the codes and scales.  Whole output, bit
+    # for bit against quantizing the bf16 output.
     require_gpu()
     M, N, K = 4096, 6144, 4096
     rows, big = lib().fp8_blockscaled_gemm_tile_plan(M, N)
@@ -144,3 +145,29 @@ def test_fused_llama_o_full_size(mode):
     ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, ms.reshape(-1), ns.reshape(-1))
     ybf = (ybits.astype(np.uint32) << 16).view(np.float32)[ms.reshape(-1), ns.reshape(-1)]
     gemm_tolerance_check(ybf, ref, "full sampled bf16 Y", frob=2e-3)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fused_split_by_token_rows(mode):
+    """A shape that the tile plan splits by token rows (6144 x 4096: rows
+    0..4095 on 256-row tiles, the rest on 128-row tiles of 8 waves, one
+    launch), and a ragged one split by weight panels with a half last panel
+    (4000 x 6016): the whole output bit for bit against quantizing the bf16
+    output, and sampled bf16 values against the oracle."""
+    require_gpu()
+    for M, N, K in ((6144, 4096, 512), (4000, 6016, 384)):
+        rows, big = lib().fp8_blockscaled_gemm_tile_plan(M, N)
+        assert (rows, big) != (M, (N + 255) // 256) and rows > 0, (M, N, rows, big)
+        aq, as_, bq, bs = _operands(M, N, K, seed=M + N + mode)
+        say("gemm_quant split", M, N, K, MODES[mode], rows, big)
+        q, s, ybits = _run(aq, as_, bq, bs, mode)
+        q_ref, s_ref = oracle.quant_act_1x128(ybits, mode)
+        assert_bytes_equal(q, q_ref, f"{M}x{N} bytes")
+        assert_scales_equal(s, s_ref, f"{M}x{N} scales")
+        _check_half_step(q, s, ybits, f"{M}x{N}")
+        ms = np.concatenate([np.arange(5, M, 97), [rows - 1, rows, M - 1]])
+        ns = np.concatenate([np.arange(3, N, 53), [N - 1]])
+        mm, nn = np.meshgrid(ms[ms < M], ns, indexing="ij")
+        ref = oracle.gemm_sampled_f64(aq, as_, bq, bs, mm.reshape(-1), nn.reshape(-1))
+        ybf = (ybits.astype(np.uint32) << 16).view(np.float32)[mm.reshape(-1), nn.reshape(-1)]
+        gemm_tolerance_check(ybf, ref, f"{M}x{N} sampled bf16 Y")
