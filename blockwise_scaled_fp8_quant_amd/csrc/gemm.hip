@@ -1176,6 +1176,35 @@ __device__ __forceinline__ uint4 rows_to_subtiles(uint32_t w0, uint32_t w1, uint
   return (uint4){t01[0], t01[1], t23[0], t23[1]};
 }
 
+// E4M3 codes of a block's values held as bf16 pairs (h[i] = values 4i .. 4i+3
+// of the lane) with its parameters, by the activation rule.  A block whose
+// quotients cannot exceed 448 (1 + 2^-23) -- power-of-two scales, or amax
+// scales on the fast path with a normal scale -- converts without the
+// explicit clamp: the hardware conversion (round to nearest even) takes such
+// values to 448 itself.  The choice is one branch, uniform over the wave.
+template <int kOut, int kN>
+__device__ __forceinline__ void block_codes(const BlockQ &bq, const uint32_t (&h)[kN][2], uint32_t (&cw)[kN]) {
+  const bool plain = kOut == kModePow2 || (!bq.slow && bq.s >= 0x1p-126f);
+  if (__builtin_amdgcn_ballot_w64(!plain) == 0) {
+#pragma unroll
+    for (int ni = 0; ni < kN; ++ni) {
+      const float q0 = quotient<kOut>(bq, bf16_lo(h[ni][0])), q1 = quotient<kOut>(bq, bf16_hi(h[ni][0]));
+      const float q2 = quotient<kOut>(bq, bf16_lo(h[ni][1])), q3 = quotient<kOut>(bq, bf16_hi(h[ni][1]));
+      cw[ni] = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false), true);
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < kN; ++ni) {
+      const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
+      float qv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
+      cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+    }
+  }
+}
+
 // Quantized epilogue of the 128-row, 8-wave tile (the 128-row part of a
 // single-launch tile plan): four waves along n with 64 weight rows each, so
 // the 1x128 block of a row's columns 128b .. 128b+127 is held by waves 2b
@@ -1219,16 +1248,7 @@ __device__ __forceinline__ void quant_epilogue_half(const TileJob &t, const Tile
     const int r = wm * 64 + mi * 16 + (lane & 15);
     const BlockQ bq = block_params<kOut>(__builtin_fmaxf(amax[mi], ml[(wn ^ 1) * C::kBM + r]));
     uint32_t cw[C::kSubN];
-#pragma unroll
-    for (int ni = 0; ni < C::kSubN; ++ni) {
-      const float x[4] = {bf16_lo(h[mi][ni][0]), bf16_hi(h[mi][ni][0]), bf16_lo(h[mi][ni][1]),
-                          bf16_hi(h[mi][ni][1])};
-      float qv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
-      cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-    }
+    block_codes<kOut>(bq, h[mi], cw);
     if (r < t.m_valid && half == 0 && (lane >> 4) == 0) o.ys[(int64_t)r * nbo + (wn >> 1)] = bq.s;
     const uint4 v = rows_to_subtiles(cw[0], cw[1], cw[2], cw[3]);
     if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * N + wn * 64 + 16 * (lane >> 4), v);
@@ -1319,16 +1339,7 @@ __device__ __forceinline__ void swiglu_epilogue_half(const TileJob &t, const Til
     const int r = wm * 64 + (gate ? mh : 2 + mh) * 16 + (lane & 15);
     const BlockQ bq = block_params<kOut>(__builtin_fmaxf(amax[mh], ml[(half ^ 1) * C::kBM + r]));
     uint32_t cw[C::kSubN];
-#pragma unroll
-    for (int ni = 0; ni < C::kSubN; ++ni) {
-      const float x[4] = {bf16_lo(h[mh][ni][0]), bf16_hi(h[mh][ni][0]), bf16_lo(h[mh][ni][1]),
-                          bf16_hi(h[mh][ni][1])};
-      float qv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
-      cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-    }
+    block_codes<kOut>(bq, h[mh], cw);
     if (r < t.m_valid && half == 0 && (lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
     const uint4 v = rows_to_subtiles(cw[0], cw[1], cw[2], cw[3]);
     if (r < t.m_valid) store_stream16(o.yq + (int64_t)r * F + half * 64 + 16 * (lane >> 4), v);
@@ -1494,15 +1505,7 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
       const BlockQ bq = block_params<kOut>(amax);
       uint32_t cw[kSubN];
-#pragma unroll
-      for (int ni = 0; ni < kSubN; ++ni) {
-        const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
-        float qv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
-        cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-      }
+      block_codes<kOut>(bq, h, cw);
       if (r < t.m_valid && (lane >> 4) == 0) o.ys[(int64_t)r * nbo] = bq.s;
 #pragma unroll
       for (int q = 0; q < kSubN / 4; ++q) {
@@ -1564,15 +1567,7 @@ __device__ __forceinline__ void tile_finish(const TileJob &t, const TileOut &o, 
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
         const BlockQ bq = block_params<kOut>(amax);
         uint32_t cw[kSubN];
-#pragma unroll
-        for (int ni = 0; ni < kSubN; ++ni) {
-          const float x[4] = {bf16_lo(h[ni][0]), bf16_hi(h[ni][0]), bf16_lo(h[ni][1]), bf16_hi(h[ni][1])};
-          float qv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            qv[i] = (kOut == kModeAmax && bq.slow) ? x[i] / bq.s : quotient<kOut>(bq, x[i]);
-          cw[ni] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-        }
+        block_codes<kOut>(bq, h, cw);
         if (r < t.m_valid && (lane >> 4) == 0) o.ys[(int64_t)r * nbo + wn] = bq.s;
 #pragma unroll
         for (int q = 0; q < kSubN / 4; ++q) {
