@@ -18,10 +18,13 @@
 //    consecutive n of one token row m: they share one scale product and are
 //    stored as one 8-byte bf16 quad.
 //  - Each wave owns 128 (n) x 64 (m) outputs = 8 x 4 MFMA sub-tiles (128 fp32
-//    accumulators per lane).  Two tile shapes:
-//      256 x 256 tiles, 8 waves (2 per SIMD), 2-stage pipeline  (large M)
-//      256 x 128 tiles, 4 waves (1 per SIMD), 3-stage pipeline  (small M,
-//                                                                 grouped)
+//    accumulators per lane), or 64 (n) x 64 (m) in the 128-row tiles.  Tile
+//    shapes (weight rows x token rows), all with a 2-stage pipeline:
+//      256 x 256 tiles, 8 waves (2 per SIMD)               (large M)
+//      256 x 128 tiles, 8 waves, 4 along n                 (small M, a
+//                                      group's last slot, split plans)
+//      256 x 128 tiles, 4 waves (1 per SIMD)               (per-row weight
+//                                      scales: the weight gradient)
 //  - Everything a K block needs -- the weight and token tiles and both scale
 //    vectors -- reaches LDS by direct global->LDS DMA (global_load_lds), so a
 //    stage is a fixed number of vector-memory instructions per wave and the
@@ -148,9 +151,9 @@ struct TileCfg {
 using CfgLarge = TileCfg<256, 8, 2, 8, 0, 1, 2, true>;
 using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 3>;
 using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
-// 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD) for
-// bf16 outputs without per-row weight scales, whose epilogues do not need a
-// wave to hold 128 weight rows.
+// 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD)
+// for every output but the per-row-scale one; the quantized and SwiGLU
+// epilogues then split a 1x128 output block between two waves.
 using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
 template <class V>
 using LargeCfg = typename std::conditional<V::kPow2 && !V::kBRow, CfgLarge, CfgLargeLockstep>::type;
