@@ -23,8 +23,8 @@
 //      256 x 256 tiles, 8 waves (2 per SIMD)               (large M)
 //      256 x 128 tiles, 8 waves, 4 along n                 (small M, a
 //                                      group's last slot, split plans)
-//      256 x 128 tiles, 4 waves (1 per SIMD)               (per-row weight
-//                                      scales: the weight gradient)
+//      256 x 128 tiles, 4 waves (1 per SIMD)               (per-row power-
+//                              of-two weight scales: the weight gradient)
 //  - Everything a K block needs -- the weight and token tiles and both scale
 //    vectors -- reaches LDS by direct global->LDS DMA (global_load_lds), so a
 //    stage is a fixed number of vector-memory instructions per wave and the
@@ -152,13 +152,14 @@ using CfgLarge = TileCfg<256, 8, 2, 8, 0, 1, 2, true>;
 using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 3>;
 using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
 // 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD)
-// for every output but the per-row-scale one; the quantized and SwiGLU
-// epilogues then split a 1x128 output block between two waves.
+// for every variant but per-row power-of-two weight scales (whose E8M0 bytes
+// a lane hands to the eight sub-tiles of a 128-row wave); the quantized and
+// SwiGLU epilogues then split a 1x128 output block between two waves.
 using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
 template <class V>
 using LargeCfg = typename std::conditional<V::kPow2 && !V::kBRow, CfgLarge, CfgLargeLockstep>::type;
 template <class V>
-using SmallCfg = typename std::conditional<!V::kBRow, CfgSmall8, CfgSmall>::type;
+using SmallCfg = typename std::conditional<!(V::kBRow && V::kPow2), CfgSmall8, CfgSmall>::type;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -245,7 +246,7 @@ __device__ __forceinline__ const float4 *sa_chunk_ptr(const uint8_t *lds, int k,
 }
 template <class C>
 __device__ __forceinline__ const float4 *sbf_chunk_ptr(const uint8_t *lds, int k, int wn, int ni, int lane) {
-  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 8 + ni) * 256 +
+  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * C::kSubN + ni) * 256 +
                                           16 * (lane >> 4));
 }
 template <class C>
@@ -719,7 +720,7 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, const uint8_t *lds,
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int kWAhead = C::kWAhead;
   static_assert(kWAhead >= 1 && kWAhead <= kMaxWAhead, "weight read-ahead");
-  static_assert(!V::kBRow || C::kWaveN == 128, "per-row weight scales: 128 weight rows per wave");
+  static_assert(!(V::kBRow && kPow2) || C::kWaveN == 128, "per-row power-of-two scales: 128 weight rows per wave");
   constexpr int R = kWAhead + 1;
   v8i wf[R];
 #pragma unroll
@@ -1758,7 +1759,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   constexpr bool kGather = V::kGather;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
-  if constexpr (!kGrouped && C::kBM == 256 && !V::kBRow && !V::kSwiGLU) {
+  if constexpr (!kGrouped && C::kBM == 256 && !(V::kBRow && V::kPow2) && !V::kSwiGLU) {
     if (p.wgs_large > 0 && (int64_t)blockIdx.x >= p.wgs_large) {
       // The workgroups are dispatched in order, so the 128-row tiles fill
       // the CUs as the 256-row ones finish (no launch boundary between the
@@ -1777,7 +1778,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
       t.gidx = nullptr;
       t.T = 0;
       t.b_q = r.b_q + n0 * p.K;
-      t.b_s = r.b_s + (n0 >> 7) * t.KB;
+      t.b_s = r.b_s + (V::kBRow ? n0 : (n0 >> 7)) * t.KB;
       t.m_valid = (int)((r.M - m0) < CfgSmall8::kBM ? (r.M - m0) : CfgSmall8::kBM);
       t.n_valid = (int)((r.N - n0) < kBN ? (r.N - n0) : kBN);
       TileOut o{nullptr, nullptr, nullptr};
@@ -1953,7 +1954,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
   }
-  if constexpr (!kBRow && !kSwiGLU) {
+  if constexpr (!(kBRow && kPow2) && !kSwiGLU) {
     // Both shapes in one launch (the 128-row tiles run 8 waves too): rows
     // [0, rows_large) x panels [0, n1) on 256-row tiles, the rest (the other
     // rows, or the other panels) on 128-row tiles.
@@ -1972,7 +1973,8 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
         p.N = n_off;
         p.tiles_n = (int32_t)n1;
         p.slots_m = mt_large;
-        r = GemmRegion{a_q, a_s, b_q + n_off * K, b_s + (n_off / 128) * (K / kBK), y ? y + n_off : nullptr,
+        r = GemmRegion{a_q, a_s, b_q + n_off * K, b_s + (kBRow ? n_off : n_off / 128) * (K / kBK),
+                       y ? y + n_off : nullptr,
                        yq ? yq + n_off : nullptr, ys ? ys + n_off / 128 : nullptr, M, N - n_off, 0,
                        (int32_t)(tiles_n - n1)};
       }
