@@ -23,8 +23,6 @@
 //      256 x 256 tiles, 8 waves (2 per SIMD)               (large M)
 //      256 x 128 tiles, 8 waves, 4 along n                 (small M, a
 //                                      group's last slot, split plans)
-//      256 x 128 tiles, 4 waves (1 per SIMD)               (per-row power-
-//                              of-two weight scales: the weight gradient)
 //  - Everything a K block needs -- the weight and token tiles and both scale
 //    vectors -- reaches LDS by direct global->LDS DMA (global_load_lds), so a
 //    stage is a fixed number of vector-memory instructions per wave and the
@@ -95,9 +93,8 @@ struct TileCfg {
   // step 5 and later the DMA is not finished when the block ends.  Step 3
   // against 4: dense +1-2%, grouped MoE GEMMs +1-10% (Qwen3 down +10%, gathered
   // rows +4-6%), whose tiles' operands miss in L2 more often, so the DMA needs
-  // the extra step to land.  128-row tiles
-  // (4 waves, one per SIMD, so each K block takes longer per wave): step 5
-  // with two stages, +22% against three stages and step 0.
+  // the extra step to land.  128-row tiles (8 waves, four sub-tile rows per
+  // wave): step 2 (step 1: -1-3%, step 0: -3-7%).
   // The last kLoaders waves issue the stage DMA.
   static constexpr int kLoaders = kLoaders_;
   static constexpr int kDmaStep = kDmaStep_;
@@ -150,16 +147,15 @@ struct TileCfg {
 // (Llama gate+up and down).  Without folds the ping-pong loop is 3-6% ahead.
 using CfgLarge = TileCfg<256, 8, 2, 8, 0, 1, 2, true>;
 using CfgLargeLockstep = TileCfg<256, 8, 2, 8, 3>;
-using CfgSmall = TileCfg<128, 4, 2, 4, 5>;
-// 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD)
-// for every variant but per-row power-of-two weight scales (whose E8M0 bytes
-// a lane hands to the eight sub-tiles of a 128-row wave); the quantized and
-// SwiGLU epilogues then split a 1x128 output block between two waves.
+// 128-row tiles with 8 waves (4 along n, 64 weight rows each; 2 per SIMD).
+// The quantized and SwiGLU epilogues split a 1x128 output block between two
+// waves; per-row weight-side scales are staged for the wave's four sub-tile
+// rows.
 using CfgSmall8 = TileCfg<128, 8, 2, 8, 2, 1, 4>;
 template <class V>
 using LargeCfg = typename std::conditional<V::kPow2 && !V::kBRow, CfgLarge, CfgLargeLockstep>::type;
 template <class V>
-using SmallCfg = typename std::conditional<!(V::kBRow && V::kPow2), CfgSmall8, CfgSmall>::type;
+using SmallCfg = CfgSmall8;
 
 // Row swizzle of the 16-byte chunks: chunk c of row r lives in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1).  Sixteen consecutive rows reading the same
@@ -210,6 +206,12 @@ __host__ __device__ constexpr int sbf_chunk_row(int i, int t) { return 16 * i + 
 __host__ __device__ constexpr int sbp_chunk_row(int i, int t) {
   return 128 * (i >> 3) + 16 * (t & 7) + 2 * (i & 7) + (t >> 3);
 }
+// The same for 64-row waves (the 128-row, 8-wave tiles): the four rows a lane
+// supplies to the four A sub-tiles of its wave (64w + 16s + c) are
+// consecutive.
+__host__ __device__ constexpr int sbp64_chunk_row(int i, int t) {
+  return (i >> 2) * 64 + (t & 3) * 16 + 4 * (i & 3) + (t >> 2);
+}
 // Every row of the tile exactly once per chunk.
 template <int (*kRow)(int, int)>
 constexpr bool chunk_covers(int rows) {
@@ -223,7 +225,8 @@ constexpr bool chunk_covers(int rows) {
   return true;
 }
 static_assert(chunk_covers<sa_chunk_row>(256) && chunk_covers<sa_chunk_row>(128) &&
-                  chunk_covers<sbf_chunk_row>(256) && chunk_covers<sbp_chunk_row>(256),
+                  chunk_covers<sbf_chunk_row>(256) && chunk_covers<sbp_chunk_row>(256) &&
+                  chunk_covers<sbp64_chunk_row>(256),
               "scale chunk rows");
 
 // The chunk and quarter that the stage of block kn >= 1 loads.
@@ -252,8 +255,12 @@ __device__ __forceinline__ const float4 *sbf_chunk_ptr(const uint8_t *lds, int k
 template <class C>
 __device__ __forceinline__ const float4 *sbp_chunk_ptr(const uint8_t *lds, int k, int wn, int lane) {
   const int c = lane & 15;
-  return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 8 + (c >> 1)) * 256 +
-                                          32 * (c & 1));
+  if constexpr (C::kWaveN == 128)
+    return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 8 + (c >> 1)) * 256 +
+                                            32 * (c & 1));
+  else
+    return reinterpret_cast<const float4 *>(lds + chunk_base<C>(k) + C::kChunkSA + (wn * 4 + (c >> 2)) * 256 +
+                                            16 * (c & 3));
 }
 
 // This lane's index, computed where it is used.  The asm statement cannot be
@@ -450,9 +457,9 @@ __device__ __forceinline__ void issue_chunk_quarter(const TileRsrc &rs, int KB, 
   const int j = (l - C::kScaleLoaders + C::kLoaders) % C::kLoaders;
   if (j < kBN / 64) {
     const int i = q * 4 + j;
+    constexpr auto kRowB = !V::kPow2 ? sbf_chunk_row : (C::kWaveN == 128 ? sbp_chunk_row : sbp64_chunk_row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void_t *)(cb + C::kChunkSA + i * 256), 4,
-                                             chunk_lane_off<V::kPow2 ? sbp_chunk_row : sbf_chunk_row>(i, KB) + kb,
-                                             0, 0, 0);
+                                             chunk_lane_off<kRowB>(i, KB) + kb, 0, 0, 0);
   }
 }
 
@@ -581,10 +588,9 @@ __device__ __forceinline__ void read_head(const uint8_t *buf, const uint8_t *lds
   else
     h.sa4 = *reinterpret_cast<const float4 *>(buf + C::kOffSA + (wm * 64 + (lane & 15) * 4) * 4);
   if constexpr (V::kPow2 && V::kBRow) {
-    static_assert(C::kWaveN == 128, "per-row power-of-two weight scales: 128 weight rows per wave");
     const float4 *rp = sbp_chunk_ptr<C>(lds, k, wn, lane);
     h.lo = rp[0];
-    h.hi = rp[1];
+    h.hi = C::kWaveN == 128 ? rp[1] : rp[0];  // 64-row waves: four rows (the copy sets no other row's bit)
   } else if constexpr (!V::kBRow) {
     h.sb = *reinterpret_cast<const float *>(buf + C::kOffSB + ((wn * C::kWaveN) >> 7) * 4);  // the wave's 128-row block
   }
@@ -720,7 +726,6 @@ __device__ __forceinline__ void mma_steps(const uint8_t *tb, const uint8_t *lds,
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int kWAhead = C::kWAhead;
   static_assert(kWAhead >= 1 && kWAhead <= kMaxWAhead, "weight read-ahead");
-  static_assert(!(V::kBRow && kPow2) || C::kWaveN == 128, "per-row power-of-two scales: 128 weight rows per wave");
   constexpr int R = kWAhead + 1;
   v8i wf[R];
 #pragma unroll
@@ -1759,7 +1764,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   constexpr bool kGather = V::kGather;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
-  if constexpr (!kGrouped && C::kBM == 256 && !(V::kBRow && V::kPow2) && !V::kSwiGLU) {
+  if constexpr (!kGrouped && C::kBM == 256 && !V::kSwiGLU) {
     if (p.wgs_large > 0 && (int64_t)blockIdx.x >= p.wgs_large) {
       // The workgroups are dispatched in order, so the 128-row tiles fill
       // the CUs as the 256-row ones finish (no launch boundary between the
@@ -1904,13 +1909,13 @@ static hipError_t launch(GemmParams p, hipStream_t stream) {
 void dense_tile_plan(int64_t M, int64_t N, bool may_split, int64_t &rows_large, int64_t &panels_large) {
   const int64_t tiles_n = (N + kBN - 1) / kBN;
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
-  const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  const int64_t mt_small = (M + CfgSmall8::kBM - 1) / CfgSmall8::kBM;
   auto rounds = [](int64_t tiles) { return (tiles + 255) / 256; };
   auto cost_n = [&](int64_t n1) {  // n1 panels on large tiles, the rest on small ones
     return rounds(mt_large * n1) * 10 + rounds(mt_small * (tiles_n - n1)) * 7;
   };
   auto cost_m = [&](int64_t m1) {  // m1 large row tiles (256 rows each), the rest on small ones
-    return rounds(m1 * tiles_n) * 10 + rounds((M - m1 * CfgLarge::kBM + CfgSmall::kBM - 1) / CfgSmall::kBM * tiles_n) * 7;
+    return rounds(m1 * tiles_n) * 10 + rounds((M - m1 * CfgLarge::kBM + CfgSmall8::kBM - 1) / CfgSmall8::kBM * tiles_n) * 7;
   };
   int64_t best = cost_n(tiles_n), n1 = tiles_n, m1 = -1;
   if (cost_n(0) < best) {
@@ -1947,14 +1952,14 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
   const int32_t tiles_n = (int32_t)((N + kBN - 1) / kBN);
   GemmParams p{a_q, a_s, b_q, b_s, nullptr, y, yq, ys, nullptr, 0, M, N, K, 0, 1, tiles_n, N, 0, {}};
   const int64_t mt_large = (M + CfgLarge::kBM - 1) / CfgLarge::kBM;
-  const int64_t mt_small = (M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+  const int64_t mt_small = (M + CfgSmall8::kBM - 1) / CfgSmall8::kBM;
   int64_t rows_large, n1;
   dense_tile_plan(M, N, !kSwiGLU, rows_large, n1);
   if (rows_large == M && n1 == tiles_n) {
     p.slots_m = mt_large;
     return launch<LargeCfg<V>, V>(p, stream);
   }
-  if constexpr (!(kBRow && kPow2) && !kSwiGLU) {
+  if constexpr (!kSwiGLU) {
     // Both shapes in one launch (the 128-row tiles run 8 waves too): rows
     // [0, rows_large) x panels [0, n1) on 256-row tiles, the rest (the other
     // rows, or the other panels) on 128-row tiles.
@@ -2000,7 +2005,7 @@ static hipError_t dense(const uint8_t *a_q, const float *a_s, const uint8_t *b_q
       p.ys = ys + rows_large * (p.ldy >> 7);
     }
     p.M = M - rows_large;
-    p.slots_m = (p.M + CfgSmall::kBM - 1) / CfgSmall::kBM;
+    p.slots_m = (p.M + CfgSmall8::kBM - 1) / CfgSmall8::kBM;
     return launch<SmallCfg<V>, V>(p, stream);
   }
   if (n1 > 0) {
@@ -2042,7 +2047,7 @@ static hipError_t grouped(const uint8_t *a_q, const float *a_s, const uint8_t *b
     p.slots_m = M_total / CfgLarge::kBM + G;
     return launch<LargeCfg<V>, V>(p, stream);
   }
-  p.slots_m = M_total / CfgSmall::kBM + G;
+  p.slots_m = M_total / CfgSmall8::kBM + G;
   return launch<SmallCfg<V>, V>(p, stream);
 }
 
