@@ -134,9 +134,9 @@ def moe_routing(shape: MoEShape, seed_parts=None):
     seeded permutation lists the experts in rank order (the expert it puts
     first has rank 1) and p(e) ~ rank(e)^-alpha; the permutation is drawn
     before the Gumbel noise.  Uniform load (alpha = 0): the Gumbel noise
-    alone, with no permutation drawn.  This is the recipe the survey of the
-    workloads states its expert-load figures for (Qwen3: max 7397 / median
-    196 / min 79 rows per expert; Moonlight: 1477..1662).
+    alone, with no permutation drawn.  With the default seeds the expert
+    loads come out as Qwen3: max 7397 / median 196 / min 79 rows per expert;
+    Moonlight: 1477..1662.
     """
     wid = 4 if shape.zipf_alpha > 0 else 5
     rng = np.random.default_rng(np.random.SeedSequence(seed_parts or [wid, 0, 3]))
